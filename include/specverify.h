@@ -1,0 +1,242 @@
+/*
+ * libspecverify -- batched draft verification for speculative decoding on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources: the web pages "EAGLE-3 speculative decoding review"
+ * (6unoyunr.github.io), "EAGLE math" (aicassindra.com, transformer_math) and
+ * "Speculative decoding" (addictedtoai.net wiki)):
+ *
+ *   A draft proposes gamma tokens x_0..x_{gamma-1}.  The target scores the
+ *   prefix plus the drafts in one pass, giving gamma+1 rows of logits: row i
+ *   is the target's distribution for drafted position i, and row gamma is the
+ *   "bonus" row after the last draft.  Verification walks the drafts left to
+ *   right, accepts x_i with probability min(1, p_i(x_i)/q_i(x_i)), stops at
+ *   the first rejection j and resamples that position from
+ *   norm(max(0, p_j - q_j)); if every draft is accepted it takes one more
+ *   token from p_gamma.  Greedy decoding accepts a draft iff it equals the
+ *   target's argmax.  Greedy tree verification accepts the longest
+ *   root-to-node path whose tokens equal the target's argmax at their parent.
+ *   EAGLE drafts features and reuses the target's LM head z = W h.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers: every array argument is DEVICE memory owned by the caller,
+ *    row-major and contiguous with the vocabulary innermost.  Base pointers
+ *    of logits, features and weights must be 16-byte aligned (SPEC_EALIGN).
+ *    Integer and float side arrays must be 4-byte aligned.
+ *  - Logits are float32 (SPEC_F32) or bf16 bit patterns (SPEC_BF16).  Each
+ *    logit is finite or -inf, every row holds at least one finite logit and
+ *    |logit| / temperature < 1e37; NaN inputs give undefined results.
+ *  - Temperature: p = softmax(z_target / T), q = softmax(z_draft / T) with the
+ *    same T > 0 (finite).  Greedy modes have their own calls.
+ *  - Uniforms: u[b][i] for i < gamma is the accept test of drafted position
+ *    i (accept iff u < p/q); u[b][gamma] is the single final draw.  Values
+ *    must lie in [0, 1).
+ *  - Final draw: inverse CDF over ascending token index: the first token
+ *    whose cumulative mass exceeds u * total; zero-mass tokens are never
+ *    drawn.
+ *  - Argmax ties resolve to the lowest token index.
+ *  - Calls are asynchronous on stream `s` (NULL = the default stream) and
+ *    allocate nothing.  Outputs are valid once the stream has synchronised.
+ *  - Workspace: `ws` is caller-owned device memory of at least
+ *    spec_workspace_bytes(...) bytes, 256-byte aligned.  It must be zero-filled
+ *    before its first use (spec_workspace_init does that); every call leaves
+ *    its counters zeroed again.  Two calls may run concurrently only with
+ *    distinct workspaces.
+ *  - Errors: argument errors are reported synchronously, before anything is
+ *    launched, as a non-zero spec_status.  A failed launch reports
+ *    SPEC_EHIP.  Data-dependent conditions that can only be seen on the
+ *    device (an out-of-range draft token, an invalid tree) are reported per
+ *    sequence as accept_len[b] = -1 with every output token of b set to -1.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = 1,     /* a size, count, pointer or scalar argument is invalid */
+  SPEC_EDTYPE = 2,     /* unknown dtype code */
+  SPEC_EALIGN = 3,     /* a base pointer is not aligned as required */
+  SPEC_EWORKSPACE = 4, /* workspace missing or smaller than required */
+  SPEC_EHIP = 5        /* the HIP runtime reported an error */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+typedef enum {
+  SPEC_MODE_SAMPLE = 0,   /* spec_verify_sample: gamma_or_N = gamma        */
+  SPEC_MODE_GREEDY = 1,   /* spec_verify_greedy: gamma_or_N = gamma        */
+  SPEC_MODE_TREE = 2,     /* spec_verify_tree:   gamma_or_N = N (nodes)    */
+  SPEC_MODE_LMHEAD = 3,   /* lmhead_verify:      gamma_or_N = gamma, d     */
+  SPEC_MODE_ROWSTATS = 4  /* spec_row_stats / spec_probe_probs: B = rows   */
+} spec_mode;
+
+/* Limits checked by every entry point. */
+#define SPEC_MAX_GAMMA 63       /* one 64-wide wavefront lane per position   */
+#define SPEC_MAX_TREE_NODES 4096
+#define SPEC_MAX_BATCH (1 << 20)
+
+/* Bytes of workspace the call of the given mode needs for these sizes
+ * (0 when an argument is out of range).  d is used by SPEC_MODE_LMHEAD only.
+ * The LMHEAD workspace holds the float32 logits of all B(2*gamma+1) rows. */
+size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d);
+
+/* Zero-fill a workspace (a device fill kernel; graph-capture safe). */
+spec_status spec_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Human-readable name of a status code (static storage). */
+const char* spec_status_str(spec_status st);
+
+/*
+ * spec_row_stats -- one pass over each logit row.
+ * Pages: "EAGLE-3 speculative decoding review", "EAGLE: Predict Features, Not
+ * Tokens" (logits z -> softmax -> next-token distribution) and "Does Using a
+ * Small Model's Answer Reduce Quality?" (greedy takes the argmax).
+ *
+ * logits      [rows, V] in `dt`.
+ * want        bit 0: max and sum statistics; bit 1: argmax.  At least one.
+ * out_max     [rows] float32: max_v z[r][v]                  (want & 1 or 2)
+ * out_sum     [rows] float64: sum_v exp((z[r][v]-max)/T)     (want & 1; may be
+ *             NULL otherwise).  p[r][v] = exp((z[r][v]-max)/T) / out_sum[r].
+ * out_argmax  [rows] int32: lowest index of the maximum       (want & 2; may be
+ *             NULL otherwise).
+ * temperature used only for the sum (ignored when !(want & 1)).
+ * Workspace: spec_workspace_bytes(SPEC_MODE_ROWSTATS, rows, 0, V, 0).
+ */
+spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V,
+                           float temperature, int want, float* out_max,
+                           double* out_sum, int32_t* out_argmax, void* ws,
+                           size_t ws_bytes, hipStream_t s);
+
+/*
+ * spec_verify_sample -- speculative sampling verification of B sequences.
+ * Pages: "EAGLE-3 speculative decoding review", "Speculative Decoding"
+ * (3. Accept or Reject) and "Does Using a Small Model's Answer Reduce
+ * Quality?" (A(x) = min(1, p(x)/q(x)); residual norm(max(0, p - q)));
+ * "EAGLE math", "Vanilla speculative decoding" ((p - q)_+, the +1 bonus
+ * token); "Speculative decoding" wiki, "The mechanism".
+ *
+ * target_logits [B, gamma+1, V]; draft_logits [B, gamma, V] (same dtype).
+ * draft_tokens  [B, gamma] int32, each in [0, V).
+ * uniforms      [B, gamma+1] float32 in [0, 1).
+ * accept_len    [B] int32 out: j = number of accepted drafts (0..gamma).
+ * out_tokens    [B, gamma+1] int32 out: x_0..x_{j-1}, then the resampled
+ *               (j < gamma) or bonus (j = gamma) token, then -1 padding.
+ * 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= B <= SPEC_MAX_BATCH, 1 <= V < 2^31.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_SAMPLE, B, gamma, V, 0).
+ */
+spec_status spec_verify_sample(const void* target_logits, const void* draft_logits,
+                               spec_dtype dt, const int32_t* draft_tokens,
+                               const float* uniforms, int B, int gamma, int V,
+                               float temperature, int32_t* accept_len,
+                               int32_t* out_tokens, void* ws, size_t ws_bytes,
+                               hipStream_t s);
+
+/*
+ * spec_verify_greedy -- greedy verification of B sequences.
+ * Pages: "EAGLE-3 speculative decoding review", "Does Using a Small Model's
+ * Answer Reduce Quality?" (accept iff the draft equals the target's argmax;
+ * otherwise emit the target token and discard the rest; the result equals
+ * target-only greedy decoding) and "Speculative Decoding" (the bonus token).
+ *
+ * target_logits [B, gamma+1, V]; draft_tokens [B, gamma] int32.
+ * accept_len [B] out; out_tokens [B, gamma+1] out: x_0..x_{j-1}, argmax of
+ * row j, then -1.  Draft tokens outside [0, V) never match.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_GREEDY, B, gamma, V, 0).
+ */
+spec_status spec_verify_greedy(const void* target_logits, spec_dtype dt,
+                               const int32_t* draft_tokens, int B, int gamma,
+                               int V, int32_t* accept_len, int32_t* out_tokens,
+                               void* ws, size_t ws_bytes, hipStream_t s);
+
+/*
+ * spec_verify_tree -- greedy verification of a candidate tree per sequence.
+ * Pages: "EAGLE-3 speculative decoding review", "EAGLE-2: Does Every Context
+ * Need the Same Draft Tree?" (each node sees the shared prefix and its own
+ * ancestors) and "The Complete EAGLE-3 Inference Process" (4. Strict
+ * Acceptance: accept the longest prefix matching the target's choices);
+ * "EAGLE math", "EAGLE-2: dynamic draft trees".
+ *
+ * target_logits [B, N, V]: row n is the target's distribution after node n.
+ * node_tokens   [B, N] int32: token carried by node n (node 0 = the last
+ *               committed token; it is not verified).
+ * parent        [N] (parent_batch_stride = 0, shared) or [B, N]
+ *               (parent_batch_stride = N): parent[0] = -1 and
+ *               0 <= parent[n] < n.  A violation gives accept_len[b] = -1.
+ * accept_len [B] out: depth of the accepted node n* (the deepest node whose
+ *            whole root path matches; lowest index among equals).
+ * out_path   [B, N] out: node indices of the accepted path, root excluded,
+ *            root-to-leaf order, then -1.
+ * out_tokens [B, N] out: the path's tokens, then the argmax of row n*
+ *            (bonus), then -1.
+ * 1 <= N <= SPEC_MAX_TREE_NODES.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_TREE, B, N, V, 0).
+ */
+spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
+                             const int32_t* node_tokens, const int32_t* parent,
+                             int parent_batch_stride, int B, int N, int V,
+                             int32_t* accept_len, int32_t* out_path,
+                             int32_t* out_tokens, void* ws, size_t ws_bytes,
+                             hipStream_t s);
+
+/*
+ * lmhead_project -- logits of feature rows through the LM head, z = h W.
+ * Pages: "EAGLE-3 speculative decoding review", "EAGLE: Predict Features, Not
+ * Tokens" (the LM head turns the top-layer feature into vocabulary logits;
+ * the draft reuses the target's LM head); "EAGLE math", "EAGLE's move".
+ *
+ * feat [M, d] bf16 bits; W [d, V] bf16 bits (vocabulary innermost);
+ * out_logits [M, V] float32 (bf16 x bf16 products, float32 accumulation).
+ * d must be a multiple of 64; 1 <= M, 1 <= V.
+ */
+spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W,
+                           int V, float* out_logits, hipStream_t s);
+
+/*
+ * lmhead_verify -- EAGLE-style verification: the target features
+ * (B*(gamma+1) rows, row b*(gamma+1)+i) and the draft features (B*gamma
+ * rows, row b*gamma+i) go through the shared LM head into float32 logits
+ * held in the workspace, then spec_verify_sample runs on them without a
+ * host round trip.  Same outputs and uniforms convention as
+ * spec_verify_sample.  d must be a multiple of 64.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).
+ */
+spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat,
+                          const uint16_t* W, const int32_t* draft_tokens,
+                          const float* uniforms, int B, int gamma, int d, int V,
+                          float temperature, int32_t* accept_len,
+                          int32_t* out_tokens, void* ws, size_t ws_bytes,
+                          hipStream_t s);
+
+/*
+ * spec_probe_probs -- test probe: the full distributions the sampling path
+ * works with, for `rows` pairs of target/draft rows, computed by the same
+ * device statistics and element functions as spec_verify_sample's draw.
+ * Pages: as spec_verify_sample.
+ *
+ * target_logits, draft_logits [rows, V] (draft may be NULL: then q and the
+ * residual are not produced).
+ * out_p, out_q, out_resid [rows, V] float64: p, q and the normalised
+ * residual max(0, p - q) / sum(max(0, p - q)) (all zeros when p == q
+ * everywhere).  out_q / out_resid may be NULL.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_ROWSTATS, 2*rows, 0, V, 0).
+ */
+spec_status spec_probe_probs(const void* target_logits, const void* draft_logits,
+                             spec_dtype dt, int rows, int V, float temperature,
+                             double* out_p, double* out_q, double* out_resid,
+                             void* ws, size_t ws_bytes, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */
