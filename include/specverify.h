@@ -41,8 +41,9 @@
  *  - Workspace: `ws` is caller-owned device memory of at least
  *    spec_workspace_bytes(...) bytes, 256-byte aligned.  It must be zero-filled
  *    before its first use (spec_workspace_init does that); every call leaves
- *    its counters zeroed again.  Two calls may run concurrently only with
- *    distinct workspaces.
+ *    its counters zeroed again.  A workspace belongs to one (mode, sizes)
+ *    layout: zero it again before using it for another.  Two calls may run
+ *    concurrently only with distinct workspaces.
  *  - Errors: argument errors are reported synchronously, before anything is
  *    launched, as a non-zero spec_status.  A failed launch reports
  *    SPEC_EHIP.  Data-dependent conditions that can only be seen on the
@@ -208,7 +209,9 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
  * held in the workspace, then spec_verify_sample runs on them without a
  * host round trip.  Same outputs and uniforms convention as
  * spec_verify_sample.  d must be a multiple of 64.
- * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).
+ * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
+ * the call the logits are left in the last ceil256(B(2 gamma+1) V 4) bytes
+ * of the workspace: B(gamma+1) target rows, then B gamma draft rows.
  */
 spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat,
                           const uint16_t* W, const int32_t* draft_tokens,

@@ -1,0 +1,31 @@
+"""libspecverify: batched draft verification for speculative decoding on
+MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+
+The Python surface is a thin ctypes binding (``_binding``); every step of
+the computation runs in the HIP library.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MAX_GAMMA,
+    MAX_TREE_NODES,
+    MODE_GREEDY,
+    MODE_LMHEAD,
+    MODE_ROWSTATS,
+    MODE_SAMPLE,
+    MODE_TREE,
+    SPEC_BF16,
+    SPEC_F32,
+    SpecError,
+    lib,
+    lmhead_logits_view,
+    lmhead_project,
+    lmhead_verify,
+    new_workspace,
+    probe_probs,
+    row_stats,
+    verify_greedy,
+    verify_sample,
+    verify_tree,
+    workspace_bytes,
+)

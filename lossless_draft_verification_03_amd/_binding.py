@@ -1,0 +1,214 @@
+"""ctypes binding of libspecverify (argument marshalling only).
+
+Every function here forwards to the C ABI declared in include/specverify.h
+with device pointers taken from PyTorch tensors and the current HIP stream.
+No step of the computation runs in Python: if the shared library is not
+built this module raises on import, and there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m lossless_draft_verification_03_amd.build` "
+        "(or __graft_entry__.build()); there is no non-HIP fallback")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_EHIP = range(6)
+SPEC_F32, SPEC_BF16 = 0, 1
+MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS = range(5)
+MAX_GAMMA = 63
+MAX_TREE_NODES = 4096
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "spec_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "spec_workspace_init": (_i, [_vp, _sz, _vp]),
+    "spec_status_str": (ctypes.c_char_p, [_i]),
+    "spec_row_stats": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
+    "lmhead_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_probe_probs": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+EXPORTS = tuple(_SIGS)
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {lib.spec_status_str(status).decode()}")
+
+
+def _check(status, where):
+    if status != SPEC_OK:
+        raise SpecError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dtype_code(t):
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bf16 (bfloat16 / 16-bit bit patterns), got {t.dtype}")
+
+
+def workspace_bytes(mode, B, gamma_or_N, V, d=0):
+    return lib.spec_workspace_bytes(mode, B, gamma_or_N, V, d)
+
+
+def new_workspace(mode, B, gamma_or_N, V, d=0, device="cuda"):
+    """A zero-filled workspace for one (mode, sizes) layout."""
+    n = workspace_bytes(mode, B, gamma_or_N, V, d)
+    if n == 0:
+        raise SpecError(SPEC_EINVAL, "spec_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+_WS = {}
+
+
+def _workspace(mode, B, gN, V, d, device, ws):
+    if ws is not None:
+        return ws
+    key = (str(device), mode, B, gN, V, d)
+    w = _WS.get(key)
+    if w is None:
+        w = new_workspace(mode, B, gN, V, d, device)
+        _WS[key] = w
+    return w
+
+
+def _i32(x, device):
+    return torch.as_tensor(x, dtype=torch.int32, device=device).contiguous()
+
+
+def row_stats(logits, temperature=1.0, want=3, ws=None, out=None):
+    """Row max, sum of exp((z - max)/T) and lowest-index argmax of [rows, V]."""
+    rows, V = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty(rows, dtype=torch.float32, device=dev),
+               torch.empty(rows, dtype=torch.float64, device=dev),
+               torch.empty(rows, dtype=torch.int32, device=dev))
+    m, s, a = out
+    w = _workspace(MODE_ROWSTATS, rows, 0, V, 0, dev, ws)
+    _check(lib.spec_row_stats(_ptr(logits), dtype_code(logits), rows, V, float(temperature), want,
+                              _ptr(m), _ptr(s) if want & 1 else None, _ptr(a) if want & 2 else None,
+                              _ptr(w), w.numel(), _stream(dev)), "spec_row_stats")
+    return out
+
+
+def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, out=None):
+    """target [B, g+1, V], draft [B, g, V] -> (accept_len [B], out_tokens [B, g+1])."""
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    if draft.shape != (B, g, V) or draft.dtype != target.dtype:
+        raise ValueError("draft logits must be [B, gamma, V] with the target's dtype")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g1), dtype=torch.int32, device=dev))
+    acc, toks = out
+    w = _workspace(MODE_SAMPLE, B, g, V, 0, dev, ws)
+    _check(lib.spec_verify_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens),
+                                  _ptr(uniforms), B, g, V, float(temperature), _ptr(acc), _ptr(toks),
+                                  _ptr(w), w.numel(), _stream(dev)), "spec_verify_sample")
+    return out
+
+
+def verify_greedy(target, draft_tokens, ws=None, out=None):
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g1), dtype=torch.int32, device=dev))
+    acc, toks = out
+    w = _workspace(MODE_GREEDY, B, g, V, 0, dev, ws)
+    _check(lib.spec_verify_greedy(_ptr(target), dtype_code(target), _ptr(draft_tokens), B, g, V,
+                                  _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
+           "spec_verify_greedy")
+    return out
+
+
+def verify_tree(target, node_tokens, parent, ws=None, out=None):
+    """target [B, N, V]; parent [N] or [B, N] -> (accept_len, out_path, out_tokens)."""
+    B, N, V = target.shape
+    dev = target.device
+    stride = 0 if parent.dim() == 1 else N
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int32, device=dev))
+    acc, path, toks = out
+    w = _workspace(MODE_TREE, B, N, V, 0, dev, ws)
+    _check(lib.spec_verify_tree(_ptr(target), dtype_code(target), _ptr(node_tokens), _ptr(parent), stride,
+                                B, N, V, _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
+                                _stream(dev)), "spec_verify_tree")
+    return out
+
+
+def lmhead_project(feat, W, out=None):
+    """feat [M, d] bf16 bits, W [d, V] bf16 bits -> fp32 logits [M, V]."""
+    M, d = feat.shape
+    V = W.shape[1]
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=feat.device)
+    _check(lib.lmhead_project(_ptr(feat), M, d, _ptr(W), V, _ptr(out), _stream(feat.device)), "lmhead_project")
+    return out
+
+
+def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=None, out=None):
+    B, g = draft_tokens.shape
+    d, V = W.shape
+    dev = W.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
+    acc, toks = out
+    w = _workspace(MODE_LMHEAD, B, g, V, d, dev, ws)
+    _check(lib.lmhead_verify(_ptr(feat_t), _ptr(feat_d), _ptr(W), _ptr(draft_tokens), _ptr(uniforms), B, g, d, V,
+                             float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
+           "lmhead_verify")
+    return out
+
+
+def lmhead_logits_view(ws, B, g, V, d):
+    """The fp32 logits lmhead_verify leaves in its workspace: (target, draft).
+    They fill the last ceil256(B(2g+1) V 4) bytes of the workspace."""
+    n = workspace_bytes(MODE_LMHEAD, B, g, V, d)
+    rows = B * (2 * g + 1)
+    size = rows * V * 4
+    off = n - (size + 255) // 256 * 256
+    z = ws[off: off + size].view(torch.float32).view(rows, V)
+    return z[: B * (g + 1)].view(B, g + 1, V), z[B * (g + 1):].view(B, g, V)
+
+
+def probe_probs(target, draft, temperature, ws=None):
+    """p, q and the normalised residual (float64 [rows, V]) as the draw sees them."""
+    rows, V = target.shape
+    dev = target.device
+    p = torch.empty((rows, V), dtype=torch.float64, device=dev)
+    q = torch.empty_like(p) if draft is not None else None
+    r = torch.empty_like(p) if draft is not None else None
+    w = _workspace(MODE_ROWSTATS, 2 * rows, 0, V, 0, dev, ws)
+    _check(lib.spec_probe_probs(_ptr(target), _ptr(draft), dtype_code(target), rows, V, float(temperature),
+                                _ptr(p), _ptr(q), _ptr(r), _ptr(w), w.numel(), _stream(dev)), "spec_probe_probs")
+    return p, q, r

@@ -1,0 +1,393 @@
+// C ABI of libspecverify: argument checks, workspace layout, launches.
+// Every entry point validates its arguments before it launches anything and
+// never throws; see include/specverify.h for the contract of each call.
+#include "specverify.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sv_kernels.hpp"
+
+using namespace sv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Workspace regions; all offsets are from the workspace base.  Counters come
+// first so the zero-on-exit counters of one layout never move.
+struct Layout {
+  size_t cnt, cnt2, part, rmax, rsum, rarg, segsum, logits, total;
+  long long rows;
+  int nseg, nseg2;
+};
+
+// dt = element type of the rows the sweep reads (the sweep's segment count
+// depends on it); the public size query takes the larger (fp32) layout.
+bool make_layout(int mode, long long B, long long gN, long long V, long long d, int dt, Layout* L) {
+  memset(L, 0, sizeof(*L));
+  if (B < 1 || B > SPEC_MAX_BATCH || V < 1 || V > 0x7fffffffLL) return false;
+  long long rows = 0, seqs = 0;
+  switch (mode) {
+    case SPEC_MODE_SAMPLE:
+    case SPEC_MODE_LMHEAD:
+      if (gN < 1 || gN > SPEC_MAX_GAMMA) return false;
+      rows = B * (2 * gN + 1);
+      seqs = B;
+      break;
+    case SPEC_MODE_GREEDY:
+      if (gN < 1 || gN > SPEC_MAX_GAMMA) return false;
+      rows = B * (gN + 1);
+      break;
+    case SPEC_MODE_TREE:
+      if (gN < 1 || gN > SPEC_MAX_TREE_NODES) return false;
+      rows = B * gN;
+      break;
+    case SPEC_MODE_ROWSTATS:
+      rows = B;
+      break;
+    default:
+      return false;
+  }
+  if (mode == SPEC_MODE_LMHEAD) {
+    if (d < 64 || d % 64 != 0 || d > (1 << 20)) return false;
+    dt = DT_F32;
+  }
+  const RowSweepShape sh = row_sweep_shape((int)V, dt);
+  int seg_elems = 0;
+  const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
+  size_t o = 0;
+  L->cnt = o;    o = up(o + (size_t)rows * 4);
+  L->cnt2 = o;   o = up(o + (size_t)seqs * 4);
+  L->part = o;   o = up(o + (size_t)rows * sh.nseg * sizeof(Partial));
+  L->rmax = o;   o = up(o + (size_t)rows * 4);
+  L->rsum = o;   o = up(o + (size_t)rows * 8);
+  L->rarg = o;   o = up(o + (size_t)rows * 4);
+  L->segsum = o; o = up(o + (size_t)seqs * nseg2 * 8);
+  L->logits = o;
+  if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)V * 4);
+  L->total = o;
+  L->rows = rows;
+  L->nseg = sh.nseg;
+  L->nseg2 = nseg2;
+  return true;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool temp_const(float T, TempConst* tc) {
+  if (!(T > 0.0f) || !isfinite(T)) return false;
+  const double c = 1.4426950408889634074 / (double)T;   // log2(e) / T
+  if (!(c < 1e30)) return false;
+  float hi = (float)c;
+  if ((double)hi >= c) hi = nextafterf(hi, 0.0f);
+  tc->c_hi = hi;
+  tc->c_lo = (float)(c - (double)hi);
+  if (!(tc->c_lo > 0.0f)) tc->c_lo = 1e-30f;
+  tc->d_min = (float)(-200.0 / (double)hi);
+  tc->pad_ = 0.f;
+  tc->c64 = c;
+  return true;
+}
+
+spec_status hip_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_EHIP; }
+
+bool dtype_ok(spec_dtype dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
+
+int elem_size(spec_dtype dt) { return dt == SPEC_BF16 ? 2 : 4; }
+
+bool row_bytes_ok(long long V, spec_dtype dt) { return V * elem_size(dt) < (1LL << 31); }
+
+spec_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+  if (!ws || !aligned(ws, kAlign)) return SPEC_EWORKSPACE;
+  if (ws_bytes < L.total) return SPEC_EWORKSPACE;
+  return SPEC_OK;
+}
+
+hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long long rows1, int V,
+                     int dt, int want, const TempConst& tc, void* ws, const Layout& L, hipStream_t s) {
+  RowStatsParams p;
+  memset(&p, 0, sizeof(p));
+  const RowSweepShape sh = row_sweep_shape(V, dt);
+  p.src0 = src0;
+  p.src1 = src1;
+  p.rows0 = rows0;
+  p.rows1 = rows1;
+  p.V = V;
+  p.nseg = sh.nseg;
+  p.seg_vecs = sh.seg_vecs;
+  p.want = want;
+  p.tc = tc;
+  p.part = at<Partial>(ws, L.part);
+  p.cnt = at<unsigned>(ws, L.cnt);
+  p.out_max = at<float>(ws, L.rmax);
+  p.out_sum = at<double>(ws, L.rsum);
+  p.out_arg = at<int>(ws, L.rarg);
+  return launch_row_stats(p, dt, s);
+}
+
+spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* tokens,
+                      const float* unif, int B, int g, int V, const TempConst& tc,
+                      int32_t* accept_len, int32_t* out_tokens, void* ws, const Layout& L,
+                      hipStream_t s) {
+  hipError_t e = row_sweep(tgt, (long long)B * (g + 1), drf, (long long)B * g, V, dt, 1, tc, ws, L, s);
+  if (e != hipSuccess) return SPEC_EHIP;
+  SampleParams p;
+  memset(&p, 0, sizeof(p));
+  p.tgt = tgt;
+  p.drf = drf;
+  p.tokens = tokens;
+  p.unif = unif;
+  p.row_max = at<float>(ws, L.rmax);
+  p.row_sum = at<double>(ws, L.rsum);
+  p.B = B;
+  p.g = g;
+  p.V = V;
+  p.nseg = sample_draw_segments(V, &p.seg_elems);
+  p.tc = tc;
+  p.segsum = at<double>(ws, L.segsum);
+  p.cnt = at<unsigned>(ws, L.cnt2);
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  return hip_status(launch_sample(p, dt, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d) {
+  Layout L;
+  if (!make_layout(mode, B, gamma_or_N, V, d, DT_F32, &L)) return 0;
+  return L.total;
+}
+
+spec_status spec_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!ws || !aligned(ws, kAlign)) return SPEC_EWORKSPACE;
+  return hip_status(launch_fill_zero(ws, ws_bytes, s));
+}
+
+const char* spec_status_str(spec_status st) {
+  switch (st) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_EINVAL: return "SPEC_EINVAL: invalid size, count, pointer or scalar argument";
+    case SPEC_EDTYPE: return "SPEC_EDTYPE: unknown dtype";
+    case SPEC_EALIGN: return "SPEC_EALIGN: misaligned pointer";
+    case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace missing, misaligned or too small";
+    case SPEC_EHIP: return "SPEC_EHIP: HIP runtime error";
+  }
+  return "unknown spec_status";
+}
+
+spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V, float temperature,
+                           int want, float* out_max, double* out_sum, int32_t* out_argmax,
+                           void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (rows < 1 || V < 1 || want < 1 || want > 3 || !row_bytes_ok(V, dt)) return SPEC_EINVAL;
+  if (!logits || !out_max || ((want & 1) && !out_sum) || ((want & 2) && !out_argmax)) return SPEC_EINVAL;
+  if (!aligned(logits, 16) || !aligned(out_max, 4) || (out_sum && !aligned(out_sum, 8)) ||
+      (out_argmax && !aligned(out_argmax, 4)))
+    return SPEC_EALIGN;
+  TempConst tc;
+  memset(&tc, 0, sizeof(tc));
+  if ((want & 1) && !temp_const(temperature, &tc)) return SPEC_EINVAL;
+  Layout L;
+  if (!make_layout(SPEC_MODE_ROWSTATS, rows, 0, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  RowStatsParams p;
+  memset(&p, 0, sizeof(p));
+  const RowSweepShape sh = row_sweep_shape(V, (int)dt);
+  p.src0 = logits;
+  p.rows0 = rows;
+  p.V = V;
+  p.nseg = sh.nseg;
+  p.seg_vecs = sh.seg_vecs;
+  p.want = want;
+  p.tc = tc;
+  p.part = at<Partial>(ws, L.part);
+  p.cnt = at<unsigned>(ws, L.cnt);
+  p.out_max = out_max;
+  p.out_sum = out_sum;
+  p.out_arg = out_argmax;
+  return hip_status(launch_row_stats(p, (int)dt, s));
+}
+
+spec_status spec_verify_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
+                               const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
+                               int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
+                               void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len || !out_tokens)
+    return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || !aligned(draft_logits, 16) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  TempConst tc;
+  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
+  Layout L;
+  if (!make_layout(SPEC_MODE_SAMPLE, B, gamma, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  return sample_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc,
+                   accept_len, out_tokens, ws, L, s);
+}
+
+spec_status spec_verify_greedy(const void* target_logits, spec_dtype dt, const int32_t* draft_tokens,
+                               int B, int gamma, int V, int32_t* accept_len, int32_t* out_tokens,
+                               void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || !aligned(draft_tokens, 4) || !aligned(accept_len, 4) ||
+      !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  Layout L;
+  if (!make_layout(SPEC_MODE_GREEDY, B, gamma, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  TempConst tc;
+  memset(&tc, 0, sizeof(tc));
+  hipError_t e = row_sweep(target_logits, (long long)B * (gamma + 1), nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
+  if (e != hipSuccess) return SPEC_EHIP;
+  GreedyParams p;
+  p.arg = at<int>(ws, L.rarg);
+  p.tokens = draft_tokens;
+  p.B = B;
+  p.g = gamma;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  return hip_status(launch_greedy_finish(p, s));
+}
+
+spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int32_t* node_tokens,
+                             const int32_t* parent, int parent_batch_stride, int B, int N, int V,
+                             int32_t* accept_len, int32_t* out_path, int32_t* out_tokens, void* ws,
+                             size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || N < 1 || N > SPEC_MAX_TREE_NODES || V < 1 || !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (parent_batch_stride != 0 && parent_batch_stride != N) return SPEC_EINVAL;
+  if (!target_logits || !node_tokens || !parent || !accept_len || !out_path || !out_tokens)
+    return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || !aligned(node_tokens, 4) || !aligned(parent, 4) ||
+      !aligned(accept_len, 4) || !aligned(out_path, 4) || !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  Layout L;
+  if (!make_layout(SPEC_MODE_TREE, B, N, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  TempConst tc;
+  memset(&tc, 0, sizeof(tc));
+  hipError_t e = row_sweep(target_logits, (long long)B * N, nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
+  if (e != hipSuccess) return SPEC_EHIP;
+  TreeParams p;
+  p.arg = at<int>(ws, L.rarg);
+  p.node_tokens = node_tokens;
+  p.parent = parent;
+  p.parent_stride = parent_batch_stride;
+  p.B = B;
+  p.N = N;
+  p.accept_len = accept_len;
+  p.out_path = out_path;
+  p.out_tokens = out_tokens;
+  return hip_status(launch_tree_finish(p, s));
+}
+
+spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W, int V,
+                           float* out_logits, hipStream_t s) {
+  if (M < 1 || M > (1 << 22) || d < 64 || d % 64 != 0 || d > (1 << 20) || V < 1) return SPEC_EINVAL;
+  if (!feat || !W || !out_logits) return SPEC_EINVAL;
+  if (!aligned(feat, 16) || !aligned(W, 16) || !aligned(out_logits, 16)) return SPEC_EALIGN;
+  LmHeadParams p;
+  p.A0 = feat;
+  p.A1 = nullptr;
+  p.M0 = M;
+  p.M1 = 0;
+  p.W = W;
+  p.K = d;
+  p.N = V;
+  p.C = out_logits;
+  return hip_status(launch_lmhead(p, s));
+}
+
+spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
+                          const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d,
+                          int V, float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                          size_t ws_bytes, hipStream_t s) {
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 ||
+      (long long)V * 4 >= (1LL << 31))
+    return SPEC_EINVAL;
+  if (d < 64 || d % 64 != 0 || d > (1 << 20)) return SPEC_EINVAL;
+  if (!target_feat || !draft_feat || !W || !draft_tokens || !uniforms || !accept_len || !out_tokens)
+    return SPEC_EINVAL;
+  if (!aligned(target_feat, 16) || !aligned(draft_feat, 16) || !aligned(W, 16) ||
+      !aligned(draft_tokens, 4) || !aligned(uniforms, 4) || !aligned(accept_len, 4) ||
+      !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  TempConst tc;
+  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
+  Layout L;
+  if (!make_layout(SPEC_MODE_LMHEAD, B, gamma, V, d, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  float* Z = at<float>(ws, L.logits);
+  LmHeadParams p;
+  p.A0 = target_feat;
+  p.A1 = draft_feat;
+  p.M0 = B * (gamma + 1);
+  p.M1 = B * gamma;
+  p.W = W;
+  p.K = d;
+  p.N = V;
+  p.C = Z;
+  if (launch_lmhead(p, s) != hipSuccess) return SPEC_EHIP;
+  const float* Zd = Z + (size_t)B * (gamma + 1) * (size_t)V;
+  return sample_on(Z, Zd, DT_F32, draft_tokens, uniforms, B, gamma, V, tc, accept_len, out_tokens, ws,
+                   L, s);
+}
+
+spec_status spec_probe_probs(const void* target_logits, const void* draft_logits, spec_dtype dt, int rows,
+                             int V, float temperature, double* out_p, double* out_q, double* out_resid,
+                             void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (rows < 1 || rows > SPEC_MAX_BATCH / 2 || V < 1 || !row_bytes_ok(V, dt)) return SPEC_EINVAL;
+  if (!target_logits || !out_p || (!draft_logits && (out_q || out_resid))) return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || (draft_logits && !aligned(draft_logits, 16)) || !aligned(out_p, 8) ||
+      (out_q && !aligned(out_q, 8)) || (out_resid && !aligned(out_resid, 8)))
+    return SPEC_EALIGN;
+  TempConst tc;
+  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
+  Layout L;
+  if (!make_layout(SPEC_MODE_ROWSTATS, 2LL * rows, 0, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  hipError_t e = row_sweep(target_logits, rows, draft_logits, draft_logits ? rows : 0, V, (int)dt, 1, tc, ws,
+                           L, s);
+  if (e != hipSuccess) return SPEC_EHIP;
+  ProbeParams p;
+  p.tgt = target_logits;
+  p.drf = draft_logits;
+  p.row_max = at<float>(ws, L.rmax);
+  p.row_sum = at<double>(ws, L.rsum);
+  p.rows = rows;
+  p.V = V;
+  p.tc = tc;
+  p.out_p = out_p;
+  p.out_q = out_q;
+  p.out_resid = out_resid;
+  return hip_status(launch_probe(p, (int)dt, s));
+}
+
+}  // extern "C"

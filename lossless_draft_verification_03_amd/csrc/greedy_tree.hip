@@ -1,0 +1,202 @@
+// Greedy and greedy-tree verification, after the row sweep has produced the
+// lowest-index argmax of every target row.
+//
+// Pages: "EAGLE-3 speculative decoding review", "Does Using a Small Model's
+// Answer Reduce Quality?" (accept iff the draft equals the target's argmax;
+// otherwise emit the target token and stop), "EAGLE-2: Does Every Context Need
+// the Same Draft Tree?" (a node sees only the shared prefix and its own
+// ancestors) and "The Complete EAGLE-3 Inference Process" (4. Strict
+// Acceptance: the longest prefix matching the target's choices); "EAGLE
+// math", "EAGLE-2: dynamic draft trees".
+#include "sv_kernels.hpp"
+
+#include <limits.h>
+
+namespace sv {
+
+namespace {
+
+constexpr int SPEC_TREE_LDS_NODES = 4096;   // = SPEC_MAX_TREE_NODES
+
+// One wavefront per sequence: lane i compares draft i with argmax of row i;
+// a ballot gives the first mismatch.
+__global__ __launch_bounds__(kBlock) void k_greedy_finish(GreedyParams P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long b = (long long)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (b >= P.B) return;
+  const int g = P.g;
+  const int* arg = P.arg + b * (g + 1);
+  const int* x = P.tokens + b * g;
+  const int xi = lane < g ? x[lane] : 0;
+  const int ai = lane <= g ? arg[lane] : 0;
+  const unsigned long long mm = __ballot(lane < g && xi != ai);
+  const int j = mm ? (int)__ffsll((long long)mm) - 1 : g;
+  const int aj = __shfl(ai, j, kWave);
+  int* out = P.out_tokens + b * (g + 1);
+  if (lane <= g) out[lane] = lane < j ? xi : (lane == j ? aj : -1);
+  if (lane == 0) P.accept_len[b] = j;
+}
+
+// One workgroup per sequence.  ok(n) = ok(parent(n)) and tok(n) ==
+// argmax(parent(n)), depth(n) = depth(parent(n)) + 1, both resolved by
+// pointer jumping over the ancestor links in LDS (log2 N rounds).  The
+// accepted node maximises (depth, -index) over ok nodes.
+__global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
+  __shared__ short s_anc[2][SPEC_TREE_LDS_NODES];
+  __shared__ unsigned char s_ok[2][SPEC_TREE_LDS_NODES];
+  __shared__ short s_dep[2][SPEC_TREE_LDS_NODES];
+  __shared__ short s_par[SPEC_TREE_LDS_NODES];
+  __shared__ int s_bad;
+  __shared__ int s_key[kBlock / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const long long b = blockIdx.x;
+  const int N = P.N;
+  const int* par = P.parent + b * P.parent_stride;
+  const int* tok = P.node_tokens + b * N;
+  const int* arg = P.arg + b * N;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  for (int n = tid; n < N; n += kBlock) {
+    const int p = par[n];
+    const bool valid = n == 0 ? p == -1 : (p >= 0 && p < n);
+    if (!valid) s_bad = 1;
+    s_par[n] = (short)(n == 0 ? 0 : (valid ? p : 0));
+  }
+  __syncthreads();
+  int* out_path = P.out_path + b * N;
+  int* out_tok = P.out_tokens + b * N;
+  if (s_bad) {
+    for (int n = tid; n < N; n += kBlock) {
+      out_path[n] = -1;
+      out_tok[n] = -1;
+    }
+    if (tid == 0) P.accept_len[b] = -1;
+    return;
+  }
+  for (int n = tid; n < N; n += kBlock) {
+    const int p = s_par[n];
+    s_anc[0][n] = (short)p;
+    s_ok[0][n] = n == 0 ? 1 : (unsigned char)(tok[n] == arg[p]);
+    s_dep[0][n] = (short)(n == 0 ? 0 : 1);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int span = 1; span < N; span <<= 1) {
+    for (int n = tid; n < N; n += kBlock) {
+      const int a = s_anc[cur][n];
+      s_anc[cur ^ 1][n] = s_anc[cur][a];
+      s_ok[cur ^ 1][n] = s_ok[cur][n] & s_ok[cur][a];
+      s_dep[cur ^ 1][n] = (short)(s_dep[cur][n] + s_dep[cur][a]);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  // key = depth * 4096 + (4095 - n): the maximum is the deepest ok node with
+  // the lowest index.
+  int key = -1;
+  for (int n = tid; n < N; n += kBlock)
+    if (s_ok[cur][n]) key = max(key, (int)s_dep[cur][n] * 4096 + (4095 - n));
+  key = wave_max_i(key);
+  if (lane == 0) s_key[wid] = key;
+  __syncthreads();
+  key = max(max(s_key[0], s_key[1]), max(s_key[2], s_key[3]));
+  const int nstar = 4095 - (key & 4095);
+  const int depth = key >> 12;
+  for (int n = tid; n < N; n += kBlock) {
+    out_path[n] = -1;
+    out_tok[n] = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int m = nstar;
+    for (int d = depth - 1; d >= 0; --d) {
+      out_path[d] = m;
+      out_tok[d] = tok[m];
+      m = s_par[m];
+    }
+    out_tok[depth] = arg[nstar];
+    P.accept_len[b] = depth;
+  }
+}
+
+// p, q and the normalised residual of row pairs, through the same element
+// function as the sampling draw.  Test probe; one workgroup per row.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_probe(ProbeParams P) {
+  __shared__ double sh4[4];
+  const int tid = threadIdx.x;
+  const long long r = blockIdx.x;
+  const long long V = P.V;
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  const char* t = static_cast<const char*>(P.tgt) + r * V * ES;
+  const char* d = P.drf ? static_cast<const char*>(P.drf) + r * V * ES : nullptr;
+  const float Mt = P.row_max[r];
+  const double St = P.row_sum[r];
+  float Md = 0.f;
+  double Sd = 1.0, rho = 0.0;
+  if (d) {
+    Md = P.row_max[P.rows + r];
+    Sd = P.row_sum[P.rows + r];
+    rho = St / Sd;
+  }
+  const float rho_hi = (float)rho, rho_lo = (float)(rho - (double)rho_hi);
+  double part = 0.0;
+  for (long long e = tid; e < V; e += kBlock) {
+    const float et = exp_rel<DT>(load_elem<DT>(t, e), Mt, P.tc);
+    P.out_p[r * V + e] = (double)et / St;
+    if (d) {
+      const float ed = exp_rel<DT>(load_elem<DT>(d, e), Md, P.tc);
+      if (P.out_q) P.out_q[r * V + e] = (double)ed / Sd;
+      float w = fmaf(-ed, rho_hi, et);
+      w = fmaxf(fmaf(-ed, rho_lo, w), 0.f);
+      part += (double)w;
+      if (P.out_resid) P.out_resid[r * V + e] = (double)w;
+    }
+  }
+  if (!d || !P.out_resid) return;
+  part = wave_sum(part);
+  if ((tid & (kWave - 1)) == 0) sh4[tid / kWave] = part;
+  __syncthreads();
+  const double tot = (sh4[0] + sh4[1]) + (sh4[2] + sh4[3]);
+  const double inv = tot > 0.0 ? 1.0 / tot : 0.0;
+  for (long long e = tid; e < V; e += kBlock) P.out_resid[r * V + e] *= inv;
+}
+
+__global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = i; k < n16; k += stride) p[k] = make_uint4(0, 0, 0, 0);
+  if (i < ntail) tail[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_greedy_finish(const GreedyParams& p, hipStream_t s) {
+  const long long grid = ((long long)p.B + 3) / 4;
+  hipLaunchKernelGGL(k_greedy_finish, dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_finish(const TreeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_tree_finish, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe(const ProbeParams& p, int dt, hipStream_t s) {
+  if (dt == DT_BF16) hipLaunchKernelGGL(k_probe<DT_BF16>, dim3((unsigned)p.rows), dim3(kBlock), 0, s, p);
+  else hipLaunchKernelGGL(k_probe<DT_F32>, dim3((unsigned)p.rows), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint4*>(ptr), n16,
+                     static_cast<unsigned char*>(ptr) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,111 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+// ------------------------------------------------------------ row sweep
+// One pass over every row of up to two logit tensors (rows0 rows of the
+// first, rows1 of the second, both [*, V]).  Each wave reduces one segment of
+// one row; the last wave to finish a row merges the row's segments.
+struct RowStatsParams {
+  const void* src0;
+  const void* src1;
+  long long rows0;
+  long long rows1;
+  int V;
+  int nseg;       // wave segments per row
+  int seg_vecs;   // full 16-byte vectors per segment
+  int want;       // bit 0: max/sum, bit 1: argmax
+  TempConst tc;
+  Partial* part;  // [rows][nseg]
+  unsigned* cnt;  // [rows], zero on entry, zero on exit
+  float* out_max; // [rows]
+  double* out_sum;// [rows] (want & 1)
+  int* out_arg;   // [rows] (want & 2)
+};
+
+struct RowSweepShape {
+  int nseg;
+  int seg_vecs;
+};
+RowSweepShape row_sweep_shape(int V, int dt);
+hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);
+
+// ---------------------------------------------------------- sampling
+// Accept scan, residual / bonus segment sums and (in the last workgroup of
+// each sequence) the inverse-CDF draw.
+struct SampleParams {
+  const void* tgt;        // [B, g+1, V]
+  const void* drf;        // [B, g, V]
+  const int* tokens;      // [B, g]
+  const float* unif;      // [B, g+1]
+  const float* row_max;   // [B(g+1) target rows, then B g draft rows]
+  const double* row_sum;
+  int B, g, V;
+  int nseg;               // draw segments per row
+  int seg_elems;          // elements per draw segment (multiple of 8)
+  TempConst tc;
+  double* segsum;         // [B][nseg]
+  unsigned* cnt;          // [B]
+  int* accept_len;        // [B]
+  int* out_tokens;        // [B, g+1]
+};
+int sample_draw_segments(int V, int* seg_elems);
+hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s);
+
+// ---------------------------------------------------------- greedy / tree
+struct GreedyParams {
+  const int* arg;         // [B(g+1)] row argmax
+  const int* tokens;      // [B, g]
+  int B, g;
+  int* accept_len;
+  int* out_tokens;        // [B, g+1]
+};
+hipError_t launch_greedy_finish(const GreedyParams& p, hipStream_t s);
+
+struct TreeParams {
+  const int* arg;         // [B N] row argmax
+  const int* node_tokens; // [B, N]
+  const int* parent;      // [N] or [B, N]
+  int parent_stride;      // 0 or N
+  int B, N;
+  int* accept_len;
+  int* out_path;          // [B, N]
+  int* out_tokens;        // [B, N]
+};
+hipError_t launch_tree_finish(const TreeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------- probe
+struct ProbeParams {
+  const void* tgt;        // [rows, V]
+  const void* drf;        // [rows, V] or null
+  const float* row_max;   // [rows] target, then [rows] draft
+  const double* row_sum;
+  int rows, V;
+  TempConst tc;
+  double* out_p;
+  double* out_q;
+  double* out_resid;
+};
+hipError_t launch_probe(const ProbeParams& p, int dt, hipStream_t s);
+
+// ---------------------------------------------------------- utilities
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+// ---------------------------------------------------------- LM head
+struct LmHeadParams {
+  const uint16_t* A0;     // [M0, K] bf16
+  const uint16_t* A1;     // [M1, K] bf16 (may be null)
+  int M0, M1;
+  const uint16_t* W;      // [K, N] bf16, N innermost
+  int K, N;
+  float* C;               // [M0 + M1, N] fp32
+};
+hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s);
+
+}  // namespace sv
