@@ -154,7 +154,7 @@ def main():
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "mean_accept_len": round(accepted, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_row_stats<bf16,sum>", "achieved": round(k1_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "spec_row_stats over the 960 rows: k_row_stats<bf16,sum> + k_row_merge", "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "bytes_per_launch": k1_bytes,
                      "avg_launch_us": round(k1_ms * 1e3, 2)},

@@ -39,11 +39,10 @@
  *  - Calls are asynchronous on stream `s` (NULL = the default stream) and
  *    allocate nothing.  Outputs are valid once the stream has synchronised.
  *  - Workspace: `ws` is caller-owned device memory of at least
- *    spec_workspace_bytes(...) bytes, 256-byte aligned.  It must be zero-filled
- *    before its first use (spec_workspace_init does that); every call leaves
- *    its counters zeroed again.  A workspace belongs to one (mode, sizes)
- *    layout: zero it again before using it for another.  Two calls may run
- *    concurrently only with distinct workspaces.
+ *    spec_workspace_bytes(...) bytes, 256-byte aligned, holding per-row
+ *    partial statistics between the kernels of one call.  It needs no
+ *    initialisation: a call writes every byte it reads.  Calls that overlap
+ *    in time must use distinct workspaces.
  *  - Errors: argument errors are reported synchronously, before anything is
  *    launched, as a non-zero spec_status.  A failed launch reports
  *    SPEC_EHIP.  Data-dependent conditions that can only be seen on the
@@ -85,13 +84,15 @@ typedef enum {
 #define SPEC_MAX_GAMMA 63       /* one 64-wide wavefront lane per position   */
 #define SPEC_MAX_TREE_NODES 4096
 #define SPEC_MAX_BATCH (1 << 20)
+#define SPEC_MAX_SAMPLE_VOCAB (1 << 25)   /* V limit of the sampling calls */
 
 /* Bytes of workspace the call of the given mode needs for these sizes
  * (0 when an argument is out of range).  d is used by SPEC_MODE_LMHEAD only.
  * The LMHEAD workspace holds the float32 logits of all B(2*gamma+1) rows. */
 size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d);
 
-/* Zero-fill a workspace (a device fill kernel; graph-capture safe). */
+/* Zero-fill a workspace (a device fill kernel; graph-capture safe).  Not
+ * required before use; offered for callers that poison-check buffers. */
 spec_status spec_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
 
 /* Human-readable name of a status code (static storage). */
@@ -132,7 +133,8 @@ spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V,
  * accept_len    [B] int32 out: j = number of accepted drafts (0..gamma).
  * out_tokens    [B, gamma+1] int32 out: x_0..x_{j-1}, then the resampled
  *               (j < gamma) or bonus (j = gamma) token, then -1 padding.
- * 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= B <= SPEC_MAX_BATCH, 1 <= V < 2^31.
+ * 1 <= gamma <= SPEC_MAX_GAMMA, 1 <= B <= SPEC_MAX_BATCH,
+ * 1 <= V <= SPEC_MAX_SAMPLE_VOCAB.
  * Workspace: spec_workspace_bytes(SPEC_MODE_SAMPLE, B, gamma, V, 0).
  */
 spec_status spec_verify_sample(const void* target_logits, const void* draft_logits,

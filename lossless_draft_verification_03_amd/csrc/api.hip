@@ -19,10 +19,11 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Workspace regions; all offsets are from the workspace base.  Counters come
-// first so the zero-on-exit counters of one layout never move.
+// Workspace regions; all offsets are from the workspace base.  Every region
+// is fully written before it is read within one call, so a workspace needs
+// no initialisation and can be shared by calls of any layout (one at a time).
 struct Layout {
-  size_t cnt, cnt2, part, rmax, rsum, rarg, segsum, logits, total;
+  size_t info, part, rmax, rsum, rarg, segsum, logits, total;
   long long rows;
   int nseg, nseg2;
 };
@@ -62,8 +63,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   int seg_elems = 0;
   const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
   size_t o = 0;
-  L->cnt = o;    o = up(o + (size_t)rows * 4);
-  L->cnt2 = o;   o = up(o + (size_t)seqs * 4);
+  L->info = o;   o = up(o + (size_t)seqs * sizeof(DrawInfo));
   L->part = o;   o = up(o + (size_t)rows * sh.nseg * sizeof(Partial));
   L->rmax = o;   o = up(o + (size_t)rows * 4);
   L->rsum = o;   o = up(o + (size_t)rows * 8);
@@ -127,7 +127,6 @@ hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long l
   p.want = want;
   p.tc = tc;
   p.part = at<Partial>(ws, L.part);
-  p.cnt = at<unsigned>(ws, L.cnt);
   p.out_max = at<float>(ws, L.rmax);
   p.out_sum = at<double>(ws, L.rsum);
   p.out_arg = at<int>(ws, L.rarg);
@@ -138,14 +137,28 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
                       const float* unif, int B, int g, int V, const TempConst& tc,
                       int32_t* accept_len, int32_t* out_tokens, void* ws, const Layout& L,
                       hipStream_t s) {
-  hipError_t e = row_sweep(tgt, (long long)B * (g + 1), drf, (long long)B * g, V, dt, 1, tc, ws, L, s);
-  if (e != hipSuccess) return SPEC_EHIP;
+  RowStatsParams r;
+  memset(&r, 0, sizeof(r));
+  const RowSweepShape sh = row_sweep_shape(V, dt);
+  r.src0 = tgt;
+  r.src1 = drf;
+  r.rows0 = (long long)B * (g + 1);
+  r.rows1 = (long long)B * g;
+  r.V = V;
+  r.nseg = sh.nseg;
+  r.seg_vecs = sh.seg_vecs;
+  r.want = 1;
+  r.tc = tc;
+  r.part = at<Partial>(ws, L.part);
+  if (launch_row_sweep(r, dt, s) != hipSuccess) return SPEC_EHIP;
   SampleParams p;
   memset(&p, 0, sizeof(p));
   p.tgt = tgt;
   p.drf = drf;
   p.tokens = tokens;
   p.unif = unif;
+  p.part = r.part;
+  p.nseg_rows = sh.nseg;
   p.row_max = at<float>(ws, L.rmax);
   p.row_sum = at<double>(ws, L.rsum);
   p.B = B;
@@ -153,8 +166,8 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
   p.V = V;
   p.nseg = sample_draw_segments(V, &p.seg_elems);
   p.tc = tc;
+  p.info = at<DrawInfo>(ws, L.info);
   p.segsum = at<double>(ws, L.segsum);
-  p.cnt = at<unsigned>(ws, L.cnt2);
   p.accept_len = accept_len;
   p.out_tokens = out_tokens;
   return hip_status(launch_sample(p, dt, s));
@@ -214,7 +227,6 @@ spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V, f
   p.want = want;
   p.tc = tc;
   p.part = at<Partial>(ws, L.part);
-  p.cnt = at<unsigned>(ws, L.cnt);
   p.out_max = out_max;
   p.out_sum = out_sum;
   p.out_arg = out_argmax;
@@ -226,7 +238,8 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
                                void* ws, size_t ws_bytes, hipStream_t s) {
   if (!dtype_ok(dt)) return SPEC_EDTYPE;
-  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || !row_bytes_ok(V, dt))
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
+      !row_bytes_ok(V, dt))
     return SPEC_EINVAL;
   if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len || !out_tokens)
     return SPEC_EINVAL;
@@ -326,8 +339,7 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
                           const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d,
                           int V, float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
                           size_t ws_bytes, hipStream_t s) {
-  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 ||
-      (long long)V * 4 >= (1LL << 31))
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB)
     return SPEC_EINVAL;
   if (d < 64 || d % 64 != 0 || d > (1 << 20)) return SPEC_EINVAL;
   if (!target_feat || !draft_feat || !W || !draft_tokens || !uniforms || !accept_len || !out_tokens)

@@ -17,8 +17,11 @@
 // a = fl(z c_lo + fl(z c_hi - K)) the exponent of every element carries both
 // halves of c = log2(e)/T, so no temperature bias enters; the constant
 // offset kappa = m c - K is removed in fp64 at the end.  Four fp32
-// accumulators per lane, fp64 from the lane level up.  The last wave to
-// finish a row merges the row's segment partials in segment order in fp64.
+// accumulators per lane, fp64 from the lane level up.  Every wave writes one
+// partial (m, sum, argmax) and exits: there is no handoff between waves
+// inside the kernel (an agent-scope release/acquire per wave costs an L2
+// write-back and invalidate on this part).  A second, small kernel merges a
+// row's partials in segment order in fp64 after the kernel boundary.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -35,7 +38,10 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
   constexpr int EPV = 16 / ES;
   const float NEG_INF = -__builtin_huge_valf();
   const int lane = threadIdx.x & (kWave - 1);
-  const long long unit = (long long)blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
+  // the wave index is uniform across the wave; say so, so that everything
+  // derived from it (row, segment, buffer descriptor) lives in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const long long unit = (long long)blockIdx.x * (kBlock / kWave) + wave;
   const long long rows = P.rows0 + P.rows1;
   if (unit >= rows * P.nseg) return;
   const long long r = unit / P.nseg;
@@ -53,17 +59,27 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
   const int nv = ve > vs ? (int)(ve - vs) : 0;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base + vs * 16, (uint32_t)nv * 16u);
 
+  // Issue every load before using any: the offset is clamped into the
+  // segment (never past it), and vectors beyond the segment are masked to
+  // -inf afterwards, so a lane always has kVPT loads in flight.
+  v4i raw[kVPT];
+  if (nv > 0) {
+#pragma unroll
+    for (int k = 0; k < kVPT; ++k) {
+      const int q = min(k * kWave + lane, nv - 1);
+      raw[k] = load16(rsrc, (uint32_t)q * 16u);
+    }
+  }
+  const int neg_pat = DT == DT_BF16 ? (int)0xff80ff80u : (int)0xff800000u;
   float z[kVPT][EPV];
 #pragma unroll
   for (int k = 0; k < kVPT; ++k) {
-    const int q = k * kWave + lane;
-    if (q < nv) {
-      const v4i v = load16(rsrc, (uint32_t)q * 16u);
-      unpack<DT>(v, z[k]);
-    } else {
+    if ((k + 1) * kWave > nv) {             // wave-uniform: only the tail vectors
+      const bool valid = k * kWave + lane < nv;
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) z[k][i] = NEG_INF;
+      for (int q = 0; q < 4; ++q) raw[k][q] = valid ? raw[k][q] : neg_pat;
     }
+    unpack<DT>(raw[k], z[k]);
   }
   // Row head / tail elements outside whole vectors (segment 0 only).
   float ze = NEG_INF;
@@ -125,21 +141,23 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
     }
   }
 
-  Partial* part = P.part + r * P.nseg;
-  unsigned old = 0;
   if (lane == 0) {
     Partial pp;
     pp.m = M;
     pp.arg = idx;
     pp.s = S;
-    part[s] = pp;
-    old = count_arrival(P.cnt + r);
+    P.part[r * P.nseg + s] = pp;
   }
-  old = __shfl(old, 0, kWave);
-  if (old != (unsigned)(P.nseg - 1)) return;
+}
 
-  // Last wave of row r: merge the segment partials in segment order.
-  acquire_agent();
+// One wave per row: merge the row's segment partials in segment order.
+template <int WANT>
+__global__ __launch_bounds__(kBlock) void k_row_merge(RowStatsParams P) {
+  const float NEG_INF = -__builtin_huge_valf();
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long r = (long long)blockIdx.x * (kBlock / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (r >= P.rows0 + P.rows1) return;
+  const Partial* part = P.part + r * P.nseg;
   float Mr = NEG_INF;
   for (int t = lane; t < P.nseg; t += kWave) Mr = fmaxf(Mr, part[t].m);
   Mr = wave_max(Mr);
@@ -158,21 +176,33 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
     P.out_max[r] = Mr;
     if constexpr ((WANT & 1) != 0) P.out_sum[r] = Sr;
     if constexpr ((WANT & 2) != 0) P.out_arg[r] = ar == INT_MAX ? 0 : ar;
-    P.cnt[r] = 0u;
   }
 }
 
 template <int DT>
 hipError_t launch_dt(const RowStatsParams& p, hipStream_t s) {
-  const long long units = (p.rows0 + p.rows1) * (long long)p.nseg;
-  const long long grid = (units + (kBlock / kWave) - 1) / (kBlock / kWave);
+  const long long rows = p.rows0 + p.rows1;
+  const long long units = rows * (long long)p.nseg;
+  const long long wpb = kBlock / kWave;
+  const long long grid = (units + wpb - 1) / wpb;
+  const long long mgrid = (rows + wpb - 1) / wpb;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (p.want) {
-    case 1: hipLaunchKernelGGL((k_row_stats<DT, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_row_stats<DT, 2>), dim3((unsigned)grid), dim3(kBlock), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((k_row_stats<DT, 3>), dim3((unsigned)grid), dim3(kBlock), 0, s, p); break;
-    default: return hipErrorInvalidValue;
+    case 1:
+      hipLaunchKernelGGL((k_row_stats<DT, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+      hipLaunchKernelGGL((k_row_merge<1>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((k_row_stats<DT, 2>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+      hipLaunchKernelGGL((k_row_merge<2>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
+      break;
+    case 3:
+      hipLaunchKernelGGL((k_row_stats<DT, 3>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+      hipLaunchKernelGGL((k_row_merge<3>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -192,6 +222,17 @@ RowSweepShape row_sweep_shape(int V, int dt) {
 
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s) {
   return dt == DT_BF16 ? launch_dt<DT_BF16>(p, s) : launch_dt<DT_F32>(p, s);
+}
+
+hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s) {
+  const long long units = (p.rows0 + p.rows1) * (long long)p.nseg;
+  const long long wpb = kBlock / kWave;
+  const long long grid = (units + wpb - 1) / wpb;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL || p.want != 1) return hipErrorInvalidValue;
+  if (dt == DT_BF16) hipLaunchKernelGGL((k_row_stats<DT_BF16, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  else hipLaunchKernelGGL((k_row_stats<DT_F32, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace sv

@@ -1,6 +1,5 @@
-// Speculative sampling: accept scan, residual / bonus mass and the final
-// inverse-CDF draw, for B sequences, after the row sweep has produced every
-// row's (max, sum).
+// Speculative sampling after the row sweep: accept scan, residual / bonus
+// mass and the inverse-CDF draw, for B sequences.
 //
 // Pages: "EAGLE-3 speculative decoding review", "Speculative Decoding"
 // (3. Accept or Reject: walk the drafts left to right, stop at the first
@@ -10,15 +9,22 @@
 // speculative decoding" ((p - q)_+ and the +1 bonus token); "Speculative
 // decoding" wiki, "The mechanism".
 //
-// Grid: B x nseg workgroups.  Every workgroup of sequence b first runs the
-// accept scan (wave 0, one lane per drafted position, fp64 ratio from one
-// exponent, ballot for the first rejection j); all of them reach the same j.
-// Workgroup (b, s) then sums the draw weights of segment s of row j:
-//   j <  gamma : w = max(0, p_j - q_j)   (scaled by S_t: max(0, e_t - rho e_d))
-//   j == gamma : w = p_gamma             (scaled by S_t: e_t)
-// The last workgroup of b (agent-scope arrival count) locates the segment
-// holding u[b][gamma] * total, rescans that segment with one contiguous run
-// per lane, block-scans the lane sums in fp64 and walks the one lane's run.
+// Three kernels; the kernel boundaries are the only handoffs between
+// workgroups.
+//  k_accept     one workgroup per sequence.  Wave w takes positions w, w+4,
+//               ...: it merges the target (and draft) row partials of the
+//               position in fp64, gathers z_t(x_i) and z_d(x_i) and tests
+//               u_i < p_i(x_i)/q_i(x_i) with the ratio formed from one fp64
+//               exponent.  The first rejection j, the draw row's statistics
+//               and the accepted prefix of the output are written here.
+//  k_draw_mass  B x nseg workgroups: the draw weights of one segment of row j,
+//                 j <  gamma : w = max(0, p_j - q_j)  (as S_t w = max(0, e_t - rho e_d))
+//                 j == gamma : w = p_gamma            (as S_t w = e_t)
+//               summed in fp64.
+//  k_draw_pick  one workgroup per sequence: locate the segment holding
+//               u[b][gamma] * total, rescan it with one contiguous run per
+//               lane (weights kept in registers), block-scan the lane sums in
+//               fp64 and walk the crossing lane's run.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -27,7 +33,8 @@ namespace sv {
 
 namespace {
 
-constexpr int kDrawVPT = 4;   // vectors per lane per draw segment
+constexpr int kRun = 32;   // elements per lane in the draw's rescan (multiple of 8)
+constexpr int kSegElems = kBlock * kRun;
 
 struct DrawRow {
   const char* t;      // target row base (element 0 of the row)
@@ -47,8 +54,131 @@ __device__ __forceinline__ float weight(const DrawRow& R, float zt, float zd, co
   return fmaxf(w, 0.f);
 }
 
-// Sum of weights over elements [e_beg, e_end) of the draw row, coalesced
-// (lane-interleaved), fp64 accumulation.  Returns the lane's partial.
+template <int DT>
+__device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  const int g = P.g;
+  const long long V = P.V;
+  DrawRow R;
+  R.resid = di.j < g;
+  R.t = static_cast<const char*>(P.tgt) + ((long long)b * (g + 1) + di.j) * V * ES;
+  R.d = R.resid ? static_cast<const char*>(P.drf) + ((long long)b * g + di.j) * V * ES : R.t;
+  R.Mt = di.Mt;
+  R.Md = di.Md;
+  R.rho_hi = (float)di.rho;
+  R.rho_lo = (float)(di.rho - (double)R.rho_hi);
+  return R;
+}
+
+// Merge one row's segment partials across a wave: (max, sum relative to it).
+__device__ __forceinline__ void merge_row(const Partial* part, int nseg, const TempConst& tc, int lane,
+                                          float* M_out, double* S_out) {
+  const float NEG_INF = -__builtin_huge_valf();
+  float m = NEG_INF;
+  double sv = 0.0;
+  for (int t = lane; t < nseg; t += kWave) {
+    const Partial pp = part[t];
+    // a lane holds several partials only when nseg > 64: fold with a rescale
+    if (pp.m > m) {
+      if (m != NEG_INF) sv *= exp2_f64(((double)m - (double)pp.m) * tc.c64);
+      m = pp.m;
+      sv += pp.s;
+    } else if (pp.m != NEG_INF) {
+      sv += pp.s * exp2_f64(((double)pp.m - (double)m) * tc.c64);
+    }
+  }
+  const float M = wave_max(m);
+  if (m != NEG_INF) sv *= exp2_f64(((double)m - (double)M) * tc.c64);
+  *M_out = M;
+  *S_out = wave_sum(sv);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_accept(SampleParams P) {
+  __shared__ int sh_rej[64];
+  __shared__ int sh_bad;
+  __shared__ float sh_mt[64], sh_md[64];
+  __shared__ double sh_st[64], sh_sd[64];
+  __shared__ int sh_j;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int b = blockIdx.x;
+  const int g = P.g;
+  const long long V = P.V;
+  const long long rt0 = (long long)b * (g + 1);
+  const long long rd0 = (long long)b * g;
+  const long long rds0 = (long long)P.B * (g + 1) + rd0;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  for (int i = wid; i <= g; i += kBlock / kWave) {
+    // the token and the two gathered logits do not depend on the merge
+    int x = 0;
+    float zt = 0.f, zd = 0.f;
+    bool bad = false;
+    if (i < g) {
+      x = P.tokens[rd0 + i];
+      bad = x < 0 || (long long)x >= V;
+      if (!bad) {
+        zt = load_elem<DT>(P.tgt, (rt0 + i) * V + x);
+        zd = load_elem<DT>(P.drf, (rd0 + i) * V + x);
+      }
+    }
+    float Mt, Md = 0.f;
+    double St, Sd = 1.0;
+    merge_row(P.part + (rt0 + i) * P.nseg_rows, P.nseg_rows, P.tc, lane, &Mt, &St);
+    if (i < g) merge_row(P.part + (rds0 + i) * P.nseg_rows, P.nseg_rows, P.tc, lane, &Md, &Sd);
+    if (lane == 0) {
+      P.row_max[rt0 + i] = Mt;
+      P.row_sum[rt0 + i] = St;
+      sh_mt[i] = Mt;
+      sh_st[i] = St;
+      int rej = 0;
+      if (i < g) {
+        P.row_max[rds0 + i] = Md;
+        P.row_sum[rds0 + i] = Sd;
+        sh_md[i] = Md;
+        sh_sd[i] = Sd;
+        if (bad) {
+          sh_bad = 1;
+        } else {
+          const double et = ((double)zt - (double)Mt) * P.tc.c64;
+          const double ed = ((double)zd - (double)Md) * P.tc.c64;
+          double r;
+          if (!(et > -__builtin_huge_val())) r = 0.0;                          // p(x) = 0
+          else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();    // q(x) = 0 < p(x)
+          else r = exp2_f64(et - ed) * (Sd / St);
+          rej = !((double)P.unif[rt0 + i] < r);
+        }
+      }
+      sh_rej[i] = rej;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int j = g;
+    for (int i = 0; i < g; ++i)
+      if (sh_rej[i]) { j = i; break; }
+    if (sh_bad) j = -1;
+    sh_j = j;
+    DrawInfo di;
+    di.j = j;
+    di.Mt = j >= 0 ? sh_mt[j] : 0.f;
+    di.Md = (j >= 0 && j < g) ? sh_md[j] : 0.f;
+    di.pad_ = 0.f;
+    di.rho = (j >= 0 && j < g) ? sh_st[j] / sh_sd[j] : 0.0;
+    P.info[b] = di;
+    P.accept_len[b] = j;
+  }
+  __syncthreads();
+  const int j = sh_j;
+  int* out = P.out_tokens + rt0;
+  for (int i = tid; i <= g; i += kBlock) {
+    if (j < 0 || i > j) out[i] = -1;
+    else if (i < j) out[i] = P.tokens[rd0 + i];
+  }
+}
+
+// Sum of the draw weights over elements [e_beg, e_end) of the draw row,
+// lane-interleaved, fp64 accumulation; returns the lane's partial.
 template <int DT, bool ALIGNED>
 __device__ double segment_partial(const DrawRow& R, long long e_beg, long long e_end,
                                   const TempConst& tc, int tid) {
@@ -56,14 +186,26 @@ __device__ double segment_partial(const DrawRow& R, long long e_beg, long long e
   constexpr int EPV = 16 / ES;
   double acc = 0.0;
   if constexpr (ALIGNED) {
+    // A segment is at most kBlock * KV whole vectors; every lane issues its
+    // KV loads (offsets clamped into the segment) before computing.
+    constexpr int KV = kRun / EPV;
     const int nvec = (int)((e_end - e_beg) / EPV);
+    if (nvec <= 0) return 0.0;
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + e_beg * ES, (uint32_t)nvec * 16u);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.resid ? R.d + e_beg * ES : R.t + e_beg * ES,
-                                                (uint32_t)nvec * 16u);
-    for (int q = tid; q < nvec; q += kBlock) {
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + e_beg * ES, (uint32_t)nvec * 16u);
+    v4i vt[KV], vd[KV];
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      const uint32_t off = (uint32_t)min(k * kBlock + tid, nvec - 1) * 16u;
+      vt[k] = load16(rt, off);
+      if (R.resid) vd[k] = load16(rd, off);
+    }
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      if (k * kBlock + tid >= nvec) continue;
       float zt[EPV], zd[EPV];
-      unpack<DT>(load16(rt, (uint32_t)q * 16u), zt);
-      if (R.resid) unpack<DT>(load16(rd, (uint32_t)q * 16u), zd);
+      unpack<DT>(vt[k], zt);
+      if (R.resid) unpack<DT>(vd[k], zd);
 #pragma unroll
       for (int i = 0; i < EPV; ++i) acc += (double)weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
     }
@@ -89,224 +231,194 @@ __device__ double block_sum(double x, double* sh4, int tid) {
 }
 
 template <int DT, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_sample(SampleParams P) {
+__global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
+  __shared__ double sh4[4];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / P.nseg, s = blockIdx.x - b * P.nseg;
+  const DrawInfo di = P.info[b];
+  if (di.j < 0) return;                       // uniform
+  const DrawRow R = draw_row<DT>(P, b, di);
+  const long long V = P.V;
+  const long long sb = (long long)s * P.seg_elems;
+  const long long se = sb + P.seg_elems < V ? sb + P.seg_elems : V;
+  const double part = block_sum(segment_partial<DT, ALIGNED>(R, sb, se, P.tc, tid), sh4, tid);
+  if (tid == 0) P.segsum[(long long)b * P.nseg + s] = part;
+}
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
-  __shared__ int sh_j;
-  __shared__ int sh_last;
   __shared__ double sh4[4];
   __shared__ double sh_wtot[4];
   __shared__ int sh_first[4];
   __shared__ long long sh_y;
   __shared__ double sh_base, sh_thr;
   __shared__ int sh_k, sh_fallback;
-
+  extern __shared__ double sh_seg[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int b = blockIdx.x / P.nseg, s = blockIdx.x - b * P.nseg;
+  const int b = blockIdx.x;
   const int g = P.g;
   const long long V = P.V;
-  const long long rt0 = (long long)b * (g + 1);              // target rows of b
-  const long long rd0s = (long long)P.B * (g + 1) + (long long)b * g;   // draft rows in stats
-  const long long rd0 = (long long)b * g;                    // draft rows in the tensor
-  const TempConst tc = P.tc;
-
-  // ---- accept scan: lane i tests drafted position i
-  if (wid == 0) {
-    bool rej = false, bad = false;
-    if (lane < g) {
-      const int x = P.tokens[rd0 + lane];
-      if (x < 0 || (long long)x >= V) {
-        bad = true;
-      } else {
-        const float zt = load_elem<DT>(P.tgt, (rt0 + lane) * V + x);
-        const float zd = load_elem<DT>(P.drf, (rd0 + lane) * V + x);
-        const double et = ((double)zt - (double)P.row_max[rt0 + lane]) * tc.c64;
-        const double ed = ((double)zd - (double)P.row_max[rd0s + lane]) * tc.c64;
-        double r;
-        if (!(et > -__builtin_huge_val())) r = 0.0;                 // p(x) = 0
-        else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();  // q(x) = 0
-        else r = exp2_f64(et - ed) * (P.row_sum[rd0s + lane] / P.row_sum[rt0 + lane]);
-        const double u = (double)P.unif[rt0 + lane];
-        rej = !(u < r);
-      }
-    }
-    const unsigned long long mb = __ballot(bad);
-    const unsigned long long mr = __ballot(rej);
-    if (lane == 0) sh_j = mb ? -1 : (mr ? (int)__ffsll((long long)mr) - 1 : g);
-  }
-  __syncthreads();
-  const int j = sh_j;
-
-  DrawRow R;
-  R.resid = false;
-  R.t = R.d = nullptr;
-  R.Mt = R.Md = 0.f;
-  R.rho_hi = R.rho_lo = 0.f;
-  if (j >= 0) {
-    R.resid = j < g;
-    R.t = static_cast<const char*>(P.tgt) + (rt0 + j) * V * ES;
-    R.Mt = P.row_max[rt0 + j];
-    if (R.resid) {
-      R.d = static_cast<const char*>(P.drf) + (rd0 + j) * V * ES;
-      R.Md = P.row_max[rd0s + j];
-      const double rho = P.row_sum[rt0 + j] / P.row_sum[rd0s + j];
-      R.rho_hi = (float)rho;
-      R.rho_lo = (float)(rho - (double)R.rho_hi);
-    }
-  }
-
-  // ---- pass 1: this workgroup's segment mass
-  const long long sb = (long long)s * P.seg_elems;
-  const long long se = sb + P.seg_elems < V ? sb + P.seg_elems : V;
-  double part = 0.0;
-  if (j >= 0) part = segment_partial<DT, ALIGNED>(R, sb, se, tc, tid);
-  part = block_sum(part, sh4, tid);
-  if (tid == 0) {
-    P.segsum[(long long)b * P.nseg + s] = part;
-    sh_last = count_arrival(P.cnt + b) == (unsigned)(P.nseg - 1);
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  acquire_agent();
-
-  int* out = P.out_tokens + rt0;
-  if (j < 0) {
-    for (int i = tid; i <= g; i += kBlock) out[i] = -1;
-    if (tid == 0) {
-      P.accept_len[b] = -1;
-      P.cnt[b] = 0u;
-    }
-    return;
-  }
-
-  // ---- locate the segment holding u * total (thread 0, segment order)
+  const DrawInfo di = P.info[b];
+  if (di.j < 0) return;                       // k_accept already wrote -1s
+  DrawRow R = draw_row<DT>(P, b, di);
+  const long long ubase = (long long)b * (g + 1);
   const double* seg = P.segsum + (long long)b * P.nseg;
+  for (int t = tid; t < P.nseg; t += kBlock) sh_seg[t] = seg[t];
+  __syncthreads();
   if (tid == 0) {
     double total = 0.0;
-    for (int t = 0; t < P.nseg; ++t) total += seg[t];
+    for (int t = 0; t < P.nseg; ++t) total += sh_seg[t];
     sh_fallback = total > 0.0 ? 0 : 1;
-    sh_thr = (double)P.unif[rt0 + g] * total;
+    sh_thr = (double)P.unif[ubase + g] * total;
   }
   __syncthreads();
   if (sh_fallback) {
     // A zero residual cannot follow a rejection in exact arithmetic; if
     // rounding produces one, draw from p_j (this workgroup recomputes the
-    // row's bonus-style segment masses alone).
+    // row's segment masses alone).
     R.resid = false;
+    R.d = R.t;
     for (int t = 0; t < P.nseg; ++t) {
       const long long b0 = (long long)t * P.seg_elems;
       const long long b1 = b0 + P.seg_elems < V ? b0 + P.seg_elems : V;
-      const double m = block_sum(segment_partial<DT, ALIGNED>(R, b0, b1, tc, tid), sh4, tid);
-      if (tid == 0) P.segsum[(long long)b * P.nseg + t] = m;
+      const double m = block_sum(segment_partial<DT, ALIGNED>(R, b0, b1, P.tc, tid), sh4, tid);
+      if (tid == 0) sh_seg[t] = m;
     }
     __syncthreads();
     if (tid == 0) {
       double total = 0.0;
-      for (int t = 0; t < P.nseg; ++t) total += seg[t];
-      sh_thr = (double)P.unif[rt0 + g] * total;
+      for (int t = 0; t < P.nseg; ++t) total += sh_seg[t];
+      sh_thr = (double)P.unif[ubase + g] * total;
     }
     __syncthreads();
   }
   if (tid == 0) {
     const double thr = sh_thr;
-    double acc = 0.0;
-    int k = -1, lastpos = -1;
-    double lastbase = 0.0;
+    double acc = 0.0, lastbase = 0.0;
+    int k = -1, lastpos = 0;
     for (int t = 0; t < P.nseg; ++t) {
-      const double m = seg[t];
+      const double m = sh_seg[t];
       if (m > 0.0 && acc + m > thr) { k = t; break; }
       if (m > 0.0) { lastpos = t; lastbase = acc; }
       acc += m;
     }
     if (k >= 0) { sh_k = k; sh_base = acc; sh_fallback = 0; }
     else { sh_k = lastpos; sh_base = lastbase; sh_fallback = 1; }   // rounding: last positive segment
+    sh_y = -1;
   }
   __syncthreads();
-  const int k = sh_k;
-  const long long kb = (long long)k * P.seg_elems;
+  const long long kb = (long long)sh_k * P.seg_elems;
   const long long ke = kb + P.seg_elems < V ? kb + P.seg_elems : V;
-
-  // ---- pass 2: one contiguous run per lane inside segment k
-  long long run = (ke - kb + kBlock - 1) / kBlock;
-  if (ALIGNED) run = (run + EPV - 1) / EPV * EPV;
-  long long rb = kb + (long long)tid * run;
-  if (rb > ke) rb = ke;
-  long long re = rb + run < ke ? rb + run : ke;
-  double T = 0.0;
-  for (long long e = rb; e < re; ++e) {
-    const float zt = load_elem<DT>(R.t, e);
-    const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
-    T += (double)weight<DT>(R, zt, zd, tc);
+  // this lane's run [rb, re) inside segment k, weights kept in registers
+  const long long rb0 = kb + (long long)tid * kRun;
+  const long long rb = rb0 < ke ? rb0 : ke;
+  const long long re = rb + kRun < ke ? rb + kRun : ke;
+  float w[kRun];
+  if constexpr (ALIGNED) {
+    // one descriptor for the whole segment (uniform), per-lane offsets
+    constexpr int KV = kRun / EPV;
+    const int nvec = (int)((re - rb) / EPV);
+    const int segvec = (int)((ke - kb) / EPV);
+    const int lane_vec0 = (int)((rb - kb) / EPV);
+    if (nvec > 0) {
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + kb * ES, (uint32_t)segvec * 16u);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + kb * ES, (uint32_t)segvec * 16u);
+      v4i vt[KV], vd[KV];
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        const uint32_t off = (uint32_t)(lane_vec0 + min(k, nvec - 1)) * 16u;
+        vt[k] = load16(rt, off);
+        if (R.resid) vd[k] = load16(rd, off);
+      }
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        float zt[EPV], zd[EPV];
+        unpack<DT>(vt[k], zt);
+        if (R.resid) unpack<DT>(vd[k], zd);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i)
+          w[k * EPV + i] = k < nvec ? weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, P.tc) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRun; ++e) w[e] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) {
+      const long long ee = rb + e;
+      float v = 0.f;
+      if (ee < re) {
+        const float zt = load_elem<DT>(R.t, ee);
+        const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
+        v = weight<DT>(R, zt, zd, P.tc);
+      }
+      w[e] = v;
+    }
   }
-  // exclusive block scan of the lane sums
+  double T = 0.0;
+#pragma unroll
+  for (int e = 0; e < kRun; ++e) T += (double)w[e];
   const double incl = wave_incl_scan(T, lane);
   if (lane == kWave - 1) sh_wtot[wid] = incl;
   __syncthreads();
   double wbase = 0.0;
-  for (int w = 0; w < wid; ++w) wbase += sh_wtot[w];
+  for (int v = 0; v < wid; ++v) wbase += sh_wtot[v];
   const double excl = sh_base + wbase + (incl - T);
-  const bool cross = !sh_fallback && T > 0.0 && excl + T > sh_thr;
-  const bool haspos = T > 0.0;
+  const double thr = sh_thr;
+  const bool cross = !sh_fallback && T > 0.0 && excl + T > thr;
   const unsigned long long mc = __ballot(cross);
-  const unsigned long long mp = __ballot(haspos);
+  const unsigned long long mp = __ballot(T > 0.0);
   if (lane == 0) sh_first[wid] = mc ? wid * kWave + (int)__ffsll((long long)mc) - 1 : INT_MAX;
   __syncthreads();
-  int first = min(min(sh_first[0], sh_first[1]), min(sh_first[2], sh_first[3]));
+  const int first = min(min(sh_first[0], sh_first[1]), min(sh_first[2], sh_first[3]));
   __syncthreads();
-  // last lane with positive mass (used when rounding leaves no crossing)
   if (lane == 0) sh_first[wid] = mp ? wid * kWave + 63 - (int)__clzll((long long)mp) : -1;
   __syncthreads();
   const int lastpos = max(max(sh_first[0], sh_first[1]), max(sh_first[2], sh_first[3]));
   const int who = first != INT_MAX ? first : lastpos;
   if (tid == who) {
     double acc = excl;
-    long long y = -1, ylast = -1;
-    for (long long e = rb; e < re; ++e) {
-      const float zt = load_elem<DT>(R.t, e);
-      const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
-      const float w = weight<DT>(R, zt, zd, tc);
-      if (w > 0.f) {
-        acc += (double)w;
+    int y = -1, ylast = -1;
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) {
+      if (w[e] > 0.f) {
+        acc += (double)w[e];
         ylast = e;
-        if (first != INT_MAX && acc > sh_thr) { y = e; break; }
+        if (y < 0 && first != INT_MAX && acc > thr) y = e;
       }
     }
-    sh_y = y >= 0 ? y : ylast;
+    sh_y = rb + (y >= 0 ? y : ylast);
   }
   __syncthreads();
-  const int yv = (int)sh_y;
-  const int* x = P.tokens + rd0;
-  for (int i = tid; i <= g; i += kBlock) out[i] = i < j ? x[i] : (i == j ? yv : -1);
-  if (tid == 0) {
-    P.accept_len[b] = j;
-    P.cnt[b] = 0u;
-  }
+  if (tid == 0) P.out_tokens[ubase + di.j] = (int)sh_y;
+}
+
+template <int DT, bool ALIGNED>
+hipError_t launch_sample_t(const SampleParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_accept<DT>), dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_draw_mass<DT, ALIGNED>), dim3((unsigned)((long long)p.B * p.nseg)), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_draw_pick<DT, ALIGNED>), dim3((unsigned)p.B), dim3(kBlock), (size_t)p.nseg * 8, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 int sample_draw_segments(int V, int* seg_elems) {
-  // 256 lanes x 4 vectors x 8 elements per segment (a multiple of every
-  // vector width), at least one segment.
-  const long long per = (long long)kBlock * kDrawVPT * 8;
-  long long n = ((long long)V + per - 1) / per;
+  long long n = ((long long)V + kSegElems - 1) / kSegElems;
   if (n < 1) n = 1;
-  *seg_elems = (int)per;
+  *seg_elems = kSegElems;
   return (int)n;
 }
 
 hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s) {
-  const long long grid = (long long)p.B * p.nseg;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if ((long long)p.B * p.nseg > 0x7fffffffLL) return hipErrorInvalidValue;
+  if ((size_t)p.nseg * 8 > 48 * 1024) return hipErrorInvalidValue;
   const bool aligned = dt == DT_BF16 ? (p.V % 8 == 0) : (p.V % 4 == 0);
-  if (dt == DT_BF16) {
-    if (aligned) hipLaunchKernelGGL((k_sample<DT_BF16, true>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-    else hipLaunchKernelGGL((k_sample<DT_BF16, false>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-  } else {
-    if (aligned) hipLaunchKernelGGL((k_sample<DT_F32, true>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-    else hipLaunchKernelGGL((k_sample<DT_F32, false>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-  }
-  return hipGetLastError();
+  if (dt == DT_BF16) return aligned ? launch_sample_t<DT_BF16, true>(p, s) : launch_sample_t<DT_BF16, false>(p, s);
+  return aligned ? launch_sample_t<DT_F32, true>(p, s) : launch_sample_t<DT_F32, false>(p, s);
 }
 
 }  // namespace sv

@@ -21,8 +21,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// Cache-policy bits of a buffer load: 2 marks the access non-temporal.
+// Logits are read once per call, and on MI355X non-temporal 16-byte loads
+// stream from HBM about 10% faster than default-policy ones.
+constexpr int kStreamAux = 2;
+
 __device__ __forceinline__ v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamAux);
 }
 
 // bf16 bit patterns packed two per dword: element 0 in the low half.
@@ -148,13 +153,14 @@ __device__ __forceinline__ float exp_rel(float z, float M, const TempConst& tc) 
   }
 }
 
-// ---------------------------------------------- agent-scope completion count
-__device__ __forceinline__ unsigned count_arrival(unsigned* cnt) {
-  return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void acquire_agent() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
+// Sequence-level result of the accept scan, handed to the draw kernels.
+struct DrawInfo {
+  int j;        // accepted drafts (0..gamma), or -1 for an invalid draft token
+  float Mt;     // max of target row j
+  float Md;     // max of draft row j (j < gamma)
+  float pad_;
+  double rho;   // S_t / S_d of row j (j < gamma)
+};
 
 // Per-row statistics handed between kernels.
 struct Partial {

@@ -11,7 +11,7 @@ namespace sv {
 // ------------------------------------------------------------ row sweep
 // One pass over every row of up to two logit tensors (rows0 rows of the
 // first, rows1 of the second, both [*, V]).  Each wave reduces one segment of
-// one row; the last wave to finish a row merges the row's segments.
+// one row into a partial; a second kernel merges each row's partials.
 struct RowStatsParams {
   const void* src0;
   const void* src1;
@@ -23,7 +23,6 @@ struct RowStatsParams {
   int want;       // bit 0: max/sum, bit 1: argmax
   TempConst tc;
   Partial* part;  // [rows][nseg]
-  unsigned* cnt;  // [rows], zero on entry, zero on exit
   float* out_max; // [rows]
   double* out_sum;// [rows] (want & 1)
   int* out_arg;   // [rows] (want & 2)
@@ -35,23 +34,29 @@ struct RowSweepShape {
 };
 RowSweepShape row_sweep_shape(int V, int dt);
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);
+// The sweep alone (partials only); the sampling path merges its rows itself.
+hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s);
 
 // ---------------------------------------------------------- sampling
-// Accept scan, residual / bonus segment sums and (in the last workgroup of
-// each sequence) the inverse-CDF draw.
+// Three kernels after the row sweep: the accept scan (one workgroup per
+// sequence, which also merges that sequence's row partials), the residual /
+// bonus segment masses (B x nseg workgroups) and the inverse-CDF draw (one
+// workgroup per sequence).
 struct SampleParams {
   const void* tgt;        // [B, g+1, V]
   const void* drf;        // [B, g, V]
   const int* tokens;      // [B, g]
   const float* unif;      // [B, g+1]
-  const float* row_max;   // [B(g+1) target rows, then B g draft rows]
-  const double* row_sum;
+  const Partial* part;    // [rows][nseg_rows] row-sweep partials
+  int nseg_rows;
+  float* row_max;         // [B(g+1) target rows, then B g draft rows]
+  double* row_sum;
   int B, g, V;
   int nseg;               // draw segments per row
   int seg_elems;          // elements per draw segment (multiple of 8)
   TempConst tc;
+  DrawInfo* info;         // [B]
   double* segsum;         // [B][nseg]
-  unsigned* cnt;          // [B]
   int* accept_len;        // [B]
   int* out_tokens;        // [B, g+1]
 };

@@ -320,7 +320,9 @@ def test_gpu_constant_alpha_mean_length():
 
 
 # ------------------------------------------------------------- robustness
-def test_deterministic_and_workspace_reusable(c3):
+def test_deterministic_and_workspace_shared_across_layouts(c3):
+    """Bitwise-identical repeats, and one workspace (poisoned between calls)
+    serving calls of different modes and sizes."""
     t, d = to_dev(c3["target"]), to_dev(c3["draft"])
     x, u = to_dev(c3["draft_tokens"]), to_dev(c3["uniforms"])
     ws = L.new_workspace(L.MODE_SAMPLE, 64, 7, 128256)
@@ -328,10 +330,17 @@ def test_deterministic_and_workspace_reusable(c3):
     for _ in range(3):
         acc, out = L.verify_sample(t, d, x, u, 0.7, ws=ws)
         outs.append((acc.cpu().numpy().copy(), out.cpu().numpy().copy()))
+        ws.fill_(0xA5)
+        small = make_workload("tiny", B=5, gamma=3, V=333, dtype="bf16", seed=len(outs))
+        sacc, sout = L.verify_sample(to_dev(small["target"]), to_dev(small["draft"]),
+                                     to_dev(small["draft_tokens"]), to_dev(small["uniforms"]), 1.0, ws=ws)
+        oacc, oout, infos = oracle.verify_sample(small["target"], small["draft"], "bf16", small["draft_tokens"],
+                                                 small["uniforms"], 1.0)
+        assert not classify_sample(sacc.cpu().numpy(), sout.cpu().numpy(), oacc, oout, infos)["unexplained"]
+        gacc, gout = L.verify_greedy(t, x, ws=ws)
+        ws.fill_(0x5A)
     for o in outs[1:]:
         assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
-    # the counters region is zero again after every call
-    assert int(ws[:1024].sum().item()) == 0
 
 
 # ---------------------------------------------------------------- LM head
