@@ -23,7 +23,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // is fully written before it is read within one call, so a workspace needs
 // no initialisation and can be shared by calls of any layout (one at a time).
 struct Layout {
-  size_t info, part, rmax, rsum, rarg, segsum, logits, total;
+  size_t info, part, rmax, rsum, rarg, gath, segsum, logits, total;
   long long rows;
   int nseg, nseg2;
 };
@@ -68,6 +68,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   L->rmax = o;   o = up(o + (size_t)rows * 4);
   L->rsum = o;   o = up(o + (size_t)rows * 8);
   L->rarg = o;   o = up(o + (size_t)rows * 4);
+  L->gath = o;   o = up(o + (size_t)rows * 4);
   L->segsum = o; o = up(o + (size_t)seqs * nseg2 * 8);
   L->logits = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)V * 4);
@@ -112,8 +113,11 @@ spec_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
   return SPEC_OK;
 }
 
+// Sweep only (partials in the workspace), or sweep + merge into L's
+// per-row arrays when `merge` is set.
 hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long long rows1, int V,
-                     int dt, int want, const TempConst& tc, void* ws, const Layout& L, hipStream_t s) {
+                     int dt, int want, const TempConst& tc, void* ws, const Layout& L, hipStream_t s,
+                     bool merge = false) {
   RowStatsParams p;
   memset(&p, 0, sizeof(p));
   const RowSweepShape sh = row_sweep_shape(V, dt);
@@ -130,7 +134,7 @@ hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long l
   p.out_max = at<float>(ws, L.rmax);
   p.out_sum = at<double>(ws, L.rsum);
   p.out_arg = at<int>(ws, L.rarg);
-  return launch_row_stats(p, dt, s);
+  return merge ? launch_row_stats(p, dt, s) : launch_row_sweep(p, dt, s);
 }
 
 spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* tokens,
@@ -150,6 +154,9 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
   r.want = 1;
   r.tc = tc;
   r.part = at<Partial>(ws, L.part);
+  r.gather_tokens = tokens;
+  r.gather_g = g;
+  r.gather_out = at<float>(ws, L.gath);
   if (launch_row_sweep(r, dt, s) != hipSuccess) return SPEC_EHIP;
   SampleParams p;
   memset(&p, 0, sizeof(p));
@@ -159,8 +166,7 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
   p.unif = unif;
   p.part = r.part;
   p.nseg_rows = sh.nseg;
-  p.row_max = at<float>(ws, L.rmax);
-  p.row_sum = at<double>(ws, L.rsum);
+  p.gathered = r.gather_out;
   p.B = B;
   p.g = g;
   p.V = V;
@@ -275,7 +281,8 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dt, const i
   hipError_t e = row_sweep(target_logits, (long long)B * (gamma + 1), nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
   if (e != hipSuccess) return SPEC_EHIP;
   GreedyParams p;
-  p.arg = at<int>(ws, L.rarg);
+  p.part = at<Partial>(ws, L.part);
+  p.nseg = row_sweep_shape(V, (int)dt).nseg;
   p.tokens = draft_tokens;
   p.B = B;
   p.g = gamma;
@@ -306,7 +313,8 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
   hipError_t e = row_sweep(target_logits, (long long)B * N, nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
   if (e != hipSuccess) return SPEC_EHIP;
   TreeParams p;
-  p.arg = at<int>(ws, L.rarg);
+  p.part = at<Partial>(ws, L.part);
+  p.nseg = row_sweep_shape(V, (int)dt).nseg;
   p.node_tokens = node_tokens;
   p.parent = parent;
   p.parent_stride = parent_batch_stride;
@@ -386,7 +394,7 @@ spec_status spec_probe_probs(const void* target_logits, const void* draft_logits
   const spec_status w = check_ws(ws, ws_bytes, L);
   if (w != SPEC_OK) return w;
   hipError_t e = row_sweep(target_logits, rows, draft_logits, draft_logits ? rows : 0, V, (int)dt, 1, tc, ws,
-                           L, s);
+                           L, s, true);
   if (e != hipSuccess) return SPEC_EHIP;
   ProbeParams p;
   p.tgt = target_logits;

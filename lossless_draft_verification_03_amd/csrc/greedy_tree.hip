@@ -18,34 +18,47 @@ namespace {
 
 constexpr int SPEC_TREE_LDS_NODES = 4096;   // = SPEC_MAX_TREE_NODES
 
-// One wavefront per sequence: lane i compares draft i with argmax of row i;
-// a ballot gives the first mismatch.
+// One workgroup per sequence: lane groups of NP lanes merge the argmax
+// partials of the g + 1 target rows, then lane i of wave 0 compares draft i
+// with the argmax of row i and a ballot gives the first mismatch.
+template <int NP>
 __global__ __launch_bounds__(kBlock) void k_greedy_finish(GreedyParams P) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const long long b = (long long)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
-  if (b >= P.B) return;
+  __shared__ int sh_arg[64];
+  const int tid = threadIdx.x;
+  const long long b = blockIdx.x;
   const int g = P.g;
-  const int* arg = P.arg + b * (g + 1);
   const int* x = P.tokens + b * g;
-  const int xi = lane < g ? x[lane] : 0;
-  const int ai = lane <= g ? arg[lane] : 0;
-  const unsigned long long mm = __ballot(lane < g && xi != ai);
+  const int xi = tid < g ? x[tid] : 0;
+  for (int row = tid / NP; row <= g; row += kBlock / NP) {
+    float M;
+    double S;
+    int a;
+    merge_partials<2, NP>(P.part + (b * (g + 1) + row) * P.nseg, P.nseg, TempConst{}, tid & (NP - 1), &M, &S, &a);
+    if ((tid & (NP - 1)) == 0) sh_arg[row] = a;
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  const int ai = tid <= g ? sh_arg[tid] : 0;
+  const unsigned long long mm = __ballot(tid < g && xi != ai);
   const int j = mm ? (int)__ffsll((long long)mm) - 1 : g;
-  const int aj = __shfl(ai, j, kWave);
+  const int aj = sh_arg[j];
   int* out = P.out_tokens + b * (g + 1);
-  if (lane <= g) out[lane] = lane < j ? xi : (lane == j ? aj : -1);
-  if (lane == 0) P.accept_len[b] = j;
+  if (tid <= g) out[tid] = tid < j ? xi : (tid == j ? aj : -1);
+  if (tid == 0) P.accept_len[b] = j;
 }
 
-// One workgroup per sequence.  ok(n) = ok(parent(n)) and tok(n) ==
-// argmax(parent(n)), depth(n) = depth(parent(n)) + 1, both resolved by
-// pointer jumping over the ancestor links in LDS (log2 N rounds).  The
-// accepted node maximises (depth, -index) over ok nodes.
+// One workgroup per sequence.  Lane groups first merge the argmax partials
+// of the N node rows.  ok(n) = ok(parent(n)) and tok(n) == argmax(parent(n)),
+// depth(n) = depth(parent(n)) + 1, both resolved by pointer jumping over the
+// ancestor links in LDS (log2 N rounds).  The accepted node maximises
+// (depth, -index) over ok nodes.
+template <int NP>
 __global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
   __shared__ short s_anc[2][SPEC_TREE_LDS_NODES];
   __shared__ unsigned char s_ok[2][SPEC_TREE_LDS_NODES];
   __shared__ short s_dep[2][SPEC_TREE_LDS_NODES];
   __shared__ short s_par[SPEC_TREE_LDS_NODES];
+  __shared__ int s_arg[SPEC_TREE_LDS_NODES];
   __shared__ int s_bad;
   __shared__ int s_key[kBlock / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -53,8 +66,14 @@ __global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
   const int N = P.N;
   const int* par = P.parent + b * P.parent_stride;
   const int* tok = P.node_tokens + b * N;
-  const int* arg = P.arg + b * N;
   if (tid == 0) s_bad = 0;
+  for (int row = tid / NP; row < N; row += kBlock / NP) {
+    float M;
+    double S;
+    int a;
+    merge_partials<2, NP>(P.part + (b * N + row) * P.nseg, P.nseg, TempConst{}, tid & (NP - 1), &M, &S, &a);
+    if ((tid & (NP - 1)) == 0) s_arg[row] = a;
+  }
   __syncthreads();
   for (int n = tid; n < N; n += kBlock) {
     const int p = par[n];
@@ -76,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
   for (int n = tid; n < N; n += kBlock) {
     const int p = s_par[n];
     s_anc[0][n] = (short)p;
-    s_ok[0][n] = n == 0 ? 1 : (unsigned char)(tok[n] == arg[p]);
+    s_ok[0][n] = n == 0 ? 1 : (unsigned char)(tok[n] == s_arg[p]);
     s_dep[0][n] = (short)(n == 0 ? 0 : 1);
   }
   __syncthreads();
@@ -114,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
       out_tok[d] = tok[m];
       m = s_par[m];
     }
-    out_tok[depth] = arg[nstar];
+    out_tok[depth] = s_arg[nstar];
     P.accept_len[b] = depth;
   }
 }
@@ -172,13 +191,30 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 }  // namespace
 
 hipError_t launch_greedy_finish(const GreedyParams& p, hipStream_t s) {
-  const long long grid = ((long long)p.B + 3) / 4;
-  hipLaunchKernelGGL(k_greedy_finish, dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  const dim3 grid((unsigned)p.B), block(kBlock);
+  switch (merge_group(p.nseg)) {
+    case 1: hipLaunchKernelGGL(k_greedy_finish<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(k_greedy_finish<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(k_greedy_finish<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(k_greedy_finish<8>, grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL(k_greedy_finish<16>, grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL(k_greedy_finish<32>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(k_greedy_finish<64>, grid, block, 0, s, p); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_tree_finish(const TreeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_tree_finish, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  const dim3 grid((unsigned)p.B), block(kBlock);
+  switch (merge_group(p.nseg)) {
+    case 1: hipLaunchKernelGGL(k_tree_finish<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(k_tree_finish<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(k_tree_finish<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(k_tree_finish<8>, grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL(k_tree_finish<16>, grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL(k_tree_finish<32>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(k_tree_finish<64>, grid, block, 0, s, p); break;
+  }
   return hipGetLastError();
 }
 

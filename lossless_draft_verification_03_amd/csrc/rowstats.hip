@@ -6,22 +6,28 @@
 // Small Model's Answer Reduce Quality?" (greedy takes the target's argmax).
 //
 // Work split: a row is cut into `nseg` segments of whole 16-byte vectors and
-// each wavefront reduces one segment; a workgroup is four independent waves.
-// A lane loads VPT vectors (coalesced: vector q of the segment goes to lane
-// q % 64) before it computes anything, so every lane keeps VPT 16-byte loads
-// in flight.  Elements of a row that do not fill a whole aligned vector (row
-// head / tail when V is not a multiple of the vector width) are loaded one by
-// one by the wave of segment 0.
+// one workgroup (four waves) reduces one segment into a partial (m, sum,
+// argmax).  Lane t of the workgroup loads vectors t, t+256, ... of its
+// segment, all kVPT of them before it computes anything (offsets clamped
+// into the segment, the excess masked afterwards), with the non-temporal
+// cache policy.  Elements of a row outside whole aligned vectors (row head /
+// tail when V is not a multiple of the vector width) are loaded one by one
+// by segment 0.  With kVPT = 8 a bf16 row of 128256 logits is eight
+// segments, so consumers merge a row's few partials inline.
 //
-// Numerics of the sum: per wave, with m the wave max, K = fl(m c_hi) and
+// Optionally the sweep also picks out z[r][x_r] for a per-row token x_r (the
+// drafted token of that position) while the row is in registers, so the
+// accept test needs no dependent gather.
+//
+// Numerics of the sum: with m the segment max, K = fl(m c_hi) and
 // a = fl(z c_lo + fl(z c_hi - K)) the exponent of every element carries both
-// halves of c = log2(e)/T, so no temperature bias enters; the constant
-// offset kappa = m c - K is removed in fp64 at the end.  Four fp32
-// accumulators per lane, fp64 from the lane level up.  Every wave writes one
-// partial (m, sum, argmax) and exits: there is no handoff between waves
-// inside the kernel (an agent-scope release/acquire per wave costs an L2
-// write-back and invalidate on this part).  A second, small kernel merges a
-// row's partials in segment order in fp64 after the kernel boundary.
+// halves of c = log2(e)/T, so no temperature bias enters.  The partial keeps
+// s = sum 2^a together with K; a consumer rescales it to the row max M with
+// one fp64 factor 2^(K - M c).  Four fp32 accumulators per lane, fp64 from
+// the lane level up, wave reductions by DPP in a fixed order.  There is no
+// handoff between workgroups inside the kernel: an agent-scope
+// release/acquire per workgroup costs an L2 write-back and invalidate on
+// this part, so partials are merged after the kernel boundary.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -30,20 +36,22 @@ namespace sv {
 
 namespace {
 
-constexpr int kVPT = 8;   // 16-byte vectors per lane per segment
+#ifndef SV_SWEEP_VPT
+#define SV_SWEEP_VPT 8
+#endif
+constexpr int kVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segment
 
 template <int DT, int WANT>
-__global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
+__global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
+  __shared__ float sh_m[kBlock / kWave];
+  __shared__ double sh_s[kBlock / kWave];
+  __shared__ int sh_a[kBlock / kWave];
   const float NEG_INF = -__builtin_huge_valf();
-  const int lane = threadIdx.x & (kWave - 1);
-  // the wave index is uniform across the wave; say so, so that everything
-  // derived from it (row, segment, buffer descriptor) lives in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const long long unit = (long long)blockIdx.x * (kBlock / kWave) + wave;
-  const long long rows = P.rows0 + P.rows1;
-  if (unit >= rows * P.nseg) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const long long unit = blockIdx.x;
   const long long r = unit / P.nseg;
   const int s = (int)(unit - r * P.nseg);
   const bool second = r >= P.rows0;
@@ -59,151 +67,181 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(RowStatsParams P) {
   const int nv = ve > vs ? (int)(ve - vs) : 0;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base + vs * 16, (uint32_t)nv * 16u);
 
-  // Issue every load before using any: the offset is clamped into the
-  // segment (never past it), and vectors beyond the segment are masked to
-  // -inf afterwards, so a lane always has kVPT loads in flight.
+  // the drafted token of this row, if the caller asked for the gather
+  long long gx = -1;
+  if (P.gather_tokens != nullptr) {
+    const long long g1 = second ? P.gather_g : P.gather_g + 1;
+    const long long b = rr / g1, i = rr - b * g1;
+    if (i < P.gather_g) {
+      const int x = P.gather_tokens[b * P.gather_g + i];
+      if (x >= 0 && (long long)x < V) gx = x;
+    }
+  }
+
   v4i raw[kVPT];
   if (nv > 0) {
 #pragma unroll
     for (int k = 0; k < kVPT; ++k) {
-      const int q = min(k * kWave + lane, nv - 1);
+      const int q = min(k * kBlock + tid, nv - 1);
       raw[k] = load16(rsrc, (uint32_t)q * 16u);
     }
   }
   const int neg_pat = DT == DT_BF16 ? (int)0xff80ff80u : (int)0xff800000u;
-  float z[kVPT][EPV];
 #pragma unroll
   for (int k = 0; k < kVPT; ++k) {
-    if ((k + 1) * kWave > nv) {             // wave-uniform: only the tail vectors
-      const bool valid = k * kWave + lane < nv;
+    if ((k + 1) * kBlock > nv) {            // uniform: only the tail vectors
+      const bool valid = k * kBlock + tid < nv;
 #pragma unroll
       for (int q = 0; q < 4; ++q) raw[k][q] = valid ? raw[k][q] : neg_pat;
     }
-    unpack<DT>(raw[k], z[k]);
   }
-  // Row head / tail elements outside whole vectors (segment 0 only).
+  // Row head / tail elements outside whole vectors (segment 0, wave 0).
   float ze = NEG_INF;
   int ie = INT_MAX;
-  if (s == 0) {
+  if (s == 0 && tid < 2 * EPV) {
     const long long he = e1 < vfirst * EPV ? e1 : vfirst * EPV;
     const long long tb = (vlast > vfirst ? vlast : vfirst) * EPV;
     long long e = -1;
-    if (lane < EPV) {
-      if (e0 + lane < he) e = e0 + lane;
-    } else if (lane < 2 * EPV) {
-      if (tb + (lane - EPV) < e1) e = tb + (lane - EPV);
+    if (tid < EPV) {
+      if (e0 + tid < he) e = e0 + tid;
+    } else {
+      if (tb + (tid - EPV) < e1) e = tb + (tid - EPV);
     }
     if (e >= 0) {
       ze = load_elem<DT>(base, e);
       ie = (int)(e - e0);
     }
   }
+  // row-local index of element i of this lane's vector k: lane_base + k*kBlock*EPV + i
+  const int lane_base = (int)((vs + tid) * EPV - e0);
 
+  // pick out z[x] if x lies in this segment's whole vectors or edge elements
+  if (gx >= 0) {
+    const long long gv = (e0 + gx) / EPV;    // vector holding element x
+    if (gv >= vs && gv < ve) {
+      const int q = (int)(gv - vs);
+      if ((q & (kBlock - 1)) == tid) {
+        const int kk = q / kBlock;
+        const int ii = (int)((e0 + gx) - gv * EPV);
+        float zz = 0.f;
+#pragma unroll
+        for (int k = 0; k < kVPT; ++k) {
+          if (k == kk) {
+            float z[EPV];
+            unpack<DT>(raw[k], z);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i)
+              if (i == ii) zz = z[i];
+          }
+        }
+        P.gather_out[r] = zz;
+      }
+    }
+    if (ie == (int)gx) P.gather_out[r] = ze;
+  }
+
+  // workgroup max: every wave's max through LDS (one barrier)
   float m = ze;
 #pragma unroll
-  for (int k = 0; k < kVPT; ++k)
+  for (int k = 0; k < kVPT; ++k) {
+    float z[EPV];
+    unpack<DT>(raw[k], z);
 #pragma unroll
-    for (int i = 0; i < EPV; ++i) m = fmaxf(m, z[k][i]);
-  const float M = wave_max(m);
+    for (int i = 0; i < EPV; ++i) m = fmaxf(m, z[i]);
+  }
+  const float Mw = wave_max(m);
+  if (lane == 0) sh_m[wid] = Mw;
+  __syncthreads();
+  float M = sh_m[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / kWave; ++w) M = fmaxf(M, sh_m[w]);
 
   int idx = INT_MAX;
   if constexpr ((WANT & 2) != 0) {
-    if (M != NEG_INF) {
-      const int lane_base = (int)((vs + lane) * EPV - e0);
+    if (M != NEG_INF && Mw == M) {          // uniform per wave
 #pragma unroll
-      for (int k = kVPT - 1; k >= 0; --k)
+      for (int k = kVPT - 1; k >= 0; --k) {
+        float z[EPV];
+        unpack<DT>(raw[k], z);
 #pragma unroll
         for (int i = EPV - 1; i >= 0; --i)
-          if (z[k][i] == M) idx = lane_base + k * kWave * EPV + i;
+          if (z[i] == M) idx = lane_base + k * kBlock * EPV + i;
+      }
       if (ze == M) idx = min(idx, ie);
+      idx = wave_min(idx);
     }
-    idx = wave_min(idx);
   }
 
   double S = 0.0;
+  float K = 0.f;
   if constexpr ((WANT & 1) != 0) {
     if (M != NEG_INF) {
       const float c_hi = P.tc.c_hi, c_lo = P.tc.c_lo;
-      const float K = M * c_hi;
+      K = M * c_hi;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < kVPT; ++k)
+      for (int k = 0; k < kVPT; ++k) {
+        float z[EPV];
+        unpack<DT>(raw[k], z);
 #pragma unroll
         for (int i = 0; i < EPV; ++i) {
-          const float a = fmaf(z[k][i], c_lo, fmaf(z[k][i], c_hi, -K));
+          const float a = fmaf(z[i], c_lo, fmaf(z[i], c_hi, -K));
           acc[i & 3] += __builtin_amdgcn_exp2f(a);
         }
+      }
       acc[0] += __builtin_amdgcn_exp2f(fmaf(ze, c_lo, fmaf(ze, c_hi, -K)));
-      double t = ((double)acc[0] + (double)acc[1]) + ((double)acc[2] + (double)acc[3]);
-      t = wave_sum(t);
-      const double kappa = (double)M * P.tc.c64 - (double)K;
-      S = t * exp2_f64(-kappa);
+      S = wave_sum(((double)acc[0] + (double)acc[1]) + ((double)acc[2] + (double)acc[3]));
     }
   }
-
   if (lane == 0) {
+    sh_s[wid] = S;
+    sh_a[wid] = idx;
+  }
+  __syncthreads();
+  if (tid == 0) {
     Partial pp;
     pp.m = M;
-    pp.arg = idx;
-    pp.s = S;
+    pp.arg = min(min(sh_a[0], sh_a[1]), min(sh_a[2], sh_a[3]));
+    pp.K = K;
+    pp.pad_ = 0.f;
+    pp.s = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
     P.part[r * P.nseg + s] = pp;
   }
 }
 
-// One wave per row: merge the row's segment partials in segment order.
+// One wave per row: merge the row's segment partials.
 template <int WANT>
 __global__ __launch_bounds__(kBlock) void k_row_merge(RowStatsParams P) {
-  const float NEG_INF = -__builtin_huge_valf();
   const int lane = threadIdx.x & (kWave - 1);
-  const long long r = (long long)blockIdx.x * (kBlock / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const long long r =
+      (long long)blockIdx.x * (kBlock / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (r >= P.rows0 + P.rows1) return;
-  const Partial* part = P.part + r * P.nseg;
-  float Mr = NEG_INF;
-  for (int t = lane; t < P.nseg; t += kWave) Mr = fmaxf(Mr, part[t].m);
-  Mr = wave_max(Mr);
-  double Sr = 0.0;
-  int ar = INT_MAX;
-  for (int t = lane; t < P.nseg; t += kWave) {
-    const Partial pp = part[t];
-    if constexpr ((WANT & 1) != 0)
-      if (pp.m != NEG_INF) Sr += pp.s * exp2_f64(((double)pp.m - (double)Mr) * P.tc.c64);
-    if constexpr ((WANT & 2) != 0)
-      if (pp.m == Mr) ar = min(ar, pp.arg);
-  }
-  if constexpr ((WANT & 1) != 0) Sr = wave_sum(Sr);
-  if constexpr ((WANT & 2) != 0) ar = wave_min(ar);
+  float M;
+  double S;
+  int a;
+  merge_partials<WANT, kWave>(P.part + r * P.nseg, P.nseg, P.tc, lane, &M, &S, &a);
   if (lane == 0) {
-    P.out_max[r] = Mr;
-    if constexpr ((WANT & 1) != 0) P.out_sum[r] = Sr;
-    if constexpr ((WANT & 2) != 0) P.out_arg[r] = ar == INT_MAX ? 0 : ar;
+    P.out_max[r] = M;
+    if constexpr ((WANT & 1) != 0) P.out_sum[r] = S;
+    if constexpr ((WANT & 2) != 0) P.out_arg[r] = a;
   }
 }
 
-template <int DT>
-hipError_t launch_dt(const RowStatsParams& p, hipStream_t s) {
-  const long long rows = p.rows0 + p.rows1;
-  const long long units = rows * (long long)p.nseg;
-  const long long wpb = kBlock / kWave;
-  const long long grid = (units + wpb - 1) / wpb;
-  const long long mgrid = (rows + wpb - 1) / wpb;
+template <int DT, int WANT>
+hipError_t launch_sweep_t(const RowStatsParams& p, hipStream_t s) {
+  const long long grid = (p.rows0 + p.rows1) * (long long)p.nseg;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  switch (p.want) {
-    case 1:
-      hipLaunchKernelGGL((k_row_stats<DT, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-      hipLaunchKernelGGL((k_row_merge<1>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((k_row_stats<DT, 2>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-      hipLaunchKernelGGL((k_row_merge<2>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
-      break;
-    case 3:
-      hipLaunchKernelGGL((k_row_stats<DT, 3>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-      hipLaunchKernelGGL((k_row_merge<3>), dim3((unsigned)mgrid), dim3(kBlock), 0, s, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((k_row_sweep<DT, WANT>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int WANT>
+hipError_t launch_merge_t(const RowStatsParams& p, hipStream_t s) {
+  const long long wpb = kBlock / kWave;
+  const long long grid = (p.rows0 + p.rows1 + wpb - 1) / wpb;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_row_merge<WANT>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
@@ -212,7 +250,7 @@ hipError_t launch_dt(const RowStatsParams& p, hipStream_t s) {
 RowSweepShape row_sweep_shape(int V, int dt) {
   const long long epv = dt == DT_BF16 ? 8 : 4;
   const long long whole = (long long)V / epv;           // whole vectors per row, at most
-  const long long cap = (long long)kVPT * kWave;        // vectors one wave reduces
+  const long long cap = (long long)kVPT * kBlock;       // vectors one workgroup reduces
   long long nseg = (whole + cap - 1) / cap;
   if (nseg < 1) nseg = 1;
   long long seg = (whole + nseg - 1) / nseg;
@@ -220,19 +258,36 @@ RowSweepShape row_sweep_shape(int V, int dt) {
   return RowSweepShape{(int)nseg, (int)seg};
 }
 
-hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s) {
-  return dt == DT_BF16 ? launch_dt<DT_BF16>(p, s) : launch_dt<DT_F32>(p, s);
+hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s) {
+  if (dt == DT_BF16) {
+    switch (p.want) {
+      case 1: return launch_sweep_t<DT_BF16, 1>(p, s);
+      case 2: return launch_sweep_t<DT_BF16, 2>(p, s);
+      case 3: return launch_sweep_t<DT_BF16, 3>(p, s);
+    }
+  } else {
+    switch (p.want) {
+      case 1: return launch_sweep_t<DT_F32, 1>(p, s);
+      case 2: return launch_sweep_t<DT_F32, 2>(p, s);
+      case 3: return launch_sweep_t<DT_F32, 3>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s) {
-  const long long units = (p.rows0 + p.rows1) * (long long)p.nseg;
-  const long long wpb = kBlock / kWave;
-  const long long grid = (units + wpb - 1) / wpb;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL || p.want != 1) return hipErrorInvalidValue;
-  if (dt == DT_BF16) hipLaunchKernelGGL((k_row_stats<DT_BF16, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-  else hipLaunchKernelGGL((k_row_stats<DT_F32, 1>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_row_merge(const RowStatsParams& p, hipStream_t s) {
+  switch (p.want) {
+    case 1: return launch_merge_t<1>(p, s);
+    case 2: return launch_merge_t<2>(p, s);
+    case 3: return launch_merge_t<3>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s) {
+  const hipError_t e = launch_row_sweep(p, dt, s);
+  if (e != hipSuccess) return e;
+  return launch_row_merge(p, s);
 }
 
 }  // namespace sv

@@ -9,18 +9,18 @@
 // speculative decoding" ((p - q)_+ and the +1 bonus token); "Speculative
 // decoding" wiki, "The mechanism".
 //
-// Three kernels; the kernel boundaries are the only handoffs between
-// workgroups.
-//  k_accept     one workgroup per sequence.  Wave w takes positions w, w+4,
-//               ...: it merges the target (and draft) row partials of the
-//               position in fp64, gathers z_t(x_i) and z_d(x_i) and tests
-//               u_i < p_i(x_i)/q_i(x_i) with the ratio formed from one fp64
-//               exponent.  The first rejection j, the draw row's statistics
-//               and the accepted prefix of the output are written here.
-//  k_draw_mass  B x nseg workgroups: the draw weights of one segment of row j,
+// Two kernels after the row sweep; the kernel boundaries are the only
+// handoffs between workgroups.
+//  k_draw_mass  B x nseg workgroups.  Every workgroup of sequence b first
+//               merges the row partials of its 2 gamma + 1 rows in fp64
+//               (lane groups of NP lanes, one row per group) and runs the
+//               accept scan: lane i tests u_i < p_i(x_i)/q_i(x_i) with the
+//               ratio formed from one fp64 exponent (z(x_i) was picked out by
+//               the sweep); a ballot gives the first rejection j.  All of
+//               them reach the same j; workgroup (b, 0) records it.  Then the
+//               draw weights of one segment of row j are summed in fp64:
 //                 j <  gamma : w = max(0, p_j - q_j)  (as S_t w = max(0, e_t - rho e_d))
 //                 j == gamma : w = p_gamma            (as S_t w = e_t)
-//               summed in fp64.
 //  k_draw_pick  one workgroup per sequence: locate the segment holding
 //               u[b][gamma] * total, rescan it with one contiguous run per
 //               lane (weights kept in registers), block-scan the lane sums in
@@ -68,113 +68,6 @@ __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
   R.rho_hi = (float)di.rho;
   R.rho_lo = (float)(di.rho - (double)R.rho_hi);
   return R;
-}
-
-// Merge one row's segment partials across a wave: (max, sum relative to it).
-__device__ __forceinline__ void merge_row(const Partial* part, int nseg, const TempConst& tc, int lane,
-                                          float* M_out, double* S_out) {
-  const float NEG_INF = -__builtin_huge_valf();
-  float m = NEG_INF;
-  double sv = 0.0;
-  for (int t = lane; t < nseg; t += kWave) {
-    const Partial pp = part[t];
-    // a lane holds several partials only when nseg > 64: fold with a rescale
-    if (pp.m > m) {
-      if (m != NEG_INF) sv *= exp2_f64(((double)m - (double)pp.m) * tc.c64);
-      m = pp.m;
-      sv += pp.s;
-    } else if (pp.m != NEG_INF) {
-      sv += pp.s * exp2_f64(((double)pp.m - (double)m) * tc.c64);
-    }
-  }
-  const float M = wave_max(m);
-  if (m != NEG_INF) sv *= exp2_f64(((double)m - (double)M) * tc.c64);
-  *M_out = M;
-  *S_out = wave_sum(sv);
-}
-
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_accept(SampleParams P) {
-  __shared__ int sh_rej[64];
-  __shared__ int sh_bad;
-  __shared__ float sh_mt[64], sh_md[64];
-  __shared__ double sh_st[64], sh_sd[64];
-  __shared__ int sh_j;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int b = blockIdx.x;
-  const int g = P.g;
-  const long long V = P.V;
-  const long long rt0 = (long long)b * (g + 1);
-  const long long rd0 = (long long)b * g;
-  const long long rds0 = (long long)P.B * (g + 1) + rd0;
-  if (tid == 0) sh_bad = 0;
-  __syncthreads();
-  for (int i = wid; i <= g; i += kBlock / kWave) {
-    // the token and the two gathered logits do not depend on the merge
-    int x = 0;
-    float zt = 0.f, zd = 0.f;
-    bool bad = false;
-    if (i < g) {
-      x = P.tokens[rd0 + i];
-      bad = x < 0 || (long long)x >= V;
-      if (!bad) {
-        zt = load_elem<DT>(P.tgt, (rt0 + i) * V + x);
-        zd = load_elem<DT>(P.drf, (rd0 + i) * V + x);
-      }
-    }
-    float Mt, Md = 0.f;
-    double St, Sd = 1.0;
-    merge_row(P.part + (rt0 + i) * P.nseg_rows, P.nseg_rows, P.tc, lane, &Mt, &St);
-    if (i < g) merge_row(P.part + (rds0 + i) * P.nseg_rows, P.nseg_rows, P.tc, lane, &Md, &Sd);
-    if (lane == 0) {
-      P.row_max[rt0 + i] = Mt;
-      P.row_sum[rt0 + i] = St;
-      sh_mt[i] = Mt;
-      sh_st[i] = St;
-      int rej = 0;
-      if (i < g) {
-        P.row_max[rds0 + i] = Md;
-        P.row_sum[rds0 + i] = Sd;
-        sh_md[i] = Md;
-        sh_sd[i] = Sd;
-        if (bad) {
-          sh_bad = 1;
-        } else {
-          const double et = ((double)zt - (double)Mt) * P.tc.c64;
-          const double ed = ((double)zd - (double)Md) * P.tc.c64;
-          double r;
-          if (!(et > -__builtin_huge_val())) r = 0.0;                          // p(x) = 0
-          else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();    // q(x) = 0 < p(x)
-          else r = exp2_f64(et - ed) * (Sd / St);
-          rej = !((double)P.unif[rt0 + i] < r);
-        }
-      }
-      sh_rej[i] = rej;
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int j = g;
-    for (int i = 0; i < g; ++i)
-      if (sh_rej[i]) { j = i; break; }
-    if (sh_bad) j = -1;
-    sh_j = j;
-    DrawInfo di;
-    di.j = j;
-    di.Mt = j >= 0 ? sh_mt[j] : 0.f;
-    di.Md = (j >= 0 && j < g) ? sh_md[j] : 0.f;
-    di.pad_ = 0.f;
-    di.rho = (j >= 0 && j < g) ? sh_st[j] / sh_sd[j] : 0.0;
-    P.info[b] = di;
-    P.accept_len[b] = j;
-  }
-  __syncthreads();
-  const int j = sh_j;
-  int* out = P.out_tokens + rt0;
-  for (int i = tid; i <= g; i += kBlock) {
-    if (j < 0 || i > j) out[i] = -1;
-    else if (i < j) out[i] = P.tokens[rd0 + i];
-  }
 }
 
 // Sum of the draw weights over elements [e_beg, e_end) of the draw row,
@@ -230,19 +123,123 @@ __device__ double block_sum(double x, double* sh4, int tid) {
   return t;
 }
 
-template <int DT, bool ALIGNED>
+template <int DT, bool ALIGNED, int NP>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
   __shared__ double sh4[4];
-  const int tid = threadIdx.x;
+  __shared__ float sh_M[2 * 64];
+  __shared__ double sh_S[2 * 64];
+  __shared__ DrawInfo sh_di;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int b = blockIdx.x / P.nseg, s = blockIdx.x - b * P.nseg;
-  const DrawInfo di = P.info[b];
+  const int g = P.g;
+  const long long V = P.V;
+  const long long rt0 = (long long)b * (g + 1);
+  const long long rd0 = (long long)b * g;
+  const long long rds0 = (long long)P.B * (g + 1) + rd0;
+  // inputs of the accept test that do not depend on the merge
+  int x = 0;
+  float zt = 0.f, zd = 0.f, u = 0.f;
+  if (tid < g) {
+    x = P.tokens[rd0 + tid];
+    zt = P.gathered[rt0 + tid];
+    zd = P.gathered[rds0 + tid];
+    u = P.unif[rt0 + tid];
+  }
+  // merge: rows 0..g are target rows, g+1..2g draft rows
+  const int nr = 2 * g + 1;
+  for (int row = tid / NP; row < nr; row += kBlock / NP) {
+    const long long gr = row <= g ? rt0 + row : rds0 + (row - g - 1);
+    float M;
+    double S;
+    int a;
+    merge_partials<1, NP>(P.part + gr * P.nseg_rows, P.nseg_rows, P.tc, tid & (NP - 1), &M, &S, &a);
+    if ((tid & (NP - 1)) == 0) {
+      sh_M[row] = M;
+      sh_S[row] = S;
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    bool rej = false, bad = false;
+    if (tid < g) {
+      if (x < 0 || (long long)x >= V) {
+        bad = true;
+      } else {
+        const double Mt = sh_M[tid], Md = sh_M[g + 1 + tid];
+        const double et = ((double)zt - Mt) * P.tc.c64;
+        const double ed = ((double)zd - Md) * P.tc.c64;
+        double r;
+        if (!(et > -__builtin_huge_val())) r = 0.0;                          // p(x) = 0
+        else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();    // q(x) = 0 < p(x)
+        else r = exp2_f64(et - ed) * (sh_S[g + 1 + tid] / sh_S[tid]);
+        rej = !((double)u < r);
+      }
+    }
+    const unsigned long long mb = __ballot(bad);
+    const unsigned long long mr = __ballot(rej);
+    if (tid == 0) {
+      const int j = mb ? -1 : (mr ? (int)__ffsll((long long)mr) - 1 : g);
+      DrawInfo di;
+      di.j = j;
+      di.Mt = j >= 0 ? sh_M[j] : 0.f;
+      di.Md = (j >= 0 && j < g) ? sh_M[g + 1 + j] : 0.f;
+      di.pad_ = 0.f;
+      di.rho = (j >= 0 && j < g) ? sh_S[j] / sh_S[g + 1 + j] : 0.0;
+      sh_di = di;
+      if (s == 0) {
+        P.info[b] = di;
+        P.accept_len[b] = j;
+      }
+    }
+  }
+  __syncthreads();
+  const DrawInfo di = sh_di;
+  if (s == 0) {
+    int* out = P.out_tokens + rt0;
+    for (int i = tid; i <= g; i += kBlock) {
+      if (di.j < 0 || i > di.j) out[i] = -1;
+      else if (i < di.j) out[i] = P.tokens[rd0 + i];
+    }
+  }
   if (di.j < 0) return;                       // uniform
   const DrawRow R = draw_row<DT>(P, b, di);
-  const long long V = P.V;
   const long long sb = (long long)s * P.seg_elems;
   const long long se = sb + P.seg_elems < V ? sb + P.seg_elems : V;
   const double part = block_sum(segment_partial<DT, ALIGNED>(R, sb, se, P.tc, tid), sh4, tid);
   if (tid == 0) P.segsum[(long long)b * P.nseg + s] = part;
+}
+
+// Wave-parallel location of the segment holding thr: lanes scan the segment
+// masses in chunks of 64 (fp64 inclusive scans, fixed order).  Returns the
+// segment index and the mass before it; if rounding leaves no crossing, the
+// last segment with positive mass and fallback = 1.
+__device__ __forceinline__ int locate_segment(const double* seg, int nseg, double thr, int lane, double* base,
+                                             int* fallback) {
+  double carry = 0.0;
+  int last = 0;
+  double lastbase = 0.0;
+  for (int c0 = 0; c0 < nseg; c0 += kWave) {
+    const int t = c0 + lane;
+    const double m = t < nseg ? seg[t] : 0.0;
+    const double incl = carry + wave_incl_scan(m, lane);
+    const unsigned long long mc = __ballot(m > 0.0 && incl > thr);
+    const unsigned long long mp = __ballot(m > 0.0);
+    if (mc) {
+      const int l = (int)__ffsll((long long)mc) - 1;
+      *base = readlane_d(incl, l) - readlane_d(m, l);
+      *fallback = 0;
+      return c0 + l;
+    }
+    if (mp) {
+      const int l = 63 - (int)__clzll((long long)mp);
+      last = c0 + l;
+      lastbase = readlane_d(incl, l) - readlane_d(m, l);
+    }
+    carry = readlane_d(incl, kWave - 1);
+  }
+  *base = lastbase;
+  *fallback = 1;
+  return last;
 }
 
 template <int DT, bool ALIGNED>
@@ -260,18 +257,23 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   const int b = blockIdx.x;
   const int g = P.g;
   const long long V = P.V;
-  const DrawInfo di = P.info[b];
-  if (di.j < 0) return;                       // k_accept already wrote -1s
-  DrawRow R = draw_row<DT>(P, b, di);
   const long long ubase = (long long)b * (g + 1);
+  // everything this kernel reads first, issued together
+  const DrawInfo di = P.info[b];
+  const float u = P.unif[ubase + g];
   const double* seg = P.segsum + (long long)b * P.nseg;
   for (int t = tid; t < P.nseg; t += kBlock) sh_seg[t] = seg[t];
   __syncthreads();
-  if (tid == 0) {
+  if (di.j < 0) return;                       // k_draw_mass (b, 0) wrote the -1s
+  DrawRow R = draw_row<DT>(P, b, di);
+  if (wid == 0) {
     double total = 0.0;
-    for (int t = 0; t < P.nseg; ++t) total += sh_seg[t];
-    sh_fallback = total > 0.0 ? 0 : 1;
-    sh_thr = (double)P.unif[ubase + g] * total;
+    for (int c0 = 0; c0 < P.nseg; c0 += kWave)
+      total += wave_sum(c0 + lane < P.nseg ? sh_seg[c0 + lane] : 0.0);
+    if (lane == 0) {
+      sh_fallback = total > 0.0 ? 0 : 1;
+      sh_thr = (double)u * total;
+    }
   }
   __syncthreads();
   if (sh_fallback) {
@@ -287,26 +289,24 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
       if (tid == 0) sh_seg[t] = m;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (wid == 0) {
       double total = 0.0;
-      for (int t = 0; t < P.nseg; ++t) total += sh_seg[t];
-      sh_thr = (double)P.unif[ubase + g] * total;
+      for (int c0 = 0; c0 < P.nseg; c0 += kWave)
+        total += wave_sum(c0 + lane < P.nseg ? sh_seg[c0 + lane] : 0.0);
+      if (lane == 0) sh_thr = (double)u * total;
     }
     __syncthreads();
   }
-  if (tid == 0) {
-    const double thr = sh_thr;
-    double acc = 0.0, lastbase = 0.0;
-    int k = -1, lastpos = 0;
-    for (int t = 0; t < P.nseg; ++t) {
-      const double m = sh_seg[t];
-      if (m > 0.0 && acc + m > thr) { k = t; break; }
-      if (m > 0.0) { lastpos = t; lastbase = acc; }
-      acc += m;
+  if (wid == 0) {
+    double base;
+    int fb;
+    const int k = locate_segment(sh_seg, P.nseg, sh_thr, lane, &base, &fb);
+    if (lane == 0) {
+      sh_k = k;
+      sh_base = base;
+      sh_fallback = fb;
+      sh_y = -1;
     }
-    if (k >= 0) { sh_k = k; sh_base = acc; sh_fallback = 0; }
-    else { sh_k = lastpos; sh_base = lastbase; sh_fallback = 1; }   // rounding: last positive segment
-    sh_y = -1;
   }
   __syncthreads();
   const long long kb = (long long)sh_k * P.seg_elems;
@@ -358,9 +358,11 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
       w[e] = v;
     }
   }
-  double T = 0.0;
+  // lane sum in run order through four interleaved fp64 chains
+  double T4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int e = 0; e < kRun; ++e) T += (double)w[e];
+  for (int e = 0; e < kRun; ++e) T4[e & 3] += (double)w[e];
+  const double T = (T4[0] + T4[1]) + (T4[2] + T4[3]);
   const double incl = wave_incl_scan(T, lane);
   if (lane == kWave - 1) sh_wtot[wid] = incl;
   __syncthreads();
@@ -396,12 +398,25 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   if (tid == 0) P.out_tokens[ubase + di.j] = (int)sh_y;
 }
 
-template <int DT, bool ALIGNED>
-hipError_t launch_sample_t(const SampleParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_accept<DT>), dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
-  hipLaunchKernelGGL((k_draw_mass<DT, ALIGNED>), dim3((unsigned)((long long)p.B * p.nseg)), dim3(kBlock), 0, s, p);
+template <int DT, bool ALIGNED, int NP>
+hipError_t launch_sample_np(const SampleParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_draw_mass<DT, ALIGNED, NP>), dim3((unsigned)((long long)p.B * p.nseg)), dim3(kBlock), 0, s,
+                     p);
   hipLaunchKernelGGL((k_draw_pick<DT, ALIGNED>), dim3((unsigned)p.B), dim3(kBlock), (size_t)p.nseg * 8, s, p);
   return hipGetLastError();
+}
+
+template <int DT, bool ALIGNED>
+hipError_t launch_sample_t(const SampleParams& p, hipStream_t s) {
+  switch (merge_group(p.nseg_rows)) {
+    case 1: return launch_sample_np<DT, ALIGNED, 1>(p, s);
+    case 2: return launch_sample_np<DT, ALIGNED, 2>(p, s);
+    case 4: return launch_sample_np<DT, ALIGNED, 4>(p, s);
+    case 8: return launch_sample_np<DT, ALIGNED, 8>(p, s);
+    case 16: return launch_sample_np<DT, ALIGNED, 16>(p, s);
+    case 32: return launch_sample_np<DT, ALIGNED, 32>(p, s);
+    default: return launch_sample_np<DT, ALIGNED, 64>(p, s);
+  }
 }
 
 }  // namespace

@@ -60,26 +60,70 @@ __device__ __forceinline__ void unpack(const v4i& v, float* out) {
 }
 
 // ------------------------------------------------------------ wave reductions
+// Within each 16-lane row: DPP quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror and row_mirror pair every lane with partners that cover
+// the row, so after four steps all 16 lanes hold the same row value (each
+// step combines a and b as op(a, b) with a commutative op, so partners get
+// bitwise-equal results).  The four row values are then read with readlane
+// and combined in a fixed order; the result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const int lo = dpp_i<CTRL>(__double2loint(x));
+  const int hi = dpp_i<CTRL>(__double2hiint(x));
+  return __hiloint2double(hi, lo);
+}
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), l);
+  return __hiloint2double(hi, lo);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 __device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = min(x, dpp_i<kDppXor1>(x));
+  x = min(x, dpp_i<kDppXor2>(x));
+  x = min(x, dpp_i<kDppHalfMirror>(x));
+  x = min(x, dpp_i<kDppMirror>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 __device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = max(x, dpp_i<kDppXor1>(x));
+  x = max(x, dpp_i<kDppXor2>(x));
+  x = max(x, dpp_i<kDppHalfMirror>(x));
+  x = max(x, dpp_i<kDppMirror>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-// Fixed butterfly: the result depends only on the lane values, never on timing.
+// Fixed combination order: the result depends only on the lane values.
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x += dpp_d<kDppXor1>(x);
+  x += dpp_d<kDppXor2>(x);
+  x += dpp_d<kDppHalfMirror>(x);
+  x += dpp_d<kDppMirror>(x);
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
 // Inclusive prefix sum over the 64 lanes (Hillis-Steele, fixed order).
 __device__ __forceinline__ double wave_incl_scan(double x, int lane) {
@@ -88,6 +132,39 @@ __device__ __forceinline__ double wave_incl_scan(double x, int lane) {
     const double y = __shfl_up(x, o, kWave);
     if (lane >= o) x += y;
   }
+  return x;
+}
+
+// Reductions inside aligned groups of G lanes (G a power of two <= 64); every
+// lane of a group gets the group's value.
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (G >= 2) x = fmaxf(x, dpp_f<kDppXor1>(x));
+  if constexpr (G >= 4) x = fmaxf(x, dpp_f<kDppXor2>(x));
+  if constexpr (G >= 8) x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  if constexpr (G >= 16) x = fmaxf(x, dpp_f<kDppMirror>(x));
+  if constexpr (G >= 32) x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  if constexpr (G >= 64) x = fmaxf(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+template <int G>
+__device__ __forceinline__ int group_min(int x) {
+  if constexpr (G >= 2) x = min(x, dpp_i<kDppXor1>(x));
+  if constexpr (G >= 4) x = min(x, dpp_i<kDppXor2>(x));
+  if constexpr (G >= 8) x = min(x, dpp_i<kDppHalfMirror>(x));
+  if constexpr (G >= 16) x = min(x, dpp_i<kDppMirror>(x));
+  if constexpr (G >= 32) x = min(x, __shfl_xor(x, 16, kWave));
+  if constexpr (G >= 64) x = min(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+template <int G>
+__device__ __forceinline__ double group_sum(double x) {
+  if constexpr (G >= 2) x += dpp_d<kDppXor1>(x);
+  if constexpr (G >= 4) x += dpp_d<kDppXor2>(x);
+  if constexpr (G >= 8) x += dpp_d<kDppHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp_d<kDppMirror>(x);
+  if constexpr (G >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32, kWave);
   return x;
 }
 
@@ -162,11 +239,61 @@ struct DrawInfo {
   double rho;   // S_t / S_d of row j (j < gamma)
 };
 
-// Per-row statistics handed between kernels.
+// Per-segment statistics handed from the row sweep to its consumers.
 struct Partial {
   float m;      // max of the segment (or -inf)
   int arg;      // lowest row-local index holding m (INT_MAX if none)
-  double s;     // sum of 2^((z - m) c) over the segment, exact reference m
+  float K;      // exponent offset of s: s = sum 2^(z c - K) over the segment
+  float pad_;
+  double s;
 };
+
+// Merge a row's segment partials within a group of GROUP consecutive lanes
+// (GROUP a power of two dividing 64; gl = lane index inside the group).  The
+// row max M is the group max of the partial maxima; the row sum relative to
+// it is sum_s s_s 2^(K_s - M c), formed in fp64 with the group's lanes
+// adding their partials in segment order and the group combining them in a
+// fixed order.  Returns M, the sum (WANT & 1) and the lowest index holding
+// M (WANT & 2; 0 for a row of -inf).
+template <int WANT, int GROUP>
+__device__ __forceinline__ void merge_partials(const Partial* part, int nseg, const TempConst& tc, int gl,
+                                               float* M_out, double* S_out, int* A_out) {
+  const float NEG_INF = -__builtin_huge_valf();
+  float m = NEG_INF;
+  int a = 0x7fffffff;
+  for (int t = gl; t < nseg; t += GROUP) {
+    const Partial pp = part[t];
+    if (pp.m > m) {
+      m = pp.m;
+      a = pp.arg;
+    } else if (pp.m == m) {
+      a = min(a, pp.arg);
+    }
+  }
+  const float M = group_max<GROUP>(m);
+  double sv = 0.0;
+  if constexpr ((WANT & 1) != 0) {
+    if (M != NEG_INF) {
+      const double Mc = (double)M * tc.c64;
+      for (int t = gl; t < nseg; t += GROUP) {
+        const Partial pp = part[t];
+        if (pp.m != NEG_INF) sv += pp.s * exp2_f64((double)pp.K - Mc);
+      }
+    }
+    sv = group_sum<GROUP>(sv);
+  }
+  int aa = (m == M && M != NEG_INF) ? a : 0x7fffffff;
+  if constexpr ((WANT & 2) != 0) aa = group_min<GROUP>(aa);
+  *M_out = M;
+  *S_out = sv;
+  *A_out = aa == 0x7fffffff ? 0 : aa;
+}
+
+// Lane-group width for merging nseg partials: the next power of two, at most 64.
+inline int merge_group(int nseg) {
+  int g = 1;
+  while (g < nseg && g < 64) g <<= 1;
+  return g;
+}
 
 }  // namespace sv

@@ -18,11 +18,17 @@ struct RowStatsParams {
   long long rows0;
   long long rows1;
   int V;
-  int nseg;       // wave segments per row
+  int nseg;       // workgroup segments per row
   int seg_vecs;   // full 16-byte vectors per segment
   int want;       // bit 0: max/sum, bit 1: argmax
   TempConst tc;
   Partial* part;  // [rows][nseg]
+  // optional gather: for target row (b, i) with i < gather_g and draft row
+  // (b, i), store z[row][tokens[b][i]] into gather_out[row] (rows of the
+  // second tensor continue after rows0)
+  const int* gather_tokens;
+  int gather_g;
+  float* gather_out;
   float* out_max; // [rows]
   double* out_sum;// [rows] (want & 1)
   int* out_arg;   // [rows] (want & 2)
@@ -33,15 +39,16 @@ struct RowSweepShape {
   int seg_vecs;
 };
 RowSweepShape row_sweep_shape(int V, int dt);
+// Sweep then merge (final per-row statistics in out_*).
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);
-// The sweep alone (partials only); the sampling path merges its rows itself.
+// The sweep alone (partials only); its consumers merge partials inline.
 hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s);
+hipError_t launch_row_merge(const RowStatsParams& p, hipStream_t s);
 
 // ---------------------------------------------------------- sampling
-// Three kernels after the row sweep: the accept scan (one workgroup per
-// sequence, which also merges that sequence's row partials), the residual /
-// bonus segment masses (B x nseg workgroups) and the inverse-CDF draw (one
-// workgroup per sequence).
+// Two kernels after the row sweep: the accept scan plus the residual / bonus
+// segment masses (B x nseg workgroups; each merges its sequence's row
+// partials) and the inverse-CDF draw (one workgroup per sequence).
 struct SampleParams {
   const void* tgt;        // [B, g+1, V]
   const void* drf;        // [B, g, V]
@@ -49,8 +56,7 @@ struct SampleParams {
   const float* unif;      // [B, g+1]
   const Partial* part;    // [rows][nseg_rows] row-sweep partials
   int nseg_rows;
-  float* row_max;         // [B(g+1) target rows, then B g draft rows]
-  double* row_sum;
+  const float* gathered;  // [rows] z[row][x] picked out by the sweep
   int B, g, V;
   int nseg;               // draw segments per row
   int seg_elems;          // elements per draw segment (multiple of 8)
@@ -65,7 +71,8 @@ hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s);
 
 // ---------------------------------------------------------- greedy / tree
 struct GreedyParams {
-  const int* arg;         // [B(g+1)] row argmax
+  const Partial* part;    // [B(g+1)][nseg] row-sweep partials (argmax)
+  int nseg;
   const int* tokens;      // [B, g]
   int B, g;
   int* accept_len;
@@ -74,7 +81,8 @@ struct GreedyParams {
 hipError_t launch_greedy_finish(const GreedyParams& p, hipStream_t s);
 
 struct TreeParams {
-  const int* arg;         // [B N] row argmax
+  const Partial* part;    // [B N][nseg] row-sweep partials (argmax)
+  int nseg;
   const int* node_tokens; // [B, N]
   const int* parent;      // [N] or [B, N]
   int parent_stride;      // 0 or N
