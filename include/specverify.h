@@ -199,7 +199,7 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  *
  * feat [M, d] bf16 bits; W [d, V] bf16 bits (vocabulary innermost);
  * out_logits [M, V] float32 (bf16 x bf16 products, float32 accumulation).
- * d must be a multiple of 64; 1 <= M, 1 <= V.
+ * d must be a multiple of 64; 1 <= M <= 2^22, 1 <= V < 2^25.
  */
 spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W,
                            int V, float* out_logits, hipStream_t s);
@@ -211,6 +211,8 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
  * held in the workspace, then spec_verify_sample runs on them without a
  * host round trip.  Same outputs and uniforms convention as
  * spec_verify_sample.  d must be a multiple of 64.
+ * Features that are not already one contiguous block (draft rows right after
+ * the target rows) are first copied into the workspace.
  * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
  * the call the logits are left in the last ceil256(B(2 gamma+1) V 4) bytes
  * of the workspace: B(gamma+1) target rows, then B gamma draft rows.

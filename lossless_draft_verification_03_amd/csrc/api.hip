@@ -23,7 +23,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // is fully written before it is read within one call, so a workspace needs
 // no initialisation and can be shared by calls of any layout (one at a time).
 struct Layout {
-  size_t info, part, rmax, rsum, rarg, gath, segsum, logits, total;
+  size_t info, part, rmax, rsum, rarg, gath, segsum, hcat, logits, total;
   long long rows;
   int nseg, nseg2;
 };
@@ -70,6 +70,8 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   L->rarg = o;   o = up(o + (size_t)rows * 4);
   L->gath = o;   o = up(o + (size_t)rows * 4);
   L->segsum = o; o = up(o + (size_t)seqs * nseg2 * 8);
+  L->hcat = o;
+  if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)d * 2);
   L->logits = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)V * 4);
   L->total = o;
@@ -329,13 +331,12 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
 spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W, int V,
                            float* out_logits, hipStream_t s) {
   if (M < 1 || M > (1 << 22) || d < 64 || d % 64 != 0 || d > (1 << 20) || V < 1) return SPEC_EINVAL;
+  if ((long long)V * 128 >= (1LL << 32) || 256LL * d * 2 >= (1LL << 32)) return SPEC_EINVAL;
   if (!feat || !W || !out_logits) return SPEC_EINVAL;
   if (!aligned(feat, 16) || !aligned(W, 16) || !aligned(out_logits, 16)) return SPEC_EALIGN;
   LmHeadParams p;
-  p.A0 = feat;
-  p.A1 = nullptr;
-  p.M0 = M;
-  p.M1 = 0;
+  p.A = feat;
+  p.M = M;
   p.W = W;
   p.K = d;
   p.N = V;
@@ -350,6 +351,7 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB)
     return SPEC_EINVAL;
   if (d < 64 || d % 64 != 0 || d > (1 << 20)) return SPEC_EINVAL;
+  if ((long long)V * 128 >= (1LL << 32)) return SPEC_EINVAL;
   if (!target_feat || !draft_feat || !W || !draft_tokens || !uniforms || !accept_len || !out_tokens)
     return SPEC_EINVAL;
   if (!aligned(target_feat, 16) || !aligned(draft_feat, 16) || !aligned(W, 16) ||
@@ -363,11 +365,19 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   const spec_status w = check_ws(ws, ws_bytes, L);
   if (w != SPEC_OK) return w;
   float* Z = at<float>(ws, L.logits);
+  // the GEMM reads all B(2 gamma + 1) feature rows from one block
+  const size_t tbytes = (size_t)B * (gamma + 1) * (size_t)d * 2, dbytes = (size_t)B * gamma * (size_t)d * 2;
+  const uint16_t* H = target_feat;
+  if ((const char*)draft_feat != (const char*)target_feat + tbytes) {
+    uint16_t* hc = at<uint16_t>(ws, L.hcat);
+    if (hipMemcpyAsync(hc, target_feat, tbytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return SPEC_EHIP;
+    if (hipMemcpyAsync((char*)hc + tbytes, draft_feat, dbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return SPEC_EHIP;
+    H = hc;
+  }
   LmHeadParams p;
-  p.A0 = target_feat;
-  p.A1 = draft_feat;
-  p.M0 = B * (gamma + 1);
-  p.M1 = B * gamma;
+  p.A = H;
+  p.M = B * (2 * gamma + 1);
   p.W = W;
   p.K = d;
   p.N = V;

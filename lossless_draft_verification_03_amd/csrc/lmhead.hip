@@ -6,13 +6,42 @@
 // and "Why feature drafting lands a higher acceptance rate" (drafted features
 // are decoded through the target's own, unchanged head).
 //
-// C[M, N] = A[M, K] W[K, N]; A = feature rows (K contiguous), W = the head
-// with the vocabulary innermost, C fp32.  Rows of A come from two tensors
-// (target features, then draft features) so the head is streamed once for
-// both.  Workgroup tile 128 x 128, K step 32, four waves in a 2 x 2 grid of
-// 64 x 64 wave tiles, each a 2 x 2 grid of v_mfma_f32_32x32x16_bf16.  W tiles
-// are transposed into LDS (k contiguous per column) so both MFMA operands are
-// 16-byte LDS reads.
+// C[M, N] = A[M, K] W[K, N]; A = feature rows (K contiguous, one tensor:
+// lmhead_verify first gathers target and draft features into one block so
+// the head is streamed once for both), W = the head with the vocabulary
+// innermost, C fp32.
+//
+// Workgroup tile 256 x 256, K step 32, four waves in a 2 x 2 grid of
+// 128 x 128 wave tiles, each a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 with
+// 256 fp32 accumulators per lane.
+//
+// Operand staging: the global loads write straight into LDS (buffer loads
+// with the LDS destination; lane i of one such load fills bytes 16 i .. 16 i
+// + 15 after the wave-uniform base), so no registers hold tiles in flight.
+// Four LDS stages form a ring and the loads of step k + 3 are issued at the
+// start of step k, three steps of MFMA work ahead of their use.  Each stage
+// buffer is its own LDS object so the compiler's wait analysis can tell the
+// ring slots apart; the one barrier per step is preceded by an explicit wait
+// for this wave's oldest load group only.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so the operand reads below hit
+// distinct banks; the swizzle only renames which global chunk a lane fetches):
+//   A stage: 256 rows x 64 bytes; chunk c of row r sits at 4 r + (c ^ sa(r)).
+//     The MFMA A operand (lane l: row l % 32, 8 consecutive k) is one
+//     ds_read_b128.
+//   W stage: 32 rows (k) x 512 bytes, as stored (n innermost); the 32-byte
+//     unit u of row r sits at unit u ^ sb(r).  The MFMA B operand needs
+//     8 consecutive k of one column per lane; gfx950's transposing read
+//     ds_read_b64_tr_b16 delivers four at a time: within each 16-lane group,
+//     output lane i, element t comes from source lane i/4 + 4t, element i%4,
+//     so a source lane j that reads row k0 + j/4, columns n0 + 4 (j%4) .. +3
+//     hands lane i the values W[k0 .. k0+3][n0 + i].
+// Vocabulary sizes that are not a multiple of 8 (rows of W not 16-byte
+// aligned) stage W through registers with element loads instead.
+//
+// Tiles are ordered so that the M tiles of an N tile land on the same XCD
+// (workgroups are dealt round-robin over the 8 XCDs), letting them share the
+// W tile through that XCD's L2.
 #include "sv_kernels.hpp"
 
 namespace sv {
@@ -20,93 +49,229 @@ namespace sv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 8;   // padded k pitch (elements) of both LDS tiles
+constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
+constexpr int kChunksPerStage = BM * BK / 8;      // 1024 16-byte chunks (A and W alike)
+constexpr int kLoadsPerWave = kChunksPerStage / 256;  // 4 wave loads of 64 chunks
+constexpr int kXcd = 8;
+static_assert(BM * BK == BK * BN, "A and W stages have the same size");
 
-template <bool NVEC>
-__global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][LDK];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// A row r: chunk swizzle (2 bits).  Rows 0..7 of any aligned 8-row group
+// (and 0..15 of a 16-row group) land on distinct (row pair, chunk) bank slots.
+__device__ __forceinline__ int swz_a(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+// W row r: 32-byte-unit swizzle (3 bits), by r % 4 from {0, 2, 5, 7}.
+__device__ __forceinline__ int swz_b(int r) { return (0x7520 >> (4 * (r & 3))) & 0xF; }
+
+// s_waitcnt with only vmcnt = n (gfx9 encoding: expcnt and lgkmcnt at max)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// 16-byte buffer load of lane i into LDS bytes lds_base + 16 i ..  Issued
+// through asm so that the compiler's wait analysis does not track it: its
+// completion is waited for explicitly (wait_vm) before the barrier of the step
+// that reads it.  rsrc: wave-uniform buffer descriptor words.
+__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+
+// raw descriptor words: base, stride 0, num_records = bytes, the same
+// format word make_rsrc uses
+__device__ __forceinline__ v4i rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)p;
+}
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
+}
+
+template <bool DMAB>
+__global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int ntiles) {
+  // one LDS object per ring slot: the A stage, then the W stage
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BM * BK], s1[2 * BM * BK], s2[2 * BM * BK],
+      s3[2 * BM * BK];
+  uint16_t* const SA[NS] = {s0, s1, s2, s3};
+  uint16_t* const SB[NS] = {s0 + BM * BK, s1 + BM * BK, s2 + BM * BK, s3 + BM * BK};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
-  const long long n0 = (long long)blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int M = P.M0 + P.M1;
-  const int K = P.K;
+  // XCD-aware tile order: slot s on XCD x takes N tile (s / mtiles) * 8 + x
+  const int w = blockIdx.x;
+  const int xcd = w % kXcd, slot = w / kXcd;
+  const int mt = slot % mtiles;
+  const int nt = (slot / mtiles) * kXcd + xcd;
+  if (nt >= ntiles) return;
+  const int m0 = mt * BM;
+  const long long n0 = (long long)nt * BN;
+  const int M = P.M, K = P.K;
   const long long N = P.N;
 
-  f32x16 acc[2][2];
+  // A rows past M read as zero through the descriptor bound
+  const int arows = min(BM, M - m0);
+  const v4i ra = rsrc_words(P.A + (long long)m0 * K, (uint32_t)((long long)arows * K * 2));
+  const uint16_t* const wtile = P.W + n0;
+  const long long wtotal = (long long)K * N - n0;  // elements of W from wtile on
+
+  // Chunk p of a stage (p = 64 (4 wid + t) + lane) is what this lane fetches
+  // in its t-th load of the step.
+  uint32_t aoff[kLoadsPerWave], boff[kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < kLoadsPerWave; ++t) {
+    const int p = (wid * kLoadsPerWave + t) * 64 + lane;
+    const int ra_ = p >> 2, pca = p & 3;
+    aoff[t] = (uint32_t)(ra_ * K * 2 + 16 * (pca ^ swz_a(ra_)));
+    const int rb = p >> 5, pcb = p & 31;
+    const int cb = 2 * ((pcb >> 1) ^ swz_b(rb)) + (pcb & 1);  // logical chunk of that slot
+    boff[t] = (uint32_t)((long long)rb * N * 2 + 16 * cb);
+  }
+
+  // issue the loads of K step ks into ring slot S
+  auto issue = [&](auto Sc, int ks) {
+    constexpr int S = decltype(Sc)::value;
+    const int k0 = ks * BK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int t = 0; t < kLoadsPerWave; ++t)
+      dma16(ra, lds_addr(SA[S] + (wid * kLoadsPerWave + t) * 512), aoff[t], (uint32_t)k0 * 2u);
+    const long long kbase = (long long)k0 * N;
+    if (DMAB) {
+      const long long left = wtotal - kbase;
+      const v4i rb = rsrc_words(wtile + kbase, (uint32_t)min(left * 2, (long long)BK * N * 2));
+#pragma unroll
+      for (int t = 0; t < kLoadsPerWave; ++t)
+        dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), boff[t], 0u);
+    } else {
+      // element loads; columns past N and rows past K read as zero
+#pragma unroll
+      for (int t = 0; t < kLoadsPerWave; ++t) {
+        const int p = (wid * kLoadsPerWave + t) * 64 + lane;
+        const int rb = p >> 5, pcb = p & 31;
+        const int cb = 2 * ((pcb >> 1) ^ swz_b(rb)) + (pcb & 1);
+        const long long gn = n0 + 8 * cb;
+        const uint16_t* src = wtile + kbase + (long long)rb * N + 8 * cb;
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = gn + i < N ? src[i] : (uint16_t)0;
+        v4i v;
+        v[0] = (int)(e[0] | ((uint32_t)e[1] << 16));
+        v[1] = (int)(e[2] | ((uint32_t)e[3] << 16));
+        v[2] = (int)(e[4] | ((uint32_t)e[5] << 16));
+        v[3] = (int)(e[6] | ((uint32_t)e[7] << 16));
+        *reinterpret_cast<v4i*>(SB[S] + p * 8) = v;
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    // A tile: 128 rows x 32 k = 512 vectors of 8 bf16.
+  // A operand: row wm*128 + 32 i + (lane % 32), chunk kk/8 + lane/32; the
+  // row's swizzle only depends on lane % 16
+  const int arow = lane & 31, achk = lane >> 5, asw = swz_a(arow);
+  // B operand (16-lane group g, lane jl in it): rows kk + 8 (g/2) + jl/4
+  // (+4 for the second read), unit wn*8 + 2 j + (g % 2), bytes 8 (jl % 4)
+  const int g = lane >> 4, jl = lane & 15;
+  const int brow = 8 * (g >> 1) + (jl >> 2);
+  const int bsw = swz_b(brow);
+  int bofs[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = tid + t * 256;
-      const int m = q >> 2, kv = (q & 3) * 8;
-      const int gm = m0 + m;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gm < M) {
-        const uint16_t* src = gm < P.M0 ? P.A0 + (long long)gm * K : P.A1 + (long long)(gm - P.M0) * K;
-        v = *reinterpret_cast<const uint4*>(src + k0 + kv);
-      }
-      *reinterpret_cast<uint4*>(&As[m][kv]) = v;
-    }
-    // W tile: 32 k x 128 n, written transposed (n-major, k contiguous).
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = tid + t * 256;
-      const int k = q >> 4, nv = (q & 15) * 8;
-      const long long gn = n0 + nv;
-      const uint16_t* src = P.W + (long long)(k0 + k) * N + gn;
-      uint16_t vals[8];
-      if (NVEC && gn + 8 <= N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        vals[0] = v.x & 0xffff; vals[1] = v.x >> 16; vals[2] = v.y & 0xffff; vals[3] = v.y >> 16;
-        vals[4] = v.z & 0xffff; vals[5] = v.z >> 16; vals[6] = v.w & 0xffff; vals[7] = v.w >> 16;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vals[i] = gn + i < N ? src[i] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Bs[nv + i][k] = vals[i];
-    }
-    __syncthreads();
+  for (int j = 0; j < 4; ++j)
+    bofs[j] = brow * BN + 16 * (wn * 8 + ((2 * j + (g & 1)) ^ bsw)) + 4 * (jl & 3);
+
+  auto compute = [&](auto Sc) {
+    constexpr int S = decltype(Sc)::value;
+    const uint16_t* As = SA[S];
+    const uint16_t* Bs = SB[S];
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[4], b[4];
+      const int ac = ((kk >> 3) + achk) ^ asw;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[wm * 64 + i * 32 + (lane & 31)][kk + (lane >> 5) * 8]);
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + arow) * BK + ac * 8);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk + (lane >> 5) * 8]);
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t* p = Bs + kk * BN + bofs[j];
+        const s16x4 lo = lds_tr16(p);
+        const s16x4 hi = lds_tr16(p + 4 * BN);
+        s16x4 both[2] = {lo, hi};
+        b[j] = *reinterpret_cast<const bf16x8*>(both);
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
+  };
+
+  // loads in flight per K step and wave (the element path waits for its own)
+  constexpr int kGroup = DMAB ? 2 * kLoadsPerWave : kLoadsPerWave;
+  const int nk = K / BK;
+  auto step = [&](auto Sc, int ks) {
+    constexpr int S = decltype(Sc)::value;
+    // this wave's loads of step ks are done once at most the groups of
+    // steps ks + 1 and ks + 2 remain outstanding
+    const int later = min(2, nk - 1 - ks);
+    if (later >= 2)
+      wait_vm<2 * kGroup>();
+    else if (later == 1)
+      wait_vm<kGroup>();
+    else
+      wait_vm<0>();
+    asm volatile("s_barrier" ::: "memory");
+    // every wave is past step ks - 1, so ring slot (ks + 3) % 4 is free
+    if (ks + 3 < nk) issue(std::integral_constant<int, (S + 3) % NS>{}, ks + 3);
+    compute(Sc);
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+  for (int ks = 0; ks < nk; ks += NS) {
+    step(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+    if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
+    if (ks + 3 < nk) step(std::integral_constant<int, 3>{}, ks + 3);
   }
+
   // Output layout of the 32 x 32 MFMA: lane l holds column l % 32 and rows
   // 8 (r / 4) + 4 (l / 32) + r % 4 for r = 0..15.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const long long col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const long long col = n0 + wn * 128 + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row < M) P.C[(long long)row * N + col] = acc[i][j][r];
       }
     }
@@ -115,12 +280,19 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P) {
 }  // namespace
 
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s) {
-  const int M = p.M0 + p.M1;
-  const long long gx = ((long long)p.N + BN - 1) / BN;
-  const long long gy = ((long long)M + BM - 1) / BM;
-  if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidValue;
-  if (p.N % 8 == 0) hipLaunchKernelGGL(k_lmhead<true>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(k_lmhead<false>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
+  if (p.K % BK != 0 || p.K < BK || p.M < 1 || p.N < 1) return hipErrorInvalidValue;
+  const long long nt = ((long long)p.N + BN - 1) / BN;
+  const long long mt = ((long long)p.M + BM - 1) / BM;
+  const long long per_xcd = (nt + kXcd - 1) / kXcd;
+  const long long grid = per_xcd * mt * kXcd;
+  // 32-bit buffer offsets: one A tile and one K step of W
+  if (grid > 0x7fffffffLL || (long long)BM * p.K * 2 >= (1LL << 32) || (long long)BK * p.N * 2 >= (1LL << 32))
+    return hipErrorInvalidValue;
+  // rows of W start 16-byte aligned only when N % 8 == 0
+  if (p.N % 8 == 0)
+    hipLaunchKernelGGL(k_lmhead<true>, dim3((unsigned)grid), dim3(256), 0, s, p, (int)mt, (int)nt);
+  else
+    hipLaunchKernelGGL(k_lmhead<false>, dim3((unsigned)grid), dim3(256), 0, s, p, (int)mt, (int)nt);
   return hipGetLastError();
 }
 

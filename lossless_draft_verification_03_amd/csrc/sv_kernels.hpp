@@ -112,12 +112,11 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 // ---------------------------------------------------------- LM head
 struct LmHeadParams {
-  const uint16_t* A0;     // [M0, K] bf16
-  const uint16_t* A1;     // [M1, K] bf16 (may be null)
-  int M0, M1;
+  const uint16_t* A;      // [M, K] bf16, rows 16-byte aligned
+  int M;
   const uint16_t* W;      // [K, N] bf16, N innermost
   int K, N;
-  float* C;               // [M0 + M1, N] fp32
+  float* C;               // [M, N] fp32
 };
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s);
 
