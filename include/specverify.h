@@ -72,6 +72,13 @@ typedef enum {
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
+/* Layout of the LM-head weight W. */
+typedef enum {
+  SPEC_W_DV = 0,  /* W[d][V]: vocabulary innermost                             */
+  SPEC_W_VD = 1   /* W[V][d]: feature dimension innermost, the layout in which
+                     a linear layer's weight is usually stored (faster path)  */
+} spec_wlayout;
+
 typedef enum {
   SPEC_MODE_SAMPLE = 0,   /* spec_verify_sample: gamma_or_N = gamma        */
   SPEC_MODE_GREEDY = 1,   /* spec_verify_greedy: gamma_or_N = gamma        */
@@ -197,12 +204,14 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * Tokens" (the LM head turns the top-layer feature into vocabulary logits;
  * the draft reuses the target's LM head); "EAGLE math", "EAGLE's move".
  *
- * feat [M, d] bf16 bits; W [d, V] bf16 bits (vocabulary innermost);
- * out_logits [M, V] float32 (bf16 x bf16 products, float32 accumulation).
- * d must be a multiple of 64; 1 <= M <= 2^22, 1 <= V < 2^25.
+ * feat [M, d] bf16 bits; W bf16 bits, [d, V] (wl = SPEC_W_DV) or [V, d]
+ * (wl = SPEC_W_VD); out_logits [M, V] float32 (bf16 x bf16 products, float32
+ * accumulation; both layouts give bit-identical logits).  feat, W and
+ * out_logits 16-byte aligned.  d must be a multiple of 64; 1 <= M <= 2^22,
+ * 1 <= V < 2^25.
  */
 spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W,
-                           int V, float* out_logits, hipStream_t s);
+                           spec_wlayout wl, int V, float* out_logits, hipStream_t s);
 
 /*
  * lmhead_verify -- EAGLE-style verification: the target features
@@ -210,7 +219,8 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
  * rows, row b*gamma+i) go through the shared LM head into float32 logits
  * held in the workspace, then spec_verify_sample runs on them without a
  * host round trip.  Same outputs and uniforms convention as
- * spec_verify_sample.  d must be a multiple of 64.
+ * spec_verify_sample.  W and its layout wl as in lmhead_project.  d must be a
+ * multiple of 64.
  * Features that are not already one contiguous block (draft rows right after
  * the target rows) are first copied into the workspace.
  * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
@@ -218,7 +228,7 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
  * of the workspace: B(gamma+1) target rows, then B gamma draft rows.
  */
 spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat,
-                          const uint16_t* W, const int32_t* draft_tokens,
+                          const uint16_t* W, spec_wlayout wl, const int32_t* draft_tokens,
                           const float* uniforms, int B, int gamma, int d, int V,
                           float temperature, int32_t* accept_len,
                           int32_t* out_tokens, void* ws, size_t ws_bytes,

@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     SPEC_BF16,
     SPEC_F32,
     SpecError,
+    W_DV,
+    W_VD,
     lib,
     lmhead_logits_view,
     lmhead_project,

@@ -23,6 +23,7 @@ lib = ctypes.CDLL(LIB_PATH)
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_EHIP = range(6)
 SPEC_F32, SPEC_BF16 = 0, 1
 MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS = range(5)
+W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (feature innermost)
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
 
@@ -35,8 +36,8 @@ _SIGS = {
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
-    "lmhead_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
+    "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_probe_probs": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGS)
@@ -166,25 +167,36 @@ def verify_tree(target, node_tokens, parent, ws=None, out=None):
     return out
 
 
-def lmhead_project(feat, W, out=None):
-    """feat [M, d] bf16 bits, W [d, V] bf16 bits -> fp32 logits [M, V]."""
+def _head_dims(W, layout):
+    if layout == W_DV:
+        return W.shape
+    if layout == W_VD:
+        return W.shape[1], W.shape[0]
+    raise ValueError("layout must be W_DV or W_VD")
+
+
+def lmhead_project(feat, W, out=None, layout=W_DV):
+    """feat [M, d] bf16 bits, W bf16 bits ([d, V] for W_DV, [V, d] for W_VD)
+    -> fp32 logits [M, V]."""
     M, d = feat.shape
-    V = W.shape[1]
+    _, V = _head_dims(W, layout)
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=feat.device)
-    _check(lib.lmhead_project(_ptr(feat), M, d, _ptr(W), V, _ptr(out), _stream(feat.device)), "lmhead_project")
+    _check(lib.lmhead_project(_ptr(feat), M, d, _ptr(W), layout, V, _ptr(out), _stream(feat.device)),
+           "lmhead_project")
     return out
 
 
-def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=None, out=None):
+def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=None, out=None, layout=W_DV):
     B, g = draft_tokens.shape
-    d, V = W.shape
+    d, V = _head_dims(W, layout)
     dev = W.device
     if out is None:
         out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
     acc, toks = out
     w = _workspace(MODE_LMHEAD, B, g, V, d, dev, ws)
-    _check(lib.lmhead_verify(_ptr(feat_t), _ptr(feat_d), _ptr(W), _ptr(draft_tokens), _ptr(uniforms), B, g, d, V,
+    _check(lib.lmhead_verify(_ptr(feat_t), _ptr(feat_d), _ptr(W), layout, _ptr(draft_tokens), _ptr(uniforms),
+                             B, g, d, V,
                              float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
            "lmhead_verify")
     return out

@@ -328,16 +328,17 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
   return hip_status(launch_tree_finish(p, s));
 }
 
-spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W, int V,
-                           float* out_logits, hipStream_t s) {
+spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W, spec_wlayout wl,
+                           int V, float* out_logits, hipStream_t s) {
   if (M < 1 || M > (1 << 22) || d < 64 || d % 64 != 0 || d > (1 << 20) || V < 1) return SPEC_EINVAL;
-  if ((long long)V * 128 >= (1LL << 32) || 256LL * d * 2 >= (1LL << 32)) return SPEC_EINVAL;
+  if (V >= (1 << 25) || (wl != SPEC_W_DV && wl != SPEC_W_VD)) return SPEC_EINVAL;
   if (!feat || !W || !out_logits) return SPEC_EINVAL;
   if (!aligned(feat, 16) || !aligned(W, 16) || !aligned(out_logits, 16)) return SPEC_EALIGN;
   LmHeadParams p;
   p.A = feat;
   p.M = M;
   p.W = W;
+  p.w_vd = wl == SPEC_W_VD;
   p.K = d;
   p.N = V;
   p.C = out_logits;
@@ -345,13 +346,13 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
 }
 
 spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
-                          const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d,
+                          spec_wlayout wl, const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d,
                           int V, float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
                           size_t ws_bytes, hipStream_t s) {
   if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB)
     return SPEC_EINVAL;
   if (d < 64 || d % 64 != 0 || d > (1 << 20)) return SPEC_EINVAL;
-  if ((long long)V * 128 >= (1LL << 32)) return SPEC_EINVAL;
+  if (V >= (1 << 25) || (wl != SPEC_W_DV && wl != SPEC_W_VD)) return SPEC_EINVAL;
   if (!target_feat || !draft_feat || !W || !draft_tokens || !uniforms || !accept_len || !out_tokens)
     return SPEC_EINVAL;
   if (!aligned(target_feat, 16) || !aligned(draft_feat, 16) || !aligned(W, 16) ||
@@ -379,6 +380,7 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   p.A = H;
   p.M = B * (2 * gamma + 1);
   p.W = W;
+  p.w_vd = wl == SPEC_W_VD;
   p.K = d;
   p.N = V;
   p.C = Z;

@@ -6,10 +6,12 @@
 // and "Why feature drafting lands a higher acceptance rate" (drafted features
 // are decoded through the target's own, unchanged head).
 //
-// C[M, N] = A[M, K] W[K, N]; A = feature rows (K contiguous, one tensor:
+// C[M, N] = A[M, K] W; A = feature rows (K contiguous, one tensor:
 // lmhead_verify first gathers target and draft features into one block so
-// the head is streamed once for both), W = the head with the vocabulary
-// innermost, C fp32.
+// the head is streamed once for both), C fp32.  W comes in either layout:
+// [N, K] with the feature dimension innermost (a linear layer's weight as
+// checkpoints store it; the fast path), or [K, N] with the vocabulary
+// innermost.
 //
 // Workgroup tile 256 x 256, K step 32, four waves in a 2 x 2 grid of
 // 128 x 128 wave tiles, each a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 with
@@ -18,26 +20,30 @@
 // Operand staging: the global loads write straight into LDS (buffer loads
 // with the LDS destination; lane i of one such load fills bytes 16 i .. 16 i
 // + 15 after the wave-uniform base), so no registers hold tiles in flight.
-// Four LDS stages form a ring and the loads of step k + 3 are issued at the
-// start of step k, three steps of MFMA work ahead of their use.  Each stage
-// buffer is its own LDS object so the compiler's wait analysis can tell the
-// ring slots apart; the one barrier per step is preceded by an explicit wait
-// for this wave's oldest load group only.
+// Four LDS stages form a ring and the loads of step k + 3 are issued during
+// step k, between its MFMAs, about three steps of MFMA work ahead of their
+// use, spread one per two MFMAs.  The one barrier per step sits in the middle
+// of the step's MFMA stream and is preceded by an explicit wait for this
+// wave's oldest load group only.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so the operand reads below hit
 // distinct banks; the swizzle only renames which global chunk a lane fetches):
 //   A stage: 256 rows x 64 bytes; chunk c of row r sits at 4 r + (c ^ sa(r)).
 //     The MFMA A operand (lane l: row l % 32, 8 consecutive k) is one
 //     ds_read_b128.
-//   W stage: 32 rows (k) x 512 bytes, as stored (n innermost); the 32-byte
-//     unit u of row r sits at unit u ^ sb(r).  The MFMA B operand needs
+//   W[N][K] stage: 256 rows (n) x 64 bytes, exactly like A; the MFMA B
+//     operand (lane l: column l % 32, 8 consecutive k) is one ds_read_b128.
+//   W[K][N] stage: 32 rows (k) x 512 bytes, as stored (n innermost); the
+//     32-byte unit u of row r sits at unit u ^ sb(r).  The B operand needs
 //     8 consecutive k of one column per lane; gfx950's transposing read
 //     ds_read_b64_tr_b16 delivers four at a time: within each 16-lane group,
 //     output lane i, element t comes from source lane i/4 + 4t, element i%4,
 //     so a source lane j that reads row k0 + j/4, columns n0 + 4 (j%4) .. +3
-//     hands lane i the values W[k0 .. k0+3][n0 + i].
-// Vocabulary sizes that are not a multiple of 8 (rows of W not 16-byte
-// aligned) stage W through registers with element loads instead.
+//     hands lane i the values W[k0 .. k0+3][n0 + i].  A transposing read
+//     moves half the bytes of a ds_read_b128 in more LDS cycles, which makes
+//     this layout LDS-bound.  Vocabulary sizes that are not a multiple of 8
+//     (rows not 16-byte aligned) stage this layout through registers with
+//     element loads instead.
 //
 // Tiles are ordered so that the M tiles of an N tile land on the same XCD
 // (workgroups are dealt round-robin over the 8 XCDs), letting them share the
@@ -106,7 +112,12 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
 }
 
-template <bool DMAB>
+// W layouts and staging paths of the kernel
+constexpr int kWDvElem = 0;  // W[K][N], N % 8 != 0: element loads through registers
+constexpr int kWDvDma = 1;   // W[K][N]: LDS-DMA, transposing LDS reads
+constexpr int kWVd = 2;      // W[N][K]: LDS-DMA, plain LDS reads (like A)
+
+template <int WL>
 __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int ntiles) {
   // one LDS object per ring slot: the A stage, then the W stage
   __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BM * BK], s1[2 * BM * BK], s2[2 * BM * BK],
@@ -147,29 +158,30 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
     boff[t] = (uint32_t)((long long)rb * N * 2 + 16 * cb);
   }
 
-  // issue the loads of K step ks into ring slot S
-  auto issue = [&](auto Sc, int ks) {
+  // load q (0..3: A chunks, 4..7: W chunks) of K step ks into ring slot S;
+  // rb = the W descriptor of that step
+  auto issue_one = [&](auto Sc, int ks, int q, const v4i& rb) {
     constexpr int S = decltype(Sc)::value;
     const int k0 = ks * BK;
-#pragma unroll
-    for (int t = 0; t < kLoadsPerWave; ++t)
-      dma16(ra, lds_addr(SA[S] + (wid * kLoadsPerWave + t) * 512), aoff[t], (uint32_t)k0 * 2u);
-    const long long kbase = (long long)k0 * N;
-    if (DMAB) {
-      const long long left = wtotal - kbase;
-      const v4i rb = rsrc_words(wtile + kbase, (uint32_t)min(left * 2, (long long)BK * N * 2));
-#pragma unroll
-      for (int t = 0; t < kLoadsPerWave; ++t)
-        dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), boff[t], 0u);
-    } else {
-      // element loads; columns past N and rows past K read as zero
+    if (q < kLoadsPerWave) {
+      dma16(ra, lds_addr(SA[S] + (wid * kLoadsPerWave + q) * 512), aoff[q], (uint32_t)k0 * 2u);
+    } else if (WL == kWDvDma) {
+      const int t = q - kLoadsPerWave;
+      dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), boff[t], 0u);
+    } else if (WL == kWVd) {
+      // rows n0 .. n0 + 255 of W[N][K]: the same tile shape and swizzle as A
+      const int t = q - kLoadsPerWave;
+      dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), aoff[t], (uint32_t)k0 * 2u);
+    } else if (q == kLoadsPerWave) {
+      // element loads of the whole W stage; columns past N read as zero
+      const long long kbase = (long long)k0 * N;
 #pragma unroll
       for (int t = 0; t < kLoadsPerWave; ++t) {
         const int p = (wid * kLoadsPerWave + t) * 64 + lane;
-        const int rb = p >> 5, pcb = p & 31;
-        const int cb = 2 * ((pcb >> 1) ^ swz_b(rb)) + (pcb & 1);
+        const int rb_ = p >> 5, pcb = p & 31;
+        const int cb = 2 * ((pcb >> 1) ^ swz_b(rb_)) + (pcb & 1);
         const long long gn = n0 + 8 * cb;
-        const uint16_t* src = wtile + kbase + (long long)rb * N + 8 * cb;
+        const uint16_t* src = wtile + kbase + (long long)rb_ * N + 8 * cb;
         uint16_t e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = gn + i < N ? src[i] : (uint16_t)0;
@@ -181,6 +193,13 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
         *reinterpret_cast<v4i*>(SB[S] + p * 8) = v;
       }
     }
+  };
+  auto w_rsrc = [&](int ks) {
+    // W[N][K]: one descriptor for the tile's rows (rows past N read as zero)
+    if (WL == kWVd) return rsrc_words(P.W + n0 * K, (uint32_t)(min((long long)BN, N - n0) * K * 2));
+    // W[K][N]: K step ks of this tile's columns
+    const long long kbase = (long long)ks * BK * N;
+    return rsrc_words(wtile + kbase, (uint32_t)min((wtotal - kbase) * 2, (long long)BK * N * 2));
   };
 
   f32x16 acc[4][4];
@@ -204,62 +223,116 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   for (int j = 0; j < 4; ++j)
     bofs[j] = brow * BN + 16 * (wn * 8 + ((2 * j + (g & 1)) ^ bsw)) + 4 * (jl & 3);
 
-  auto compute = [&](auto Sc) {
-    constexpr int S = decltype(Sc)::value;
+  // operand fragments: set 0 holds the k sub-step kk = 0 of a K step, set 1
+  // the sub-step kk = 16
+  bf16x8 fa[2][4], fb[2][4];
+  // fragment pair idx of sub-step H: A rows wm*128 + 32 idx.., W columns
+  // wn*128 + 32 idx..
+  auto read_pair = [&](auto Sc, auto Hc, int idx) {
+    constexpr int S = decltype(Sc)::value, H = decltype(Hc)::value, kk = 16 * H;
     const uint16_t* As = SA[S];
     const uint16_t* Bs = SB[S];
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 a[4], b[4];
-      const int ac = ((kk >> 3) + achk) ^ asw;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + arow) * BK + ac * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint16_t* p = Bs + kk * BN + bofs[j];
-        const s16x4 lo = lds_tr16(p);
-        const s16x4 hi = lds_tr16(p + 4 * BN);
-        s16x4 both[2] = {lo, hi};
-        b[j] = *reinterpret_cast<const bf16x8*>(both);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    const int ac = ((kk >> 3) + achk) ^ asw;
+    fa[H][idx] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + idx * 32 + arow) * BK + ac * 8);
+    if (WL == kWVd) {
+      fb[H][idx] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 128 + idx * 32 + arow) * BK + ac * 8);
+    } else {
+      const uint16_t* p = Bs + kk * BN + bofs[idx];
+      const s16x4 lo = lds_tr16(p);
+      const s16x4 hi = lds_tr16(p + 4 * BN);
+      s16x4 both[2] = {lo, hi};
+      fb[H][idx] = *reinterpret_cast<const bf16x8*>(both);
     }
   };
+  auto read_frags = [&](auto Sc, auto Hc) {
+#pragma unroll
+    for (int idx = 0; idx < 4; ++idx) read_pair(Sc, Hc, idx);
+  };
+  auto mfma = [&](auto Hc, int q) {
+    constexpr int H = decltype(Hc)::value;
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[H][i], fb[H][j], acc[i][j], 0, 0, 0);
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
 
-  // loads in flight per K step and wave (the element path waits for its own)
-  constexpr int kGroup = DMAB ? 2 * kLoadsPerWave : kLoadsPerWave;
+  // loads in flight per K step and wave (the element path waits for its own
+  // W loads, leaving only the A loads)
+  constexpr int kGroup = WL == kWDvElem ? kLoadsPerWave : 2 * kLoadsPerWave;
   const int nk = K / BK;
+
+  // One K step in two halves.  First half: the kk = 0 MFMAs, while the
+  // kk = 16 fragments of this step are read.  Then the barrier that releases
+  // K step ks + 1 (every wave is past step ks - 1 there, so ring slot
+  // (ks + 3) % 4 is free too).  Second half: the kk = 16 MFMAs, with the
+  // loads of step ks + 3 and the kk = 0 fragments of step ks + 1 issued
+  // between them, so the MFMA pipe does not wait on a barrier or an LDS read.
+  // Past the last K step the loads re-fetch that step into the free slot
+  // (never read) and the fragment reads fetch unused data: the wait counts
+  // stay the same on every step and the stream has no branches.
   auto step = [&](auto Sc, int ks) {
     constexpr int S = decltype(Sc)::value;
-    // this wave's loads of step ks are done once at most the groups of
-    // steps ks + 1 and ks + 2 remain outstanding
-    const int later = min(2, nk - 1 - ks);
-    if (later >= 2)
-      wait_vm<2 * kGroup>();
-    else if (later == 1)
-      wait_vm<kGroup>();
-    else
-      wait_vm<0>();
+    read_frags(Sc, H1{});
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mfma(H0{}, q);
+    // interleave: one MFMA, one LDS read, twelve times; then four MFMAs
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of step ks + 1 are done once at most the group of
+    // step ks + 2 remains outstanding
+    wait_vm<kGroup>();
     asm volatile("s_barrier" ::: "memory");
-    // every wave is past step ks - 1, so ring slot (ks + 3) % 4 is free
-    if (ks + 3 < nk) issue(std::integral_constant<int, (S + 3) % NS>{}, ks + 3);
-    compute(Sc);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kl = min(ks + 3, nk - 1);
+    const v4i rb = w_rsrc(kl);
+    // the loads go out one per two MFMAs so the texture address unit sees a
+    // steady stream (a load that finds its queue full stalls this wave's
+    // MFMA issue behind it); the fragment reads fill the odd slots
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mfma(H1{}, q);
+      if ((q & 1) == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one(std::integral_constant<int, (S + 3) % NS>{}, kl, q >> 1, rb);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (q < 8) {
+        read_pair(std::integral_constant<int, (S + 1) % NS>{}, H0{}, q >> 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(std::integral_constant<int, 0>{}, 0);
-  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
-  if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+  {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    const int k1 = min(1, nk - 1), k2 = min(2, nk - 1);
+    const v4i r0 = w_rsrc(0);
+#pragma unroll
+    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S0{}, 0, q, r0);
+    const v4i r1 = w_rsrc(k1);
+#pragma unroll
+    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S1{}, k1, q, r1);
+    const v4i r2 = w_rsrc(k2);
+#pragma unroll
+    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S2{}, k2, q, r2);
+    wait_vm<2 * kGroup>();
+    asm volatile("s_barrier" ::: "memory");
+    read_frags(S0{}, H0{});
+  }
   for (int ks = 0; ks < nk; ks += NS) {
     step(std::integral_constant<int, 0>{}, ks);
     if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
     if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
     if (ks + 3 < nk) step(std::integral_constant<int, 3>{}, ks + 3);
   }
+  // no load may still be writing LDS when the workgroup ends
+  wait_vm<0>();
 
   // Output layout of the 32 x 32 MFMA: lane l holds column l % 32 and rows
   // 8 (r / 4) + 4 (l / 32) + r % 4 for r = 0..15.
@@ -285,14 +358,16 @@ hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s) {
   const long long mt = ((long long)p.M + BM - 1) / BM;
   const long long per_xcd = (nt + kXcd - 1) / kXcd;
   const long long grid = per_xcd * mt * kXcd;
-  // 32-bit buffer offsets: one A tile and one K step of W
-  if (grid > 0x7fffffffLL || (long long)BM * p.K * 2 >= (1LL << 32) || (long long)BK * p.N * 2 >= (1LL << 32))
-    return hipErrorInvalidValue;
-  // rows of W start 16-byte aligned only when N % 8 == 0
-  if (p.N % 8 == 0)
-    hipLaunchKernelGGL(k_lmhead<true>, dim3((unsigned)grid), dim3(256), 0, s, p, (int)mt, (int)nt);
+  // 32-bit buffer offsets: one A tile, one W tile, one K step of W[K][N]
+  if (grid > 0x7fffffffLL || (long long)BM * p.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
+  if (!p.w_vd && (long long)BK * p.N * 2 >= (1LL << 32)) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), b(256);
+  if (p.w_vd)
+    hipLaunchKernelGGL(k_lmhead<kWVd>, g, b, 0, s, p, (int)mt, (int)nt);
+  else if (p.N % 8 == 0)  // rows of W[K][N] start 16-byte aligned
+    hipLaunchKernelGGL(k_lmhead<kWDvDma>, g, b, 0, s, p, (int)mt, (int)nt);
   else
-    hipLaunchKernelGGL(k_lmhead<false>, dim3((unsigned)grid), dim3(256), 0, s, p, (int)mt, (int)nt);
+    hipLaunchKernelGGL(k_lmhead<kWDvElem>, g, b, 0, s, p, (int)mt, (int)nt);
   return hipGetLastError();
 }
 

@@ -114,7 +114,8 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 struct LmHeadParams {
   const uint16_t* A;      // [M, K] bf16, rows 16-byte aligned
   int M;
-  const uint16_t* W;      // [K, N] bf16, N innermost
+  const uint16_t* W;      // [K, N] bf16, N innermost (w_vd = 0) or [N, K], K innermost (w_vd = 1)
+  int w_vd;
   int K, N;
   float* C;               // [M, N] fp32
 };

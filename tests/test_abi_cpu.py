@@ -74,10 +74,12 @@ def test_other_entry_points_reject_invalid_arguments():
     assert lib.spec_verify_tree(FAKE, 1, FAKE, FAKE, 0, 1, 5000, 10, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert lib.spec_verify_tree(FAKE + 8, 1, FAKE, FAKE, 0, 1, 7, 10, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 3
     # lm head: d must be a positive multiple of 64
-    assert lib.lmhead_project(FAKE, 4, 100, FAKE, 10, FAKE, None) == 1
-    assert lib.lmhead_project(FAKE, 4, 128, FAKE + 2, 10, FAKE, None) == 3
-    assert lib.lmhead_verify(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, 96, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
-    assert lib.lmhead_verify(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, 128, 50, 0.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.lmhead_project(FAKE, 4, 100, FAKE, 0, 10, FAKE, None) == 1
+    assert lib.lmhead_project(FAKE, 4, 128, FAKE + 2, 0, 10, FAKE, None) == 3
+    assert lib.lmhead_project(FAKE, 4, 128, FAKE, 2, 10, FAKE, None) == 1   # unknown weight layout
+    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 2, 3, 96, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 3, 128, 50, 0.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 7, FAKE, FAKE, 2, 3, 128, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
     # row stats: want out of range, missing sum output
     assert lib.spec_row_stats(FAKE, 1, 4, 10, 1.0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert lib.spec_row_stats(FAKE, 1, 4, 10, 1.0, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1

@@ -352,13 +352,20 @@ def test_deterministic_and_workspace_shared_across_layouts(c3):
 
 
 # ---------------------------------------------------------------- LM head
-def test_lmhead_project_small_shapes_exact_on_integers():
+@pytest.mark.parametrize("layout", ["dv", "vd"])
+def test_lmhead_project_small_shapes_exact_on_integers(layout):
+    # integer operands: every partial sum is exact in fp32, so the GPU result
+    # must equal the integer product; shapes span several tiles, ragged M and
+    # V tails, V % 8 != 0 (element-load path of the [d, V] layout), and K
+    # with fewer steps than the load ring
     rng = np.random.default_rng(2)
-    for M, d, V in ((3, 64, 997), (130, 128, 1000), (1, 256, 8), (257, 64, 129)):
+    for M, d, V in ((3, 64, 997), (130, 128, 1000), (1, 256, 8), (257, 64, 129), (300, 192, 513)):
         H = rng.integers(-4, 5, (M, d)).astype(np.float32)
         W = rng.integers(-4, 5, (d, V)).astype(np.float32)
-        Z = L.lmhead_project(to_dev(f32_to_bf16_bits(H)), to_dev(f32_to_bf16_bits(W))).cpu().numpy()
-        assert np.array_equal(Z, (H.astype(np.int64) @ W.astype(np.int64)).astype(np.float32))
+        Wl = W if layout == "dv" else np.ascontiguousarray(W.T)
+        Z = L.lmhead_project(to_dev(f32_to_bf16_bits(H)), to_dev(f32_to_bf16_bits(Wl)),
+                             layout=L.W_DV if layout == "dv" else L.W_VD).cpu().numpy()
+        assert np.array_equal(Z, (H.astype(np.int64) @ W.astype(np.int64)).astype(np.float32)), (M, d, V)
 
 
 @pytest.fixture(scope="module")
@@ -377,6 +384,13 @@ def test_eagle_lmhead_logits_and_verify(c5):
     # the projection inside lmhead_verify is the standalone projection
     proj = L.lmhead_project(ft, W)
     assert torch.equal(proj.view(B, g + 1, V), zt_gpu)
+    # the [V, d] weight layout gives bit-identical logits and verdicts: the
+    # MFMA operands hold the same values in the same k order
+    Wvd = W.t().contiguous()
+    assert torch.equal(L.lmhead_project(ft, Wvd, layout=L.W_VD), proj)
+    acc2, out2 = L.lmhead_verify(ft, fd, Wvd, x, u, float(w["temperature"]), ws=ws.clone(), layout=L.W_VD)
+    assert torch.equal(acc2, acc) and torch.equal(out2, out)
+    del Wvd
     seqs = list(range(0, B, 4))
     rows_t = np.array([b * (g + 1) + i for b in seqs for i in range(g + 1)])
     rows_d = np.array([b * g + i for b in seqs for i in range(g)])
