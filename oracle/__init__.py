@@ -33,3 +33,4 @@ from .verify import (  # noqa: F401
     lmhead_logits,
     lmhead_verify,
 )
+from .kv import kv_compact  # noqa: F401
