@@ -204,6 +204,29 @@ def main():
                                      "mean_accept_len": round(tout[0].float().mean().item(), 3)}
         del tt, tt2
         torch.cuda.empty_cache()
+        # KV compaction to the paths the tree verifier accepted: a cache of
+        # 32 layers x (K, V) planes of 8 heads x 128 bf16 per entry
+        kB, kP, kE = tw["B"], 64, 8 * 128 * 2
+        kS = 512 + tw["N"]
+        kv = torch.zeros((kB, kP, kS, kE), dtype=torch.uint8, device=dev)
+        kpre = torch.from_numpy(np.random.default_rng(0).integers(0, 513, kB).astype(np.int32)).to(dev)
+        kacc, kpath = tout[0].clone(), tout[1].clone()
+        knew = torch.empty(kB, dtype=torch.int32, device=dev)
+
+        def kstep(i):
+            L.kv_compact(kv, kpre, kacc, kpath, new_len=knew)
+
+        for i in range(args.warmup):
+            kstep(i)
+        kms = time_events(kstep, args.steps, stream)
+        acc_h, path_h = kacc.cpu().numpy(), kpath.cpu().numpy()
+        moved = sum(int(np.sum(path_h[b, :acc_h[b]] != np.arange(1, acc_h[b] + 1))) for b in range(kB))
+        kbytes = 2 * moved * kP * kE
+        modes["kv_compact_b32n63_l32h8d128"] = {
+            "ms": round(kms, 5), "entries_moved": moved * kP, "bytes_moved": kbytes,
+            "GBs": round(kbytes / (kms * 1e-3) / 1e9, 1), "frac": round(kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del kv
+        torch.cuda.empty_cache()
         # EAGLE-style LM head
         ew = make_workload("eagle_lmhead", cache=True)
         eB, eg, ed, eV = ew["B"], ew["gamma"], ew["d"], ew["V"]

@@ -252,6 +252,39 @@ spec_status spec_probe_probs(const void* target_logits, const void* draft_logits
                              double* out_p, double* out_q, double* out_resid,
                              void* ws, size_t ws_bytes, hipStream_t s);
 
+/*
+ * spec_kv_compact -- keep only the accepted path's KV-cache entries.
+ * Pages: "EAGLE-3 speculative decoding review", "The Complete EAGLE-3
+ * Inference Process" (5. Update the KV Cache: keep the accepted path's
+ * cache, discard rejected branches, resume drafting from the committed
+ * prefix) and "Implementation Is More Complex Than a Simple Two-Model Setup"
+ * (prune the KV cache to the accepted branch).
+ *
+ * kv: the cache, modified in place.  Entry (sequence b, plane p, slot s) is
+ *     entry_bytes contiguous bytes at kv + b*seq_stride + p*plane_stride +
+ *     s*entry_bytes (a plane is one layer's keys or values; slots of a plane
+ *     are contiguous).  The B x planes blocks of S entries must not overlap:
+ *     planes inside sequences ([B][planes][S]) or sequences inside planes
+ *     ([planes][B][S]), padding allowed.
+ * prefix_len [B]: L_b, entries cached before the verification forward; that
+ *     forward wrote tree node n (node 0 = the last committed token) at slot
+ *     L_b + n.
+ * path [B, path_stride]: accepted nodes in depth order, as spec_verify_tree
+ *     writes them (out_path, path_stride = N); NULL for linear drafts, whose
+ *     accepted tokens already sit in place.
+ * accept_len [B]: d_b from the verify call.
+ * new_len [B] out: L_b + 1 + d_b, or -1 (nothing moved) when d_b < 0 or the
+ *     path does not rise strictly from 1 or leaves the cache.
+ * Effect: slot L_b + t receives the pre-call entry of slot L_b + path[t-1]
+ * for t = 1..d_b, in every plane; all other slots are untouched.
+ * kv, strides and entry_bytes 16-byte aligned (entry_bytes >= 16); the int
+ * arrays 4-byte aligned.  No workspace.
+ */
+spec_status spec_kv_compact(void* kv, int B, int planes, int S, long long entry_bytes,
+                            long long seq_stride, long long plane_stride,
+                            const int32_t* prefix_len, const int32_t* path, int path_stride,
+                            const int32_t* accept_len, int32_t* new_len, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     SpecError,
     W_DV,
     W_VD,
+    kv_compact,
     lib,
     lmhead_logits_view,
     lmhead_project,

@@ -27,7 +27,7 @@ W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (fea
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
 
-_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vp, _i, _f, _sz, _ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_longlong
 _SIGS = {
     "spec_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "spec_workspace_init": (_i, [_vp, _sz, _vp]),
@@ -38,6 +38,7 @@ _SIGS = {
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
     "spec_probe_probs": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGS)
@@ -200,6 +201,26 @@ def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=Non
                              float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
            "lmhead_verify")
     return out
+
+
+def kv_compact(kv, prefix_len, accept_len, path=None, new_len=None):
+    """In-place KV compaction.  kv: tensor [B, planes, S, E] (any dtype) whose
+    last two dims are contiguous (an entry = E elements; other dims may be
+    permuted views, e.g. a [planes, B, S, E] cache passed as .transpose(0, 1)).
+    path: int32 [B, path_stride] accepted nodes (spec_verify_tree's out_path)
+    or None for linear drafts.  Returns new_len int32 [B]."""
+    B, P, S, E = kv.shape
+    es = kv.element_size()
+    if kv.stride(3) != 1 or kv.stride(2) != E:
+        raise ValueError("kv: each plane's slots must be contiguous entries")
+    dev = kv.device
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    pstride = path.shape[1] if path is not None else 0
+    _check(lib.spec_kv_compact(_ptr(kv), B, P, S, E * es, kv.stride(0) * es, kv.stride(1) * es, _ptr(prefix_len),
+                               _ptr(path) if path is not None else None, pstride, _ptr(accept_len), _ptr(new_len),
+                               _stream(dev)), "spec_kv_compact")
+    return new_len
 
 
 def lmhead_logits_view(ws, B, g, V, d):

@@ -422,4 +422,39 @@ spec_status spec_probe_probs(const void* target_logits, const void* draft_logits
   return hip_status(launch_probe(p, (int)dt, s));
 }
 
+spec_status spec_kv_compact(void* kv, int B, int planes, int S, long long entry_bytes, long long seq_stride,
+                            long long plane_stride, const int32_t* prefix_len, const int32_t* path,
+                            int path_stride, const int32_t* accept_len, int32_t* new_len, hipStream_t s) {
+  if (B < 1 || B > SPEC_MAX_BATCH || planes < 1 || S < 1 || entry_bytes < 16 || entry_bytes > (1LL << 30))
+    return SPEC_EINVAL;
+  if (seq_stride < 0 || plane_stride < 0 || (path && path_stride < 1)) return SPEC_EINVAL;
+  if (!kv || !prefix_len || !accept_len || !new_len) return SPEC_EINVAL;
+  // distinct (sequence, plane) blocks of S entries must not overlap: either
+  // planes nest inside sequences or sequences inside planes
+  const long long blk = (long long)S * entry_bytes;
+  if (blk > (1LL << 46)) return SPEC_EINVAL;
+  const bool seq_outer = (planes == 1 || plane_stride >= blk) &&
+                         (B == 1 || seq_stride >= (long long)(planes - 1) * plane_stride + blk);
+  const bool plane_outer = (B == 1 || seq_stride >= blk) &&
+                           (planes == 1 || plane_stride >= (long long)(B - 1) * seq_stride + blk);
+  if (!seq_outer && !plane_outer) return SPEC_EINVAL;
+  if (entry_bytes % 16 || seq_stride % 16 || plane_stride % 16 || !aligned(kv, 16) || !aligned(prefix_len, 4) ||
+      (path && !aligned(path, 4)) || !aligned(accept_len, 4) || !aligned(new_len, 4))
+    return SPEC_EALIGN;
+  KvParams p;
+  p.kv = static_cast<char*>(kv);
+  p.B = B;
+  p.planes = planes;
+  p.S = S;
+  p.entry_bytes = entry_bytes;
+  p.seq_stride = seq_stride;
+  p.plane_stride = plane_stride;
+  p.prefix_len = prefix_len;
+  p.path = path;
+  p.path_stride = path ? path_stride : 0;
+  p.accept_len = accept_len;
+  p.new_len = new_len;
+  return hip_status(launch_kv_compact(p, s));
+}
+
 }  // extern "C"

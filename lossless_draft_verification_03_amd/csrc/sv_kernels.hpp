@@ -121,4 +121,17 @@ struct LmHeadParams {
 };
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s);
 
+// ---------------------------------------------------------- KV compaction
+struct KvParams {
+  char* kv;                  // entry (b, p, s): entry_bytes at kv + b*seq_stride + p*plane_stride + s*entry_bytes
+  int B, planes, S;
+  long long entry_bytes, seq_stride, plane_stride;
+  const int32_t* prefix_len; // [B]
+  const int32_t* path;       // [B, path_stride] or null (linear drafts: nothing moves)
+  int path_stride;
+  const int32_t* accept_len; // [B]
+  int32_t* new_len;          // [B] out
+};
+hipError_t launch_kv_compact(const KvParams& p, hipStream_t s);
+
 }  // namespace sv

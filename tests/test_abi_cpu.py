@@ -21,7 +21,7 @@ def _header_functions():
 def test_library_exports_every_declared_symbol():
     declared = _header_functions()
     assert {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "lmhead_verify",
-            "lmhead_project", "spec_row_stats", "spec_probe_probs"} <= declared
+            "lmhead_project", "spec_row_stats", "spec_probe_probs", "spec_kv_compact"} <= declared
     assert declared == set(L.EXPORTS)
     raw = ctypes.CDLL(L.LIB_PATH)
     for name in declared:
@@ -101,3 +101,26 @@ def test_binding_has_no_fallback(monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_kv_compact_rejects_invalid_arguments():
+    f = L.lib.spec_kv_compact
+    E = 64
+    blk = 10 * E  # S = 10 slots of E bytes
+    good = dict(kv=FAKE, B=2, planes=3, S=10, E=E, ss=3 * blk, ps=blk, L=FAKE, path=FAKE, pst=5, d=FAKE, nl=FAKE)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["kv"], a["B"], a["planes"], a["S"], a["E"], a["ss"], a["ps"], a["L"], a["path"], a["pst"],
+                 a["d"], a["nl"], None)
+    assert call(B=0) == 1 and call(planes=0) == 1 and call(S=0) == 1
+    assert call(E=8) == 1                                   # an entry is at least 16 bytes
+    assert call(E=24, ss=3 * 240, ps=240) == 3              # ... and a multiple of 16
+    assert call(pst=0) == 1                                 # a path needs its row length
+    assert call(kv=None) == 1 and call(nl=None) == 1
+    assert call(ps=blk - 16) == 1                           # planes of one sequence overlap
+    assert call(ss=2 * blk) == 1                            # sequences overlap
+    assert call(kv=FAKE + 8) == 3 and call(ss=3 * blk + 8) == 3
+    # sequences inside planes is a valid layout too (no launch without a GPU:
+    # only the argument checks are exercised, so stop at a misaligned pointer)
+    assert call(ss=blk, ps=2 * blk, L=FAKE + 2) == 3
