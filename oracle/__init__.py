@@ -34,3 +34,4 @@ from .verify import (  # noqa: F401
     lmhead_verify,
 )
 from .kv import kv_compact  # noqa: F401
+from .tree_build import build_dynamic_tree, build_tree, expand_step, new_table  # noqa: F401
