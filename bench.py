@@ -227,6 +227,51 @@ def main():
             "GBs": round(kbytes / (kms * 1e-3) / 1e9, 1), "frac": round(kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del kv
         torch.cuda.empty_cache()
+        # EAGLE-2 tree: one expansion depth (32 sequences x 8 frontier rows,
+        # top-8 children each, next frontier 8) over bf16 draft rows, then
+        # re-ranking a 6-depth table to 63 drafted nodes
+        xB, xK, xk = 32, 8, 8
+        gen_t = torch.Generator(device=dev).manual_seed(0)
+        xrep = [(torch.randn((xB, xK, V), device=dev, generator=gen_t) * 2.0).to(torch.bfloat16) for _ in range(4)]
+        xcap = 1 + xk + 5 * xK * xk
+        xtable = L.new_tree_table(xB, xcap, torch.zeros(xB, dtype=torch.int32), device=dev)
+        # a depth-1 frontier of 8 nodes under the root
+        xtable[0][:, 1:1 + xK] = 0
+        xtable[1][:, 1:1 + xK] = torch.arange(xK, dtype=torch.int32, device=dev)
+        xtable[2][:, 1:1 + xK] = -0.25 * torch.arange(1, xK + 1, dtype=torch.float64, device=dev)
+        xtable[3][:, 1:1 + xK] = 1
+        xfront = torch.arange(1, xK + 1, dtype=torch.int32, device=dev).repeat(xB, 1)
+        xws = L.new_workspace(L.MODE_TREE_EXPAND, xB, xK, V, device=dev)
+        xnext = torch.empty((xB, xK), dtype=torch.int32, device=dev)
+
+        def xstep(i):
+            L.tree_expand(xrep[i % 4], xfront, xtable, 1 + xK, 1.0, xk, xK, ws=xws, next_frontier=xnext)
+
+        for i in range(args.warmup):
+            xstep(i)
+        xms = time_events(xstep, args.steps, stream)
+        xbytes = xB * xK * V * 2
+        # fill the remaining depths so the build has a full table
+        off = 1 + xK + xK * xk
+        fr = xnext.clone()
+        for dpt in range(4):
+            L.tree_expand(xrep[dpt % 4], fr, xtable, off, 1.0, xk, xK, ws=xws, next_frontier=xnext)
+            off += xK * xk
+            fr = xnext.clone()
+        bout = L.tree_build(xtable, off, 63)
+
+        def bstep(i):
+            L.tree_build(xtable, off, 63, out=bout)
+
+        for i in range(args.warmup):
+            bstep(i)
+        bms = time_events(bstep, args.steps, stream)
+        modes["tree_expand_b32k8v128k"] = {
+            "ms": round(xms, 5), "rows_per_s": round(xB * xK / (xms * 1e-3), 1),
+            "GBs": round(xbytes / (xms * 1e-3) / 1e9, 1), "frac": round(xbytes / (xms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "build_ms_63_of_%d" % off: round(bms, 5)}
+        del xrep
+        torch.cuda.empty_cache()
         # EAGLE-style LM head
         ew = make_workload("eagle_lmhead", cache=True)
         eB, eg, ed, eV = ew["B"], ew["gamma"], ew["d"], ew["V"]

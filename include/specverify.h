@@ -84,7 +84,8 @@ typedef enum {
   SPEC_MODE_GREEDY = 1,   /* spec_verify_greedy: gamma_or_N = gamma        */
   SPEC_MODE_TREE = 2,     /* spec_verify_tree:   gamma_or_N = N (nodes)    */
   SPEC_MODE_LMHEAD = 3,   /* lmhead_verify:      gamma_or_N = gamma, d     */
-  SPEC_MODE_ROWSTATS = 4  /* spec_row_stats / spec_probe_probs: B = rows   */
+  SPEC_MODE_ROWSTATS = 4, /* spec_row_stats / spec_probe_probs: B = rows   */
+  SPEC_MODE_TREE_EXPAND = 5 /* spec_tree_expand:  gamma_or_N = K_in        */
 } spec_mode;
 
 /* Limits checked by every entry point. */
@@ -92,6 +93,9 @@ typedef enum {
 #define SPEC_MAX_TREE_NODES 4096
 #define SPEC_MAX_BATCH (1 << 20)
 #define SPEC_MAX_SAMPLE_VOCAB (1 << 25)   /* V limit of the sampling calls */
+#define SPEC_MAX_TOPK 16          /* children per expanded draft-tree node    */
+#define SPEC_MAX_FRONTIER 64      /* frontier slots per expansion depth       */
+#define SPEC_MAX_BUILD_NODES 2048 /* node-table entries and tree size (build) */
 
 /* Bytes of workspace the call of the given mode needs for these sizes
  * (0 when an argument is out of range).  d is used by SPEC_MODE_LMHEAD only.
@@ -284,6 +288,71 @@ spec_status spec_kv_compact(void* kv, int B, int planes, int S, long long entry_
                             long long seq_stride, long long plane_stride,
                             const int32_t* prefix_len, const int32_t* path, int path_stride,
                             const int32_t* accept_len, int32_t* new_len, hipStream_t s);
+
+/*
+ * spec_tree_expand -- one depth of the EAGLE-2 dynamic draft tree.
+ * Pages: "EAGLE math", "EAGLE-2: dynamic draft trees" (grow the tree by
+ * expanding the nodes with the highest cumulative draft probability, prune,
+ * re-rank); "EAGLE-3 speculative decoding review", "EAGLE-2: Does Every
+ * Context Need the Same Draft Tree?" and "The Complete EAGLE-3 Inference
+ * Process" (2. Generate a Draft Tree).
+ *
+ * Node table, per sequence b (row b of each [B, cap] array): parent (table
+ * index, -1 for the root), token, score (float64 cumulative draft
+ * log-probability, the root 0), depth (root 0).  The caller writes the root
+ * at index 0 (parent -1, its token, score 0, depth 0) before the first call.
+ * draft_logits [B, K_in, V]: the draft rows of the frontier nodes.
+ * frontier [B, K_in]: their table indices; -1 (or an index >= off) marks an
+ *     empty slot.  The first depth expands the root: K_in = 1, frontier 0.
+ * For every frontier node: q = softmax(z / T); its k tokens with the largest
+ * q (equal logits: lower index first) become children at table positions
+ * off + f*k + r (slot f, rank r), score = parent score + log q(token),
+ * depth = parent depth + 1.  Empty slots get placeholders (parent -1, token
+ * -1, score -inf, depth -1).
+ * next_frontier [B, K_out] out: the K_out children with the highest score
+ *     (equal scores: lower table position first), -1 padded.  The next call
+ *     takes it as its frontier with off += K_in * k.
+ * 1 <= k <= SPEC_MAX_TOPK, K_in, K_out <= SPEC_MAX_FRONTIER, K_in * k <= 1024,
+ * V >= k, off >= 1, off + K_in * k <= cap.  Every row of a non-empty slot
+ * needs a finite logit.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_TREE_EXPAND, B, K_in, V, 0).
+ */
+spec_status spec_tree_expand(const void* draft_logits, spec_dtype dt, const int32_t* frontier,
+                             int B, int K_in, int V, float temperature, int k, int K_out,
+                             int32_t* node_parent, int32_t* node_token, double* node_score,
+                             int32_t* node_depth, int cap, int off, int32_t* next_frontier,
+                             void* ws, size_t ws_bytes, hipStream_t s);
+
+/*
+ * spec_tree_build -- re-rank the drafted nodes and lay out the tree with its
+ * attention mask.
+ * Pages: "EAGLE math", "EAGLE-2: dynamic draft trees" (re-rank which
+ * candidates to keep; the verified node count stays fixed; a tree attention
+ * mask scores every candidate in one pass); "EAGLE-3 speculative decoding
+ * review", "EAGLE-2: Does Every Context Need the Same Draft Tree?" (a node
+ * sees the shared prefix and its own ancestors only).
+ *
+ * Reads table entries 0 .. n_nodes-1 (the table spec_tree_expand fills).
+ * Keeps the root and the M drafted nodes with the highest score (equal
+ * scores: shallower first, then lower table index); a child never outscores
+ * its parent, so the kept set is a tree.  Output node order: depth, then
+ * score (higher first), then table index; parent[i] < i.
+ * out_n [B]: 1 + min(M, drafted nodes), or -1 if the table breaks the
+ *     expansion's invariants (root not at 0, a parent after its child, depth
+ *     not parent depth + 1, a kept node whose parent is not kept).
+ * out_parent, out_token, out_depth, out_index (table index) [B, M+1]: -1
+ *     padded past out_n.
+ * out_mask [B, M+1, W], W = ceil((M+1)/32) uint32 words: bit j of row i set
+ *     iff node j is node i or one of its ancestors (what node i may attend to
+ *     besides the committed prefix); zero rows past out_n.
+ * n_nodes <= cap, n_nodes <= SPEC_MAX_BUILD_NODES, M + 1 <= SPEC_MAX_BUILD_NODES.
+ * The outputs feed spec_verify_tree (parent and tokens).
+ */
+spec_status spec_tree_build(const int32_t* node_parent, const int32_t* node_token,
+                            const double* node_score, const int32_t* node_depth, int B, int cap,
+                            int n_nodes, int M, int32_t* out_n, int32_t* out_parent,
+                            int32_t* out_token, int32_t* out_depth, int32_t* out_index,
+                            uint32_t* out_mask, hipStream_t s);
 
 #ifdef __cplusplus
 }

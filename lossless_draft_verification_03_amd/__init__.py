@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     MODE_ROWSTATS,
     MODE_SAMPLE,
     MODE_TREE,
+    MODE_TREE_EXPAND,
     SPEC_BF16,
     SPEC_F32,
     SpecError,
@@ -24,9 +25,12 @@ from ._binding import (  # noqa: F401
     lmhead_logits_view,
     lmhead_project,
     lmhead_verify,
+    new_tree_table,
     new_workspace,
     probe_probs,
     row_stats,
+    tree_build,
+    tree_expand,
     verify_greedy,
     verify_sample,
     verify_tree,

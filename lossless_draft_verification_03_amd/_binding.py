@@ -22,7 +22,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_EHIP = range(6)
 SPEC_F32, SPEC_BF16 = 0, 1
-MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS = range(5)
+MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS, MODE_TREE_EXPAND = range(6)
 W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (feature innermost)
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
@@ -39,6 +39,9 @@ _SIGS = {
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
+    "spec_tree_expand": (_i, [_vp, _i, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
+                              _vp]),
+    "spec_tree_build": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_probe_probs": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGS)
@@ -221,6 +224,55 @@ def kv_compact(kv, prefix_len, accept_len, path=None, new_len=None):
                                _ptr(path) if path is not None else None, pstride, _ptr(accept_len), _ptr(new_len),
                                _stream(dev)), "spec_kv_compact")
     return new_len
+
+
+def new_tree_table(B, cap, root_tokens, device="cuda"):
+    """A node table for spec_tree_expand: (parent, token, score, depth), each
+    [B, cap], with the root at index 0."""
+    parent = torch.full((B, cap), -1, dtype=torch.int32, device=device)
+    token = torch.full((B, cap), -1, dtype=torch.int32, device=device)
+    score = torch.full((B, cap), float("-inf"), dtype=torch.float64, device=device)
+    depth = torch.full((B, cap), -1, dtype=torch.int32, device=device)
+    token[:, 0] = root_tokens.to(device=device, dtype=torch.int32)
+    score[:, 0] = 0.0
+    depth[:, 0] = 0
+    return parent, token, score, depth
+
+
+def tree_expand(draft_logits, frontier, table, off, temperature, k, K_out, ws=None, next_frontier=None):
+    """One expansion depth.  draft_logits [B, K_in, V]; frontier int32
+    [B, K_in]; table from new_tree_table (updated in place).  Returns the next
+    frontier int32 [B, K_out]."""
+    B, K_in, V = draft_logits.shape
+    parent, token, score, depth = table
+    cap = parent.shape[1]
+    dev = draft_logits.device
+    if next_frontier is None:
+        next_frontier = torch.empty((B, K_out), dtype=torch.int32, device=dev)
+    w = _workspace(MODE_TREE_EXPAND, B, K_in, V, 0, dev, ws)
+    _check(lib.spec_tree_expand(_ptr(draft_logits), dtype_code(draft_logits), _ptr(frontier), B, K_in, V,
+                                float(temperature), k, K_out, _ptr(parent), _ptr(token), _ptr(score), _ptr(depth),
+                                cap, off, _ptr(next_frontier), _ptr(w), w.numel(), _stream(dev)),
+           "spec_tree_expand")
+    return next_frontier
+
+
+def tree_build(table, n_nodes, M, out=None):
+    """Re-rank and lay out the tree.  Returns (n [B], parent, token, depth,
+    table_index [B, M+1] int32, mask [B, M+1, ceil((M+1)/32)] int32 bit rows)."""
+    parent, token, score, depth = table
+    B, cap = parent.shape
+    dev = parent.device
+    W = (M + 1 + 31) // 32
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),) + tuple(
+            torch.empty((B, M + 1), dtype=torch.int32, device=dev) for _ in range(4)) + (
+            torch.empty((B, M + 1, W), dtype=torch.int32, device=dev),)
+    n, opar, otok, odep, oidx, omask = out
+    _check(lib.spec_tree_build(_ptr(parent), _ptr(token), _ptr(score), _ptr(depth), B, cap, n_nodes, M, _ptr(n),
+                               _ptr(opar), _ptr(otok), _ptr(odep), _ptr(oidx), _ptr(omask), _stream(dev)),
+           "spec_tree_build")
+    return out
 
 
 def lmhead_logits_view(ws, B, g, V, d):

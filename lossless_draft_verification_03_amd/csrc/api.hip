@@ -186,6 +186,12 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
 extern "C" {
 
 size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d) {
+  if (mode == SPEC_MODE_TREE_EXPAND) {
+    if (B < 1 || B > SPEC_MAX_BATCH || gamma_or_N < 1 || gamma_or_N > kFrontierMax || V < 1) return 0;
+    int seg;
+    const long long n = (long long)B * gamma_or_N * tree_expand_segments(V, &seg) * (long long)sizeof(TopkPart);
+    return (size_t)((n + kAlign - 1) / kAlign * kAlign);
+  }
   Layout L;
   if (!make_layout(mode, B, gamma_or_N, V, d, DT_F32, &L)) return 0;
   return L.total;
@@ -455,6 +461,79 @@ spec_status spec_kv_compact(void* kv, int B, int planes, int S, long long entry_
   p.accept_len = accept_len;
   p.new_len = new_len;
   return hip_status(launch_kv_compact(p, s));
+}
+
+spec_status spec_tree_expand(const void* draft_logits, spec_dtype dt, const int32_t* frontier, int B, int K_in,
+                             int V, float temperature, int k, int K_out, int32_t* node_parent,
+                             int32_t* node_token, double* node_score, int32_t* node_depth, int cap, int off,
+                             int32_t* next_frontier, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || K_in < 1 || K_in > kFrontierMax || K_out < 1 || K_out > kFrontierMax ||
+      k < 1 || k > kTopkMax || K_in * k > kCandMax || V < k || !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (off < 1 || cap < 1 || (long long)off + (long long)K_in * k > cap) return SPEC_EINVAL;
+  if (!draft_logits || !frontier || !node_parent || !node_token || !node_score || !node_depth || !next_frontier)
+    return SPEC_EINVAL;
+  TempConst tc;
+  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
+  if (!aligned(draft_logits, 16) || !aligned(frontier, 4) || !aligned(node_parent, 4) || !aligned(node_token, 4) ||
+      !aligned(node_score, 8) || !aligned(node_depth, 4) || !aligned(next_frontier, 4))
+    return SPEC_EALIGN;
+  const size_t need = spec_workspace_bytes(SPEC_MODE_TREE_EXPAND, B, K_in, V, 0);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return SPEC_EWORKSPACE;
+  TreeExpandParams p;
+  p.logits = draft_logits;
+  p.dt = dt == SPEC_BF16 ? DT_BF16 : DT_F32;
+  p.frontier = frontier;
+  p.B = B;
+  p.K_in = K_in;
+  p.V = V;
+  p.tc = tc;
+  p.k = k;
+  p.K_out = K_out;
+  p.parent = node_parent;
+  p.token = node_token;
+  p.score = node_score;
+  p.depth = node_depth;
+  p.cap = cap;
+  p.off = off;
+  p.next_frontier = next_frontier;
+  p.part = static_cast<TopkPart*>(ws);
+  p.nseg = tree_expand_segments(V, &p.seg_elems);
+  return hip_status(launch_tree_expand(p, s));
+}
+
+spec_status spec_tree_build(const int32_t* node_parent, const int32_t* node_token, const double* node_score,
+                            const int32_t* node_depth, int B, int cap, int n_nodes, int M, int32_t* out_n,
+                            int32_t* out_parent, int32_t* out_token, int32_t* out_depth, int32_t* out_index,
+                            uint32_t* out_mask, hipStream_t s) {
+  if (B < 1 || B > SPEC_MAX_BATCH || n_nodes < 1 || n_nodes > cap || n_nodes > kBuildMaxNodes || M < 0 ||
+      M + 1 > kBuildMaxNodes)
+    return SPEC_EINVAL;
+  if (!node_parent || !node_token || !node_score || !node_depth || !out_n || !out_parent || !out_token ||
+      !out_depth || !out_index || !out_mask)
+    return SPEC_EINVAL;
+  if (!aligned(node_parent, 4) || !aligned(node_token, 4) || !aligned(node_score, 8) || !aligned(node_depth, 4) ||
+      !aligned(out_n, 4) || !aligned(out_parent, 4) || !aligned(out_token, 4) || !aligned(out_depth, 4) ||
+      !aligned(out_index, 4) || !aligned(out_mask, 4))
+    return SPEC_EALIGN;
+  TreeBuildParams p;
+  p.parent = node_parent;
+  p.token = node_token;
+  p.score = node_score;
+  p.depth = node_depth;
+  p.B = B;
+  p.cap = cap;
+  p.n_nodes = n_nodes;
+  p.M = M;
+  p.out_n = out_n;
+  p.out_parent = out_parent;
+  p.out_token = out_token;
+  p.out_depth = out_depth;
+  p.out_index = out_index;
+  p.out_mask = out_mask;
+  p.W = (M + 1 + 31) / 32;
+  return hip_status(launch_tree_build(p, s));
 }
 
 }  // extern "C"

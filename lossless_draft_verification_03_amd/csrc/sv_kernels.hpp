@@ -134,4 +134,53 @@ struct KvParams {
 };
 hipError_t launch_kv_compact(const KvParams& p, hipStream_t s);
 
+// ---------------------------------------------------------- draft tree
+constexpr int kTopkMax = 16;        // children per expanded node
+constexpr int kFrontierMax = 64;    // frontier slots per depth
+constexpr int kCandMax = 1024;      // children per sequence and depth
+constexpr int kBuildMaxNodes = 2048;
+
+// One (frontier row, segment) of the expansion sweep.
+struct TopkPart {
+  float m;                 // segment max
+  float s;                 // sum of 2^((z - m) c) over the segment
+  float v[kTopkMax];       // the segment's largest logits, best first
+  int idx[kTopkMax];       // their token indices (INT_MAX: none)
+};
+
+struct TreeExpandParams {
+  const void* logits;      // [B, K_in, V]
+  int dt;
+  const int32_t* frontier; // [B, K_in] table index or -1
+  int B, K_in, V;
+  TempConst tc;
+  int k, K_out;
+  int32_t* parent;         // node table [B, cap]
+  int32_t* token;
+  double* score;
+  int32_t* depth;
+  int cap, off;
+  int32_t* next_frontier;  // [B, K_out]
+  TopkPart* part;          // [B * K_in, nseg]
+  int nseg, seg_elems;
+};
+int tree_expand_segments(int V, int* seg_elems);
+hipError_t launch_tree_expand(const TreeExpandParams& p, hipStream_t s);
+
+struct TreeBuildParams {
+  const int32_t* parent;   // node table [B, cap]
+  const int32_t* token;
+  const double* score;
+  const int32_t* depth;
+  int B, cap, n_nodes, M;
+  int32_t* out_n;          // [B]
+  int32_t* out_parent;     // [B, M + 1]
+  int32_t* out_token;
+  int32_t* out_depth;
+  int32_t* out_index;
+  uint32_t* out_mask;      // [B, M + 1, W]
+  int W;
+};
+hipError_t launch_tree_build(const TreeBuildParams& p, hipStream_t s);
+
 }  // namespace sv
