@@ -124,3 +124,35 @@ def test_kv_compact_rejects_invalid_arguments():
     # sequences inside planes is a valid layout too (no launch without a GPU:
     # only the argument checks are exercised, so stop at a misaligned pointer)
     assert call(ss=blk, ps=2 * blk, L=FAKE + 2) == 3
+
+
+def test_tree_entry_points_reject_invalid_arguments():
+    ex, bd = L.lib.spec_tree_expand, L.lib.spec_tree_build
+
+    def expand(**kw):
+        a = dict(logits=FAKE, dt=1, fr=FAKE, B=2, K_in=4, V=1000, T=1.0, k=4, K_out=4, par=FAKE, tok=FAKE,
+                 sc=FAKE, dep=FAKE, cap=40, off=1, nf=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return ex(a["logits"], a["dt"], a["fr"], a["B"], a["K_in"], a["V"], a["T"], a["k"], a["K_out"], a["par"],
+                  a["tok"], a["sc"], a["dep"], a["cap"], a["off"], a["nf"], a["ws"], a["wsb"], None)
+    assert expand(dt=5) == 2
+    assert expand(k=0) == 1 and expand(k=17) == 1                    # 1 <= k <= 16
+    assert expand(K_in=65) == 1 and expand(K_out=0) == 1
+    assert expand(V=3) == 1                                          # fewer tokens than k
+    assert expand(off=0) == 1 and expand(off=30) == 1                # off + K_in*k past cap
+    assert expand(T=0.0) == 1
+    assert expand(logits=FAKE + 8) == 3 and expand(sc=FAKE + 4) == 3
+    assert expand(wsb=16) == 4
+    assert L.workspace_bytes(L.MODE_TREE_EXPAND, 2, 4, 1000) > 0
+    assert L.workspace_bytes(L.MODE_TREE_EXPAND, 2, 65, 1000) == 0
+
+    def build(**kw):
+        a = dict(par=FAKE, tok=FAKE, sc=FAKE, dep=FAKE, B=2, cap=100, n=50, M=10, on=FAKE, op=FAKE, ot=FAKE,
+                 od=FAKE, oi=FAKE, om=FAKE)
+        a.update(kw)
+        return bd(a["par"], a["tok"], a["sc"], a["dep"], a["B"], a["cap"], a["n"], a["M"], a["on"], a["op"],
+                  a["ot"], a["od"], a["oi"], a["om"], None)
+    assert build(n=0) == 1 and build(n=101) == 1                     # 1 <= n_nodes <= cap
+    assert build(cap=4000, n=2049) == 1 and build(M=2048) == 1       # build limits
+    assert build(M=-1) == 1 and build(om=None) == 1
+    assert build(sc=FAKE + 4) == 3
