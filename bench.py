@@ -178,7 +178,67 @@ def main():
         modes["greedy_b64g7v128k"] = {"ms": round(gms, 5), "positions_per_s": round(B * g / (gms * 1e-3), 1),
                                       "GBs": round(gbytes / (gms * 1e-3) / 1e9, 1),
                                       "frac": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # early-exit verification on the same replicas, then on a batch with
+        # low acceptance (draft noise 3.0) against the full sweep
+        def ee_bytes(acc_h):
+            j = np.clip(acc_h, 0, g)
+            return int(((j + 1) + np.minimum(j + 1, g)).sum()) * V * 2
+
+        eout = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
+
+        def estep(i):
+            _, t, dr = reps[i % R]
+            L.verify_sample(t, dr, x, u, T, ws=ws, out=eout, early_exit=True)
+
+        for i in range(args.warmup):
+            estep(i)
+        ems = time_events(estep, args.steps, stream)
+        ee = {"ms": round(ems, 5), "positions_per_s": round(B * g / (ems * 1e-3), 1),
+              "rows_bytes_read": ee_bytes(eout[0].cpu().numpy()), "full_sweep_ms": round(ms, 5)}
         del reps
+        torch.cuda.empty_cache()
+        wl = make_workload("b64g7v128k", draft_noise=3.0, seed=5)
+        lo_base = torch.cat([d(wl["target"]).view(rows_t, V), d(wl["draft"]).view(rows_d, V)], 0)
+        lo = []
+        for _ in range(4):
+            buf = lo_base.clone()
+            lo.append((buf[:rows_t].view(B, g + 1, V), buf[rows_t:].view(B, g, V)))
+        del lo_base
+        lx, lu = d(wl["draft_tokens"]), d(wl["uniforms"])
+
+        def lstep(i, early):
+            L.verify_sample(lo[i % 4][0], lo[i % 4][1], lx, lu, T, ws=ws, out=eout, early_exit=early)
+
+        for i in range(args.warmup):
+            lstep(i, False)
+            lstep(i, True)
+        lfull = time_events(lambda i: lstep(i, False), args.steps, stream)
+        lee = time_events(lambda i: lstep(i, True), args.steps, stream)
+        ee["low_acceptance"] = {"draft_noise": 3.0, "mean_accept_len": round(eout[0].float().mean().item(), 3),
+                                "full_sweep_ms": round(lfull, 5), "early_exit_ms": round(lee, 5),
+                                "rows_bytes_read": ee_bytes(eout[0].cpu().numpy())}
+        del lo
+        torch.cuda.empty_cache()
+        # the same low-acceptance sequences tiled to 256 (4x the bytes per position)
+        B4 = 4 * B
+        t4 = np.concatenate([wl["target"]] * 4, 0)
+        d4 = np.concatenate([wl["draft"]] * 4, 0)
+        lo4 = [(d(t4), d(d4)) for _ in range(2)]
+        del t4, d4
+        x4, u4 = d(np.concatenate([wl["draft_tokens"]] * 4, 0)), d(np.concatenate([wl["uniforms"]] * 4, 0))
+        ws4 = L.new_workspace(L.MODE_SAMPLE, B4, g, V, device=dev)
+        out4 = (torch.empty(B4, dtype=torch.int32, device=dev), torch.empty((B4, g + 1), dtype=torch.int32, device=dev))
+
+        def l4(i, early):
+            L.verify_sample(lo4[i % 2][0], lo4[i % 2][1], x4, u4, T, ws=ws4, out=out4, early_exit=early)
+
+        for i in range(2):
+            l4(i, False)
+            l4(i, True)
+        ee["low_acceptance_b256"] = {"full_sweep_ms": round(time_events(lambda i: l4(i, False), 10, stream), 5),
+                                     "early_exit_ms": round(time_events(lambda i: l4(i, True), 10, stream), 5)}
+        modes["early_exit_b64g7v128k"] = ee
+        del lo4, ws4
         torch.cuda.empty_cache()
         # tree
         tw = make_workload("tree63", cache=True)

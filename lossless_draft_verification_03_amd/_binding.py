@@ -34,6 +34,7 @@ _SIGS = {
     "spec_status_str": (ctypes.c_char_p, [_i]),
     "spec_row_stats": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
@@ -124,8 +125,10 @@ def row_stats(logits, temperature=1.0, want=3, ws=None, out=None):
     return out
 
 
-def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, out=None):
-    """target [B, g+1, V], draft [B, g, V] -> (accept_len [B], out_tokens [B, g+1])."""
+def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, out=None, early_exit=False):
+    """target [B, g+1, V], draft [B, g, V] -> (accept_len [B], out_tokens [B, g+1]).
+    early_exit: sweep the rows in position order and skip those after a
+    sequence's first rejection (same results)."""
     B, g1, V = target.shape
     g = g1 - 1
     dev = target.device
@@ -135,9 +138,9 @@ def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, o
         out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g1), dtype=torch.int32, device=dev))
     acc, toks = out
     w = _workspace(MODE_SAMPLE, B, g, V, 0, dev, ws)
-    _check(lib.spec_verify_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens),
-                                  _ptr(uniforms), B, g, V, float(temperature), _ptr(acc), _ptr(toks),
-                                  _ptr(w), w.numel(), _stream(dev)), "spec_verify_sample")
+    fn = lib.spec_verify_sample_early_exit if early_exit else lib.spec_verify_sample
+    _check(fn(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens), _ptr(uniforms), B, g, V,
+              float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)), "spec_verify_sample")
     return out
 
 

@@ -139,10 +139,10 @@ hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long l
   return merge ? launch_row_stats(p, dt, s) : launch_row_sweep(p, dt, s);
 }
 
-spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* tokens,
-                      const float* unif, int B, int g, int V, const TempConst& tc,
-                      int32_t* accept_len, int32_t* out_tokens, void* ws, const Layout& L,
-                      hipStream_t s) {
+// Sweep parameters of the sampling path (target rows, then draft rows; the
+// drafted tokens' logits gathered on the way).
+RowStatsParams sample_sweep_params(const void* tgt, const void* drf, const int32_t* tokens, int B, int g, int V,
+                                   int dt, const TempConst& tc, void* ws, const Layout& L) {
   RowStatsParams r;
   memset(&r, 0, sizeof(r));
   const RowSweepShape sh = row_sweep_shape(V, dt);
@@ -159,16 +159,22 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
   r.gather_tokens = tokens;
   r.gather_g = g;
   r.gather_out = at<float>(ws, L.gath);
-  if (launch_row_sweep(r, dt, s) != hipSuccess) return SPEC_EHIP;
+  return r;
+}
+
+// Accept scan and final draw on the partials the sweep left in the workspace.
+spec_status draw_on(const void* tgt, const void* drf, int dt, const int32_t* tokens, const float* unif, int B,
+                    int g, int V, const TempConst& tc, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                    const Layout& L, hipStream_t s) {
   SampleParams p;
   memset(&p, 0, sizeof(p));
   p.tgt = tgt;
   p.drf = drf;
   p.tokens = tokens;
   p.unif = unif;
-  p.part = r.part;
-  p.nseg_rows = sh.nseg;
-  p.gathered = r.gather_out;
+  p.part = at<Partial>(ws, L.part);
+  p.nseg_rows = row_sweep_shape(V, dt).nseg;
+  p.gathered = at<float>(ws, L.gath);
   p.B = B;
   p.g = g;
   p.V = V;
@@ -179,6 +185,34 @@ spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* t
   p.accept_len = accept_len;
   p.out_tokens = out_tokens;
   return hip_status(launch_sample(p, dt, s));
+}
+
+spec_status sample_on(const void* tgt, const void* drf, int dt, const int32_t* tokens,
+                      const float* unif, int B, int g, int V, const TempConst& tc,
+                      int32_t* accept_len, int32_t* out_tokens, void* ws, const Layout& L,
+                      hipStream_t s) {
+  const RowStatsParams r = sample_sweep_params(tgt, drf, tokens, B, g, V, dt, tc, ws, L);
+  if (launch_row_sweep(r, dt, s) != hipSuccess) return SPEC_EHIP;
+  return draw_on(tgt, drf, dt, tokens, unif, B, g, V, tc, accept_len, out_tokens, ws, L, s);
+}
+
+// Common argument checks of the two sampling entry points.
+spec_status check_sample_args(const void* target_logits, const void* draft_logits, spec_dtype dt,
+                              const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                              float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                              size_t ws_bytes, TempConst* tc, Layout* L) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
+      !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len || !out_tokens)
+    return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || !aligned(draft_logits, 16) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  if (!temp_const(temperature, tc)) return SPEC_EINVAL;
+  if (!make_layout(SPEC_MODE_SAMPLE, B, gamma, V, 0, DT_F32, L)) return SPEC_EINVAL;
+  return check_ws(ws, ws_bytes, *L);
 }
 
 }  // namespace
@@ -251,23 +285,34 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
                                int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
                                void* ws, size_t ws_bytes, hipStream_t s) {
-  if (!dtype_ok(dt)) return SPEC_EDTYPE;
-  if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
-      !row_bytes_ok(V, dt))
-    return SPEC_EINVAL;
-  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len || !out_tokens)
-    return SPEC_EINVAL;
-  if (!aligned(target_logits, 16) || !aligned(draft_logits, 16) || !aligned(draft_tokens, 4) ||
-      !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4))
-    return SPEC_EALIGN;
   TempConst tc;
-  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
   Layout L;
-  if (!make_layout(SPEC_MODE_SAMPLE, B, gamma, V, 0, DT_F32, &L)) return SPEC_EINVAL;
-  const spec_status w = check_ws(ws, ws_bytes, L);
-  if (w != SPEC_OK) return w;
+  const spec_status st = check_sample_args(target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V,
+                                           temperature, accept_len, out_tokens, ws, ws_bytes, &tc, &L);
+  if (st != SPEC_OK) return st;
   return sample_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc,
                    accept_len, out_tokens, ws, L, s);
+}
+
+spec_status spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits, spec_dtype dt,
+                                          const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
+                                          int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
+                                          void* ws, size_t ws_bytes, hipStream_t s) {
+  TempConst tc;
+  Layout L;
+  const spec_status st = check_sample_args(target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V,
+                                           temperature, accept_len, out_tokens, ws, ws_bytes, &tc, &L);
+  if (st != SPEC_OK) return st;
+  RowStatsParams r = sample_sweep_params(target_logits, draft_logits, draft_tokens, B, gamma, V, (int)dt, tc, ws, L);
+  r.step_B = B;
+  r.step_unif = uniforms;
+  r.step_alive = at<int>(ws, L.rarg);  // [B, gamma+1]; the sampler leaves this region unused
+  for (int i = 0; i <= gamma; ++i) {
+    r.step = i;
+    if (launch_row_step(r, (int)dt, s) != hipSuccess) return SPEC_EHIP;
+  }
+  return draw_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc, accept_len,
+                 out_tokens, ws, L, s);
 }
 
 spec_status spec_verify_greedy(const void* target_logits, spec_dtype dt, const int32_t* draft_tokens,

@@ -41,19 +41,66 @@ namespace {
 #endif
 constexpr int kVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segment
 
-template <int DT, int WANT>
+// STEPNP > 0: one early-exit step (see launch_row_step); STEPNP is the lane
+// group the draw kernel merges a row's partials with, so the step's accept
+// test reproduces the draw's decision bit for bit.
+template <int DT, int WANT, int STEPNP = 0>
 __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   __shared__ float sh_m[kBlock / kWave];
   __shared__ double sh_s[kBlock / kWave];
   __shared__ int sh_a[kBlock / kWave];
+  __shared__ int sh_alive;
   const float NEG_INF = -__builtin_huge_valf();
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const long long unit = blockIdx.x;
-  const long long r = unit / P.nseg;
-  const int s = (int)(unit - r * P.nseg);
+  long long r;
+  int s;
+  if constexpr (STEPNP == 0) {
+    r = unit / P.nseg;
+    s = (int)(unit - r * P.nseg);
+  } else {
+    // unit -> (sequence b, target or draft row of position i, segment)
+    const int i = P.step, g = P.gather_g;
+    const int per = i < g ? 2 : 1;
+    const long long b = unit / (per * P.nseg);
+    const int rem = (int)(unit - b * per * P.nseg);
+    const int kind = rem / P.nseg;
+    s = rem - kind * P.nseg;
+    const long long ab = b * (g + 1);
+    r = kind == 0 ? ab + i : P.rows0 + b * g + i;
+    // Row i is needed only if positions 0 .. i-1 were all accepted: the
+    // previous step recorded whether 0 .. i-2 were, and position i-1 is
+    // tested here from its rows' partials and gathered logits.
+    if (wid == 0) {
+      int al = 1;
+      if (i > 0) {
+        al = P.step_alive[ab + i - 1];
+        const int x = P.gather_tokens[b * g + i - 1];
+        if (al && (x < 0 || x >= P.V)) al = 0;
+        if (al) {
+          float Mt, Md;
+          double St, Sd;
+          int a;
+          merge_partials<1, STEPNP>(P.part + (ab + i - 1) * P.nseg, P.nseg, P.tc, lane & (STEPNP - 1), &Mt, &St,
+                                    &a);
+          merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + i - 1) * P.nseg, P.nseg, P.tc, lane & (STEPNP - 1),
+                                    &Md, &Sd, &a);
+          al = sample_rejects(P.gather_out[ab + i - 1], P.gather_out[P.rows0 + b * g + i - 1], Mt, St, Md, Sd,
+                              P.step_unif[ab + i - 1], P.tc)
+                   ? 0
+                   : 1;
+        }
+      }
+      if (lane == 0) sh_alive = al;
+    }
+    __syncthreads();
+    const int alive = sh_alive;
+    if (kind == 0 && s == 0 && tid == 0) P.step_alive[ab + i] = alive;
+    if (!alive) return;
+  }
   const bool second = r >= P.rows0;
   const char* base = static_cast<const char*>(second ? P.src1 : P.src0);
   const long long rr = second ? r - P.rows0 : r;
@@ -236,6 +283,29 @@ hipError_t launch_sweep_t(const RowStatsParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int NP>
+hipError_t launch_step_np(const RowStatsParams& p, hipStream_t s) {
+  const int per = p.step < p.gather_g ? 2 : 1;
+  const long long grid = (long long)p.step_B * per * p.nseg;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_row_sweep<DT, 1, NP>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_step_t(const RowStatsParams& p, hipStream_t s) {
+  switch (merge_group(p.nseg)) {
+    case 1: return launch_step_np<DT, 1>(p, s);
+    case 2: return launch_step_np<DT, 2>(p, s);
+    case 4: return launch_step_np<DT, 4>(p, s);
+    case 8: return launch_step_np<DT, 8>(p, s);
+    case 16: return launch_step_np<DT, 16>(p, s);
+    case 32: return launch_step_np<DT, 32>(p, s);
+    default: return launch_step_np<DT, 64>(p, s);
+  }
+}
+
 template <int WANT>
 hipError_t launch_merge_t(const RowStatsParams& p, hipStream_t s) {
   const long long wpb = kBlock / kWave;
@@ -282,6 +352,12 @@ hipError_t launch_row_merge(const RowStatsParams& p, hipStream_t s) {
     case 3: return launch_merge_t<3>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+// One position of the early-exit sweep: target and draft row `step` of every
+// sequence still alive, with the partial and gather layout of the full sweep.
+hipError_t launch_row_step(const RowStatsParams& p, int dt, hipStream_t s) {
+  return dt == DT_BF16 ? launch_step_t<DT_BF16>(p, s) : launch_step_t<DT_F32>(p, s);
 }
 
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s) {

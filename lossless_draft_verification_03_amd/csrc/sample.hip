@@ -165,14 +165,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
       if (x < 0 || (long long)x >= V) {
         bad = true;
       } else {
-        const double Mt = sh_M[tid], Md = sh_M[g + 1 + tid];
-        const double et = ((double)zt - Mt) * P.tc.c64;
-        const double ed = ((double)zd - Md) * P.tc.c64;
-        double r;
-        if (!(et > -__builtin_huge_val())) r = 0.0;                          // p(x) = 0
-        else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();    // q(x) = 0 < p(x)
-        else r = exp2_f64(et - ed) * (sh_S[g + 1 + tid] / sh_S[tid]);
-        rej = !((double)u < r);
+        rej = sample_rejects(zt, zd, sh_M[tid], sh_S[tid], sh_M[g + 1 + tid], sh_S[g + 1 + tid], u, P.tc);
       }
     }
     const unsigned long long mb = __ballot(bad);

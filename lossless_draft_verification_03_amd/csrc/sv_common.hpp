@@ -290,6 +290,22 @@ __device__ __forceinline__ void merge_partials(const Partial* part, int nseg, co
 }
 
 // Lane-group width for merging nseg partials: the next power of two, at most 64.
+// The accept test of one drafted position rejects unless
+// u < p(x)/q(x) = 2^((z_t(x) - M_t) c - (z_d(x) - M_d) c) * S_d / S_t, the
+// ratio formed from one fp64 exponent; q(x) = 0 < p(x) accepts, p(x) = 0
+// rejects.  Shared by the draw and the early-exit sweep, so both take the
+// same decision from the same merged row statistics.
+__device__ __forceinline__ bool sample_rejects(float zt, float zd, float Mt, double St, float Md, double Sd,
+                                               float u, const TempConst& tc) {
+  const double et = ((double)zt - (double)Mt) * tc.c64;
+  const double ed = ((double)zd - (double)Md) * tc.c64;
+  double r;
+  if (!(et > -__builtin_huge_val())) r = 0.0;                          // p(x) = 0
+  else if (!(ed > -__builtin_huge_val())) r = __builtin_huge_val();    // q(x) = 0 < p(x)
+  else r = exp2_f64(et - ed) * (Sd / St);
+  return !((double)u < r);
+}
+
 inline int merge_group(int nseg) {
   int g = 1;
   while (g < nseg && g < 64) g <<= 1;

@@ -32,6 +32,13 @@ struct RowStatsParams {
   float* out_max; // [rows]
   double* out_sum;// [rows] (want & 1)
   int* out_arg;   // [rows] (want & 2)
+  // early-exit step (launch_row_step): position `step` of B sequences, target
+  // row (b, step) and draft row (b, step), swept only while every earlier
+  // position was accepted; alive[b][i] (i <= gamma) records that
+  int step;
+  int step_B;
+  const float* step_unif;  // [B, gamma+1]
+  int* step_alive;         // [B, gamma+1]
 };
 
 struct RowSweepShape {
@@ -43,6 +50,7 @@ RowSweepShape row_sweep_shape(int V, int dt);
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);
 // The sweep alone (partials only); its consumers merge partials inline.
 hipError_t launch_row_sweep(const RowStatsParams& p, int dt, hipStream_t s);
+hipError_t launch_row_step(const RowStatsParams& p, int dt, hipStream_t s);
 hipError_t launch_row_merge(const RowStatsParams& p, hipStream_t s);
 
 // ---------------------------------------------------------- sampling
