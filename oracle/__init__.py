@@ -35,3 +35,4 @@ from .verify import (  # noqa: F401
 )
 from .kv import kv_compact  # noqa: F401
 from .tree_build import build_dynamic_tree, build_tree, expand_step, new_table  # noqa: F401
+from .tree_sample import verify_tree_sample, verify_tree_sample_seq  # noqa: F401
