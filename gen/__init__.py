@@ -16,5 +16,6 @@ from .synth import (  # noqa: F401
     make_linear,
     make_lmhead,
     make_tree,
+    make_tree_sample,
     make_workload,
 )

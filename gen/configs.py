@@ -1,4 +1,4 @@
-"""The five synthetic workloads, by name.
+"""The synthetic workloads, by name.
 
 Each entry states the shapes and value distributions of one workload.  The
 second argument of every N(mu, s) is a standard deviation.  Where a recipe
@@ -29,6 +29,13 @@ CONFIGS = {
     "tree63": dict(kind="tree", B=32, N=63, V=128256, dtype="bf16",
                    logits="normal", target_std=2.0, match_prob=0.7,
                    tree="binary", seed=0),
+    # Stochastic tree verification: B=32, complete binary tree of 63 nodes,
+    # bf16 target rows [32,63,128256] ~ N(0,2), draft rows = target + N(0,0.8),
+    # T = 0.7 (the large linear workload's distributions); every node's token
+    # is drawn independently from its parent's draft row; uniforms [32,63].
+    "tree_sample63": dict(kind="tree_sample", B=32, N=63, V=128256, dtype="bf16",
+                          logits="normal", target_std=2.0, draft_noise=0.8,
+                          temperature=0.7, tree="binary", seed=0),
     # B=64, gamma=5, d=4096: target features bf16 [64*6,4096] ~ N(0,1);
     # LM head bf16 [4096,128256] ~ N(0,0.02); draft features = target
     # features (rows i<gamma) + N(0,0.3); T = 1.

@@ -131,6 +131,11 @@ def tree_parents(N, shape="binary", rng=None):
             par[i] = i - 1
         elif shape == "random":
             par[i] = rng.integers(0, i)
+        elif shape == "star":
+            par[i] = 0
+        elif shape == "wide":
+            # k = 4 children per node, breadth first
+            par[i] = (i - 1) // 4
         else:
             raise ValueError(shape)
     return par
@@ -163,6 +168,42 @@ def make_tree(cfg):
                 node_tokens=node_tokens, parent=parent)
 
 
+def make_tree_sample(cfg):
+    """Draft tree for sampling verification: target and draft rows [B,N,V]
+    (row n belongs to node n), node tokens [B,N], parent [N] (or [B,N] for
+    tree="random_per_seq"), uniforms [B,N].  The children of a node are
+    independent Gumbel-max draws from q = softmax(draft row / T) of the
+    parent, the way a sampling drafter grows the tree."""
+    B, N, V, dt, T = cfg["B"], cfg["N"], cfg["V"], cfg["dtype"], float(cfg["temperature"])
+    ss = np.random.SeedSequence(cfg["seed"]).spawn(6)
+    shape = cfg.get("tree", "binary")
+    if shape == "random_per_seq":
+        kid_p = ss[4].spawn(B)
+        parent = np.stack([tree_parents(N, "random", _rng(kid_p[b])) for b in range(B)])
+    else:
+        parent = tree_parents(N, shape, _rng(ss[4]))
+    ranks = _ranks(cfg, ss[5], V)
+    kid_t, kid_n, kid_x = ss[0].spawn(B), ss[1].spawn(B), ss[2].spawn(B)
+    odt = np.uint16 if dt == "bf16" else np.float32
+    target = np.empty((B, N, V), odt)
+    draft = np.empty((B, N, V), odt)
+    node_tokens = np.zeros((B, N), np.int32)
+
+    def seq(b):
+        par = parent if parent.ndim == 1 else parent[b]
+        target[b] = _round(_target_block(cfg, _rng(kid_t[b]), N, V, ranks), dt)
+        zd = _as_f64(target[b], dt) + _normal(_rng(kid_n[b]), (N, V), cfg["draft_noise"])
+        draft[b] = _round(zd, dt)
+        if N > 1:
+            zd = _as_f64(draft[b], dt)
+            node_tokens[b, 1:] = _gumbel_max(_rng(kid_x[b]), zd[par[1:]], T)
+
+    _parallel(B, seq)
+    uniforms = _rng(ss[3]).random((B, N), dtype=np.float32)
+    return dict(kind="tree_sample", dtype=dt, B=B, N=N, V=V, temperature=np.float32(T),
+                target=target, draft=draft, node_tokens=node_tokens, parent=parent, uniforms=uniforms)
+
+
 def make_lmhead(cfg):
     """EAGLE-style inputs: features, LM head weight, draft tokens, uniforms."""
     B, g, d, V, T = cfg["B"], cfg["gamma"], cfg["d"], cfg["V"], float(cfg["temperature"])
@@ -192,7 +233,7 @@ def make_lmhead(cfg):
                 uniforms=uniforms)
 
 
-_MAKERS = {"linear": make_linear, "tree": make_tree, "lmhead": make_lmhead}
+_MAKERS = {"linear": make_linear, "tree": make_tree, "tree_sample": make_tree_sample, "lmhead": make_lmhead}
 _CACHE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), ".cache", "specgen")
 
 

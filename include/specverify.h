@@ -85,7 +85,8 @@ typedef enum {
   SPEC_MODE_TREE = 2,     /* spec_verify_tree:   gamma_or_N = N (nodes)    */
   SPEC_MODE_LMHEAD = 3,   /* lmhead_verify:      gamma_or_N = gamma, d     */
   SPEC_MODE_ROWSTATS = 4, /* spec_row_stats / spec_probe_probs: B = rows   */
-  SPEC_MODE_TREE_EXPAND = 5 /* spec_tree_expand:  gamma_or_N = K_in        */
+  SPEC_MODE_TREE_EXPAND = 5, /* spec_tree_expand:  gamma_or_N = K_in       */
+  SPEC_MODE_TREE_SAMPLE = 6  /* spec_verify_tree_sample: gamma_or_N = N    */
 } spec_mode;
 
 /* Limits checked by every entry point. */
@@ -223,6 +224,49 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
                              int32_t* accept_len, int32_t* out_path,
                              int32_t* out_tokens, void* ws, size_t ws_bytes,
                              hipStream_t s);
+
+/*
+ * spec_verify_tree_sample -- stochastic (sampling) verification of a draft
+ * tree per sequence, lossless for the target distribution.
+ * Pages: "EAGLE-3 speculative decoding review", "The Complete EAGLE-3
+ * Inference Process" (4. Strict Acceptance: min(1, p/q) acceptance with
+ * residual correction, on the tree) and "Does Using a Small Model's Answer
+ * Reduce Quality?" (A(x) = min(1, p(x)/q(x)); resample from
+ * norm(max(0, p - q))).
+ *
+ * p = softmax(target row / T), q = softmax(draft row / T).  The children of
+ * a node are taken to be independent draws from that node's q.  From the
+ * root: the children of the current node are tested in increasing index;
+ * child c (token x) is accepted iff uniforms[b][c] < p_k(x) / q(x), with
+ * p_1 = p and p_{k+1} = norm(max(0, p_k - q)) after each rejection; an
+ * accepted child becomes the current node.  If every child is rejected one
+ * token is drawn from the last residual; at a node without children the
+ * bonus token is drawn from p.  The final draw takes uniforms[b][0]
+ * (inverse CDF in vocabulary order, as in spec_verify_sample).
+ *
+ * target_logits, draft_logits [B, N, V] (dt): row n of each belongs to node
+ *               n; draft row n is the law n's children were drawn from (the
+ *               rows of leaves are read but their values never matter).
+ * node_tokens   [B, N] int32 (node 0's token is not read).
+ * parent        [N] (parent_batch_stride = 0) or [B, N] (= N): parent[0] = -1
+ *               and 0 <= parent[n] < n.
+ * uniforms      [B, N] float32 in [0, 1).
+ * accept_len [B] out: number of accepted nodes; -1 when the tree is invalid
+ *            or a token of a node n >= 1 lies outside [0, V) (outputs -1).
+ * out_path   [B, N] out: accepted nodes (root excluded) in root-to-leaf
+ *            order, then -1.
+ * out_tokens [B, N] out: their tokens, then the drawn token, then -1.
+ * 1 <= N <= SPEC_MAX_TREE_NODES, 1 <= V <= SPEC_MAX_SAMPLE_VOCAB.
+ * Logit pointers 16-byte aligned, the others 4-byte aligned.
+ * Workspace: spec_workspace_bytes(SPEC_MODE_TREE_SAMPLE, B, N, V, 0).
+ */
+spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits,
+                                    spec_dtype dt, const int32_t* node_tokens,
+                                    const int32_t* parent, int parent_batch_stride,
+                                    const float* uniforms, int B, int N, int V,
+                                    float temperature, int32_t* accept_len,
+                                    int32_t* out_path, int32_t* out_tokens, void* ws,
+                                    size_t ws_bytes, hipStream_t s);
 
 /*
  * lmhead_project -- logits of feature rows through the LM head, z = h W.

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     MODE_SAMPLE,
     MODE_TREE,
     MODE_TREE_EXPAND,
+    MODE_TREE_SAMPLE,
     SPEC_BF16,
     SPEC_F32,
     SpecError,
@@ -34,5 +35,6 @@ from ._binding import (  # noqa: F401
     verify_greedy,
     verify_sample,
     verify_tree,
+    verify_tree_sample,
     workspace_bytes,
 )

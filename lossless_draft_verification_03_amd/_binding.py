@@ -22,7 +22,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_EHIP = range(6)
 SPEC_F32, SPEC_BF16 = 0, 1
-MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS, MODE_TREE_EXPAND = range(6)
+MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS, MODE_TREE_EXPAND, MODE_TREE_SAMPLE = range(7)
 W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (feature innermost)
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
@@ -37,6 +37,8 @@ _SIGS = {
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz,
+                                     _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
@@ -171,6 +173,26 @@ def verify_tree(target, node_tokens, parent, ws=None, out=None):
     _check(lib.spec_verify_tree(_ptr(target), dtype_code(target), _ptr(node_tokens), _ptr(parent), stride,
                                 B, N, V, _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
                                 _stream(dev)), "spec_verify_tree")
+    return out
+
+
+def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None):
+    """target, draft [B, N, V]; node_tokens [B, N]; parent [N] or [B, N];
+    uniforms [B, N] -> (accept_len, out_path, out_tokens)."""
+    B, N, V = target.shape
+    if tuple(draft.shape) != (B, N, V) or dtype_code(draft) != dtype_code(target):
+        raise ValueError("draft must match target in shape and dtype")
+    dev = target.device
+    stride = 0 if parent.dim() == 1 else N
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int32, device=dev))
+    acc, path, toks = out
+    w = _workspace(MODE_TREE_SAMPLE, B, N, V, 0, dev, ws)
+    _check(lib.spec_verify_tree_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(node_tokens),
+                                       _ptr(parent), stride, _ptr(uniforms), B, N, V, float(temperature),
+                                       _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
+           "spec_verify_tree_sample")
     return out
 
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "rowstats.hip", "sample.hip", "greedy_tree.hip", "lmhead.hip", "kv.hip", "tree_build.hip"]
+SOURCES = ["api.hip", "rowstats.hip", "sample.hip", "greedy_tree.hip", "lmhead.hip", "kv.hip", "tree_build.hip", "tree_sample.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -11,6 +11,9 @@
 
 using namespace sv;
 
+static_assert(SPEC_MAX_TREE_NODES == kTreeMaxNodes, "tree size limit of the walk kernel");
+static_assert((long long)SPEC_MAX_SAMPLE_VOCAB == kMaxSampleVocab, "vocabulary limit of the draw kernels");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -48,6 +51,10 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
     case SPEC_MODE_TREE:
       if (gN < 1 || gN > SPEC_MAX_TREE_NODES) return false;
       rows = B * gN;
+      break;
+    case SPEC_MODE_TREE_SAMPLE:
+      if (gN < 1 || gN > SPEC_MAX_TREE_NODES) return false;
+      rows = 2 * B * gN;
       break;
     case SPEC_MODE_ROWSTATS:
       rows = B;
@@ -377,6 +384,51 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
   p.out_path = out_path;
   p.out_tokens = out_tokens;
   return hip_status(launch_tree_finish(p, s));
+}
+
+spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
+                                    const int32_t* node_tokens, const int32_t* parent, int parent_batch_stride,
+                                    const float* uniforms, int B, int N, int V, float temperature,
+                                    int32_t* accept_len, int32_t* out_path, int32_t* out_tokens, void* ws,
+                                    size_t ws_bytes, hipStream_t s) {
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (B < 1 || B > SPEC_MAX_BATCH || N < 1 || N > SPEC_MAX_TREE_NODES || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
+      !row_bytes_ok(V, dt))
+    return SPEC_EINVAL;
+  if (parent_batch_stride != 0 && parent_batch_stride != N) return SPEC_EINVAL;
+  if (!target_logits || !draft_logits || !node_tokens || !parent || !uniforms || !accept_len || !out_path ||
+      !out_tokens)
+    return SPEC_EINVAL;
+  if (!aligned(target_logits, 16) || !aligned(draft_logits, 16) || !aligned(node_tokens, 4) ||
+      !aligned(parent, 4) || !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_path, 4) ||
+      !aligned(out_tokens, 4))
+    return SPEC_EALIGN;
+  TempConst tc;
+  if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
+  Layout L;
+  if (!make_layout(SPEC_MODE_TREE_SAMPLE, B, N, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  const spec_status w = check_ws(ws, ws_bytes, L);
+  if (w != SPEC_OK) return w;
+  const long long rows = (long long)B * N;
+  hipError_t e = row_sweep(target_logits, rows, draft_logits, rows, V, (int)dt, 1, tc, ws, L, s);
+  if (e != hipSuccess) return SPEC_EHIP;
+  TreeSampleParams p;
+  p.tgt = target_logits;
+  p.drf = draft_logits;
+  p.tokens = node_tokens;
+  p.parent = parent;
+  p.parent_stride = parent_batch_stride;
+  p.unif = uniforms;
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.tc = tc;
+  p.part = at<Partial>(ws, L.part);
+  p.nseg_rows = row_sweep_shape(V, (int)dt).nseg;
+  p.accept_len = accept_len;
+  p.out_path = out_path;
+  p.out_tokens = out_tokens;
+  return hip_status(launch_tree_sample(p, (int)dt, s));
 }
 
 spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W, spec_wlayout wl,

@@ -36,22 +36,9 @@ namespace {
 constexpr int kRun = 32;   // elements per lane in the draw's rescan (multiple of 8)
 constexpr int kSegElems = kBlock * kRun;
 
-struct DrawRow {
-  const char* t;      // target row base (element 0 of the row)
-  const char* d;      // draft row base (resid only)
-  float Mt, Md;
-  float rho_hi, rho_lo;
-  bool resid;
-};
-
 template <int DT>
 __device__ __forceinline__ float weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
-  const float et = exp_rel<DT>(zt, R.Mt, tc);
-  if (!R.resid) return et;
-  const float ed = exp_rel<DT>(zd, R.Md, tc);
-  float w = fmaf(-ed, R.rho_hi, et);
-  w = fmaf(-ed, R.rho_lo, w);
-  return fmaxf(w, 0.f);
+  return draw_weight<DT>(R, zt, zd, tc);
 }
 
 template <int DT>
@@ -200,39 +187,6 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
   const long long se = sb + P.seg_elems < V ? sb + P.seg_elems : V;
   const double part = block_sum(segment_partial<DT, ALIGNED>(R, sb, se, P.tc, tid), sh4, tid);
   if (tid == 0) P.segsum[(long long)b * P.nseg + s] = part;
-}
-
-// Wave-parallel location of the segment holding thr: lanes scan the segment
-// masses in chunks of 64 (fp64 inclusive scans, fixed order).  Returns the
-// segment index and the mass before it; if rounding leaves no crossing, the
-// last segment with positive mass and fallback = 1.
-__device__ __forceinline__ int locate_segment(const double* seg, int nseg, double thr, int lane, double* base,
-                                             int* fallback) {
-  double carry = 0.0;
-  int last = 0;
-  double lastbase = 0.0;
-  for (int c0 = 0; c0 < nseg; c0 += kWave) {
-    const int t = c0 + lane;
-    const double m = t < nseg ? seg[t] : 0.0;
-    const double incl = carry + wave_incl_scan(m, lane);
-    const unsigned long long mc = __ballot(m > 0.0 && incl > thr);
-    const unsigned long long mp = __ballot(m > 0.0);
-    if (mc) {
-      const int l = (int)__ffsll((long long)mc) - 1;
-      *base = readlane_d(incl, l) - readlane_d(m, l);
-      *fallback = 0;
-      return c0 + l;
-    }
-    if (mp) {
-      const int l = 63 - (int)__clzll((long long)mp);
-      last = c0 + l;
-      lastbase = readlane_d(incl, l) - readlane_d(m, l);
-    }
-    carry = readlane_d(incl, kWave - 1);
-  }
-  *base = lastbase;
-  *fallback = 1;
-  return last;
 }
 
 template <int DT, bool ALIGNED>

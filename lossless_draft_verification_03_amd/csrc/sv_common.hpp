@@ -230,6 +230,61 @@ __device__ __forceinline__ float exp_rel(float z, float M, const TempConst& tc) 
   }
 }
 
+// The row a final draw samples from: the target row alone (weights
+// e_t = 2^((z_t - M_t) c), proportional to p), or a residual row with weights
+// max(0, e_t - rho e_d) proportional to max(0, p - (rho S_d / S_t) q); rho is
+// carried as the float pair rho_hi + rho_lo.
+struct DrawRow {
+  const char* t;      // target row base (element 0 of the row)
+  const char* d;      // draft row base (resid only)
+  float Mt, Md;
+  float rho_hi, rho_lo;
+  bool resid;
+};
+
+template <int DT>
+__device__ __forceinline__ float draw_weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
+  const float et = exp_rel<DT>(zt, R.Mt, tc);
+  if (!R.resid) return et;
+  const float ed = exp_rel<DT>(zd, R.Md, tc);
+  float w = fmaf(-ed, R.rho_hi, et);
+  w = fmaf(-ed, R.rho_lo, w);
+  return fmaxf(w, 0.f);
+}
+
+// Wave-parallel location of the segment holding thr: lanes scan the segment
+// masses in chunks of 64 (fp64 inclusive scans, fixed order).  Returns the
+// segment index and the mass before it; if rounding leaves no crossing, the
+// last segment with positive mass and fallback = 1.
+__device__ __forceinline__ int locate_segment(const double* seg, int nseg, double thr, int lane, double* base,
+                                             int* fallback) {
+  double carry = 0.0;
+  int last = 0;
+  double lastbase = 0.0;
+  for (int c0 = 0; c0 < nseg; c0 += kWave) {
+    const int t = c0 + lane;
+    const double m = t < nseg ? seg[t] : 0.0;
+    const double incl = carry + wave_incl_scan(m, lane);
+    const unsigned long long mc = __ballot(m > 0.0 && incl > thr);
+    const unsigned long long mp = __ballot(m > 0.0);
+    if (mc) {
+      const int l = (int)__ffsll((long long)mc) - 1;
+      *base = readlane_d(incl, l) - readlane_d(m, l);
+      *fallback = 0;
+      return c0 + l;
+    }
+    if (mp) {
+      const int l = 63 - (int)__clzll((long long)mp);
+      last = c0 + l;
+      lastbase = readlane_d(incl, l) - readlane_d(m, l);
+    }
+    carry = readlane_d(incl, kWave - 1);
+  }
+  *base = lastbase;
+  *fallback = 1;
+  return last;
+}
+
 // Sequence-level result of the accept scan, handed to the draw kernels.
 struct DrawInfo {
   int j;        // accepted drafts (0..gamma), or -1 for an invalid draft token

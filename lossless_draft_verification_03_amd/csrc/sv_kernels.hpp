@@ -191,4 +191,28 @@ struct TreeBuildParams {
 };
 hipError_t launch_tree_build(const TreeBuildParams& p, hipStream_t s);
 
+// ---------------------------------------------------------- tree sampling
+constexpr int kTreeMaxNodes = 4096;           // nodes per tree (verification calls)
+constexpr long long kMaxSampleVocab = 1LL << 25;
+
+// One workgroup per sequence walks its tree after the row sweep over the
+// 2 B N rows (target rows, then draft rows), merging the partials of the
+// rows it visits.
+struct TreeSampleParams {
+  const void* tgt;         // [B, N, V] target rows of the nodes
+  const void* drf;         // [B, N, V] draft rows (row n: the law n's children were drawn from)
+  const int32_t* tokens;   // [B, N]
+  const int32_t* parent;   // [N] or [B, N]
+  int parent_stride;       // 0 or N
+  const float* unif;       // [B, N]: u[b][n] tests node n, u[b][0] is the final draw
+  int B, N, V;
+  TempConst tc;
+  const Partial* part;     // [2 B N][nseg_rows] sweep partials
+  int nseg_rows;
+  int32_t* accept_len;     // [B]
+  int32_t* out_path;       // [B, N]
+  int32_t* out_tokens;     // [B, N]
+};
+hipError_t launch_tree_sample(const TreeSampleParams& p, int dt, hipStream_t s);
+
 }  // namespace sv

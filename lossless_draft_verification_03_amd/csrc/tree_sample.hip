@@ -1,0 +1,464 @@
+// Stochastic (sampling) verification of a draft tree, after the row sweep.
+//
+// Pages: "EAGLE-3 speculative decoding review", "The Complete EAGLE-3
+// Inference Process" (4. Strict Acceptance: for sampling, min(1, p/q)
+// acceptance with residual correction keeps the target distribution, here on
+// a tree); "Does Using a Small Model's Answer Reduce Quality?" (A(x) =
+// min(1, p(x)/q(x)); resample from norm(max(0, p - q))); "Speculative
+// Decoding", 3. Accept or Reject.
+//
+// Reading of the sibling rule (the pages name it for trees without spelling
+// out siblings): the children of a node were drawn independently from the
+// node's draft row q and are tried in increasing node index; the first child
+// is tested against p_1 = p, and after each rejection the law moves on to
+// p_{k+1} = norm(max(0, p_k - q)).  An accepted child becomes the current
+// node; when every child is rejected one token is drawn from the last
+// residual; at a node without children the bonus token is drawn from p.
+// Uniforms: u[n] (n >= 1) is node n's test, u[0] the final draw.
+//
+// Closed form used for the residual chain.  With c_1 = 0, W_1 = 1,
+//   p_k = max(0, p - c_k q) / W_k,  c_{k+1} = c_k + W_k,
+//   W_{k+1} = sum_v max(0, p(v) - c_{k+1} q(v)).
+// (Induction: where p > c_k q, max(0, p_k - q) = max(0, p - (c_k + W_k) q)
+// / W_k; elsewhere both sides are 0.)  So child k passes iff
+//   u < max(0, p(x)/q(x) - c_k) / W_k,
+// the ratio p(x)/q(x) formed in fp64 exactly as in the chain sampler, and a
+// residual is a draw row with rho = c S_t / S_d.  A zero W (impossible in
+// exact arithmetic after a rejection) leaves (c, W) unchanged.
+//
+// k_tree_walk: one 1024-thread workgroup per sequence after the row sweep.
+// It stages the tree in LDS, validates it, gathers every node's token logit
+// from its parent's target and draft rows (one round trip for the whole
+// tree), then walks from the root: merge the node's two row statistics
+// from the sweep's partials, list its children in index order (block scan),
+// test them; a rejection followed by another child costs one pass over the
+// node's two rows for W; the final draw is one pass for the segment masses,
+// then the inverse CDF inside the segment that holds u[0] * total.
+#include "sv_kernels.hpp"
+
+#include <limits.h>
+
+namespace sv {
+
+namespace {
+
+constexpr int kTB = 1024;                  // threads per walk workgroup
+constexpr int kTW = kTB / kWave;           // waves per walk workgroup
+// Elements per thread in one draw segment: four 16-byte vectors per row, so
+// the pick's registers (weights plus loads) fit the 128 VGPRs a 1024-thread
+// workgroup leaves each lane.
+template <int DT>
+constexpr int walk_run() { return DT == DT_BF16 ? 32 : 16; }
+template <int DT>
+constexpr int walk_seg() { return kTB * walk_run<DT>(); }
+constexpr int kTChunk = 16;                // segments per LDS reduction round
+constexpr int kTPer = kTreeMaxNodes / kTB; // nodes per thread in the child scan
+constexpr int kTMaxSeg = (int)(((long long)kMaxSampleVocab + kTB * 16 - 1) / (kTB * 16));
+static_assert(kTreeMaxNodes % kTB == 0, "child scan covers the node range exactly");
+
+struct WalkLds {
+  int par[kTreeMaxNodes];
+  int tok[kTreeMaxNodes];
+  float u[kTreeMaxNodes];
+  float gt[kTreeMaxNodes];   // target logit of node c's token in its parent's row
+  float gd[kTreeMaxNodes];   // draft logit of the same
+  int kids[kTreeMaxNodes];   // children of the current node, index order
+  double seg[kTMaxSeg];      // segment masses of the last pass
+  double red[kTChunk * kTW];
+  double wtot[kTW];
+  int wcnt[kTW];
+  int first[kTW];
+  float M[2];
+  double S[2];
+  double total, base, thr;
+  long long y;
+  int nk, k, fallback;
+};
+
+// One segment's draw weights, lane-interleaved 16-byte vectors, fp64
+// accumulation; returns this thread's partial.
+template <int DT, bool ALIGNED>
+__device__ double walk_seg_partial(const DrawRow& R, long long e0, long long e1, const TempConst& tc, int tid) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  double acc = 0.0;
+  if constexpr (ALIGNED) {
+    constexpr int KV = walk_run<DT>() / EPV;
+    const int nvec = (int)((e1 - e0) / EPV);
+    if (nvec <= 0) return 0.0;
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + e0 * ES, (uint32_t)nvec * 16u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + e0 * ES, (uint32_t)nvec * 16u);
+    v4i vt[KV], vd[KV];
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      const uint32_t off = (uint32_t)min(k * kTB + tid, nvec - 1) * 16u;
+      vt[k] = load16(rt, off);
+      if (R.resid) vd[k] = load16(rd, off);
+    }
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      if (k * kTB + tid >= nvec) continue;
+      float zt[EPV], zd[EPV];
+      unpack<DT>(vt[k], zt);
+      if (R.resid) unpack<DT>(vd[k], zd);
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+    }
+  } else {
+    for (long long e = e0 + tid; e < e1; e += kTB) {
+      const float zt = load_elem<DT>(R.t, e);
+      const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
+      acc += (double)draw_weight<DT>(R, zt, zd, tc);
+    }
+  }
+  return acc;
+}
+
+// Segment masses of the draw row into L.seg and their total (segment order,
+// fixed combination order throughout).  Every thread of the block calls it.
+template <int DT, bool ALIGNED>
+__device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, WalkLds& L, int tid) {
+  constexpr int SEG = walk_seg<DT>();
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nseg = (int)((V + SEG - 1) / SEG);
+  for (int s0 = 0; s0 < nseg; s0 += kTChunk) {
+    const int s1 = min(s0 + kTChunk, nseg);
+    for (int s = s0; s < s1; ++s) {
+      const long long e0 = (long long)s * SEG;
+      const long long e1 = e0 + SEG < V ? e0 + SEG : V;
+      const double a = wave_sum(walk_seg_partial<DT, ALIGNED>(R, e0, e1, tc, tid));
+      if (lane == 0) L.red[(s - s0) * kTW + wid] = a;
+    }
+    __syncthreads();
+    if (tid < s1 - s0) {
+      double t = 0.0;
+      for (int w = 0; w < kTW; ++w) t += L.red[tid * kTW + w];
+      L.seg[s0 + tid] = t;
+    }
+    __syncthreads();
+  }
+  if (wid == 0) {
+    double tot = 0.0;
+    for (int c0 = 0; c0 < nseg; c0 += kWave) tot += wave_sum(c0 + lane < nseg ? L.seg[c0 + lane] : 0.0);
+    if (lane == 0) L.total = tot;
+  }
+  __syncthreads();
+  return L.total;
+}
+
+// Inverse-CDF draw over the masses the last mass_pass left in L.seg: the
+// first element whose cumulative weight exceeds thr, or the last element
+// with positive weight if rounding leaves none.
+template <int DT, bool ALIGNED>
+__device__ long long walk_pick(const DrawRow& R, long long V, double thr, const TempConst& tc, WalkLds& L,
+                               int tid) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int RUN = walk_run<DT>();
+  constexpr int SEG = walk_seg<DT>();
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nseg = (int)((V + SEG - 1) / SEG);
+  if (wid == 0) {
+    double base;
+    int fb;
+    const int k = locate_segment(L.seg, nseg, thr, lane, &base, &fb);
+    if (lane == 0) {
+      L.k = k;
+      L.base = base;
+      L.fallback = fb;
+      L.y = -1;
+    }
+  }
+  __syncthreads();
+  const long long kb = (long long)L.k * SEG;
+  const long long ke = kb + SEG < V ? kb + SEG : V;
+  const long long rb0 = kb + (long long)tid * RUN;
+  const long long rb = rb0 < ke ? rb0 : ke;
+  const long long re = rb + RUN < ke ? rb + RUN : ke;
+  float w[RUN];
+  if constexpr (ALIGNED) {
+    constexpr int KV = RUN / EPV;
+    const int nvec = (int)((re - rb) / EPV);
+    const int segvec = (int)((ke - kb) / EPV);
+    const int lane_vec0 = (int)((rb - kb) / EPV);
+    if (nvec > 0) {
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + kb * ES, (uint32_t)segvec * 16u);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + kb * ES, (uint32_t)segvec * 16u);
+      v4i vt[KV], vd[KV];
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        const uint32_t off = (uint32_t)(lane_vec0 + min(k, nvec - 1)) * 16u;
+        vt[k] = load16(rt, off);
+        if (R.resid) vd[k] = load16(rd, off);
+      }
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        float zt[EPV], zd[EPV];
+        unpack<DT>(vt[k], zt);
+        if (R.resid) unpack<DT>(vd[k], zd);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i)
+          w[k * EPV + i] = k < nvec ? draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < RUN; ++e) w[e] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < RUN; ++e) {
+      const long long ee = rb + e;
+      float v = 0.f;
+      if (ee < re) {
+        const float zt = load_elem<DT>(R.t, ee);
+        const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
+        v = draw_weight<DT>(R, zt, zd, tc);
+      }
+      w[e] = v;
+    }
+  }
+  double T4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int e = 0; e < RUN; ++e) T4[e & 3] += (double)w[e];
+  const double T = (T4[0] + T4[1]) + (T4[2] + T4[3]);
+  const double incl = wave_incl_scan(T, lane);
+  if (lane == kWave - 1) L.wtot[wid] = incl;
+  __syncthreads();
+  double wbase = 0.0;
+  for (int v = 0; v < wid; ++v) wbase += L.wtot[v];
+  const double excl = L.base + wbase + (incl - T);
+  const bool cross = !L.fallback && T > 0.0 && excl + T > thr;
+  const unsigned long long mc = __ballot(cross);
+  const unsigned long long mp = __ballot(T > 0.0);
+  if (lane == 0) L.first[wid] = mc ? wid * kWave + (int)__ffsll((long long)mc) - 1 : INT_MAX;
+  __syncthreads();
+  int first = INT_MAX;
+  for (int v = 0; v < kTW; ++v) first = min(first, L.first[v]);
+  __syncthreads();
+  if (lane == 0) L.first[wid] = mp ? wid * kWave + 63 - (int)__clzll((long long)mp) : -1;
+  __syncthreads();
+  int lastpos = -1;
+  for (int v = 0; v < kTW; ++v) lastpos = max(lastpos, L.first[v]);
+  const int who = first != INT_MAX ? first : lastpos;
+  if (tid == who) {
+    double acc = excl;
+    int y = -1, ylast = -1;
+#pragma unroll
+    for (int e = 0; e < RUN; ++e) {
+      if (w[e] > 0.f) {
+        acc += (double)w[e];
+        ylast = e;
+        if (y < 0 && first != INT_MAX && acc > thr) y = e;
+      }
+    }
+    L.y = rb + (y >= 0 ? y : ylast);
+  }
+  __syncthreads();
+  return L.y;
+}
+
+// Test value of the k-th child: max(0, p(x)/q(x) - c) / W, with p(x)/q(x) =
+// 2^((z_t(x) - M_t) c64 - (z_d(x) - M_d) c64) S_d / S_t in fp64; p(x) = 0
+// gives 0, q(x) = 0 < p(x) gives +inf.  For c = 0, W = 1 this is the chain
+// sampler's ratio bit for bit.
+__device__ __forceinline__ double child_ratio(float zt, float zd, float Mt, double St, float Md, double Sd,
+                                              double c, double W, const TempConst& tc) {
+  const double et = ((double)zt - (double)Mt) * tc.c64;
+  const double ed = ((double)zd - (double)Md) * tc.c64;
+  if (!(et > -__builtin_huge_val())) return 0.0;
+  if (!(ed > -__builtin_huge_val())) return __builtin_huge_val();
+  const double r = exp2_f64(et - ed) * (Sd / St);
+  const double d = r - c;
+  return d > 0.0 ? d / W : 0.0;
+}
+
+__device__ __forceinline__ void set_rho(DrawRow& R, double c, double St, double Sd) {
+  R.resid = c > 0.0;
+  const double rho = R.resid ? c * (St / Sd) : 0.0;
+  R.rho_hi = (float)rho;
+  R.rho_lo = (float)(rho - (double)R.rho_hi);
+}
+
+template <int DT, bool ALIGNED, int NP>
+__global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  __shared__ WalkLds L;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int b = blockIdx.x;
+  const int N = P.N;
+  const long long V = P.V;
+  const long long row0 = (long long)b * N;
+  const char* tgt = static_cast<const char*>(P.tgt);
+  const char* drf = static_cast<const char*>(P.drf);
+  const int* par_g = P.parent + (long long)b * P.parent_stride;
+  int* out_path = P.out_path + row0;
+  int* out_tok = P.out_tokens + row0;
+
+  // stage and validate the tree; gather each node's token logit from its
+  // parent's rows (only for nodes whose parent and token are in range)
+  int bad = 0;
+  for (int c = tid; c < N; c += kTB) {
+    const int p = par_g[c];
+    const int x = P.tokens[row0 + c];
+    const bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
+    const bool xok = c == 0 || (x >= 0 && (long long)x < V);
+    float zt = 0.f, zd = 0.f;
+    if (c > 0 && pok && xok) {
+      zt = load_elem<DT>(tgt, (row0 + p) * V + x);
+      zd = load_elem<DT>(drf, (row0 + p) * V + x);
+    }
+    bad |= !(pok && xok);
+    L.par[c] = p;
+    L.tok[c] = x;
+    L.u[c] = P.unif[row0 + c];
+    L.gt[c] = zt;
+    L.gd[c] = zd;
+  }
+  if (__syncthreads_or(bad)) {
+    for (int c = tid; c < N; c += kTB) {
+      out_path[c] = -1;
+      out_tok[c] = -1;
+    }
+    if (tid == 0) P.accept_len[b] = -1;
+    return;                                   // uniform
+  }
+
+  int n = 0, d = 0;
+  DrawRow R;
+  double c_fb = 0.0;                          // the law to fall back to if the draw row has no mass
+  for (;;) {
+    // statistics of node n's target (wave 0) and draft (wave 1) rows
+    if (wid < 2) {
+      const long long r = (wid == 0 ? 0 : (long long)P.B * N) + row0 + n;
+      float M;
+      double S;
+      int a;
+      merge_partials<1, NP>(P.part + r * P.nseg_rows, P.nseg_rows, P.tc, lane & (NP - 1), &M, &S, &a);
+      if (lane == 0) {
+        L.M[wid] = M;
+        L.S[wid] = S;
+      }
+    }
+    // children of n in index order: block scan over kTPer nodes per thread
+    int flag[kTPer];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kTPer; ++j) {
+      const int c = tid * kTPer + j;
+      flag[j] = c > n && c < N && L.par[c] == n;
+      cnt += flag[j];
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) L.wcnt[wid] = incl;
+    __syncthreads();
+    int pos = incl - cnt, nk = 0;
+    for (int v = 0; v < kTW; ++v) {
+      const int t = L.wcnt[v];
+      if (v < wid) pos += t;
+      nk += t;
+    }
+#pragma unroll
+    for (int j = 0; j < kTPer; ++j)
+      if (flag[j]) L.kids[pos++] = tid * kTPer + j;
+    __syncthreads();
+    const float Mt = L.M[0], Md = L.M[1];
+    const double St = L.S[0], Sd = L.S[1];
+    R.t = tgt + (row0 + n) * V * ES;
+    R.d = drf + (row0 + n) * V * ES;
+    R.Mt = Mt;
+    R.Md = Md;
+    if (nk == 0) {                            // leaf: bonus token from p
+      set_rho(R, 0.0, St, Sd);
+      c_fb = 0.0;
+      break;
+    }
+    // every thread evaluates the same tests on the same LDS values, so the
+    // decisions (and the passes between them) are block-uniform
+    double cc = 0.0, W = 1.0;
+    int chosen = -1;
+    for (int i = 0; i < nk; ++i) {
+      const int ci = L.kids[i];
+      const double r = child_ratio(L.gt[ci], L.gd[ci], Mt, St, Md, Sd, cc, W, P.tc);
+      if ((double)L.u[ci] < r) {
+        chosen = ci;
+        break;
+      }
+      const double cn = cc + W;
+      if (i + 1 == nk) {                      // every child rejected
+        set_rho(R, cn, St, Sd);
+        c_fb = cc;
+        break;
+      }
+      set_rho(R, cn, St, Sd);
+      const double Wn = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid) / St;
+      if (Wn > 0.0) {
+        cc = cn;
+        W = Wn;
+      }
+    }
+    if (chosen < 0) break;
+    if (tid == 0) {
+      out_path[d] = chosen;
+      out_tok[d] = L.tok[chosen];
+    }
+    ++d;
+    n = chosen;
+    __syncthreads();                          // LDS of this node is read before it is reused
+  }
+
+  // final draw from R (fallback: the law before the last residual, then p)
+  double total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+  if (!(total > 0.0) && R.resid) {
+    set_rho(R, c_fb, L.S[0], L.S[1]);
+    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+  }
+  if (!(total > 0.0) && R.resid) {
+    set_rho(R, 0.0, L.S[0], L.S[1]);
+    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+  }
+  const long long y = walk_pick<DT, ALIGNED>(R, V, (double)L.u[0] * total, P.tc, L, tid);
+  for (int c = tid; c < N; c += kTB) {
+    if (c >= d) out_path[c] = -1;
+    if (c > d) out_tok[c] = -1;
+  }
+  if (tid == 0) {
+    out_tok[d] = (int)y;
+    P.accept_len[b] = d;
+  }
+}
+
+template <int DT, bool ALIGNED, int NP>
+hipError_t launch_walk_np(const TreeSampleParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_tree_walk<DT, ALIGNED, NP>), dim3((unsigned)p.B), dim3(kTB), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT, bool ALIGNED>
+hipError_t launch_walk_t(const TreeSampleParams& p, hipStream_t s) {
+  switch (merge_group(p.nseg_rows)) {
+    case 1: return launch_walk_np<DT, ALIGNED, 1>(p, s);
+    case 2: return launch_walk_np<DT, ALIGNED, 2>(p, s);
+    case 4: return launch_walk_np<DT, ALIGNED, 4>(p, s);
+    case 8: return launch_walk_np<DT, ALIGNED, 8>(p, s);
+    case 16: return launch_walk_np<DT, ALIGNED, 16>(p, s);
+    case 32: return launch_walk_np<DT, ALIGNED, 32>(p, s);
+    default: return launch_walk_np<DT, ALIGNED, 64>(p, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_sample(const TreeSampleParams& p, int dt, hipStream_t s) {
+  if (p.B < 1 || p.N < 1 || p.N > kTreeMaxNodes || p.V < 1 || (long long)p.V > kMaxSampleVocab)
+    return hipErrorInvalidValue;
+  const bool aligned = dt == DT_BF16 ? (p.V % 8 == 0) : (p.V % 4 == 0);
+  if (dt == DT_BF16) return aligned ? launch_walk_t<DT_BF16, true>(p, s) : launch_walk_t<DT_BF16, false>(p, s);
+  return aligned ? launch_walk_t<DT_F32, true>(p, s) : launch_walk_t<DT_F32, false>(p, s);
+}
+
+}  // namespace sv

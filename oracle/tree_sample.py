@@ -22,7 +22,9 @@ at every node has law p (multi-draft recursive rejection sampling).  An
 accepted child becomes the current node.  If every child is rejected, one
 token is drawn from the last residual p_{m+1}; at a node without children the
 bonus token is drawn from p.  Uniforms: u[n] (n >= 1) is node n's test; u[0],
-the root's slot (the root is never tested), is the final draw.
+the root's slot (the root is never tested), is the final draw.  As for a
+chain of drafts, a token outside [0, V) on any node but the root makes the
+sequence invalid (accept_len = -1).
 """
 import numpy as np
 
@@ -44,10 +46,11 @@ def verify_tree_sample_seq(zt, zd, node_tokens, parent, u, T):
     root down (root excluded), tokens = their tokens then the final token.
     info: tests [(node, u, r)], draw (inverse_cdf info), w (the final draw's
     weights, unnormalised)."""
-    if not tree_is_valid(parent):
-        return -1, [], [], dict(tests=[], draw=None, w=None)
     zt = np.asarray(zt, np.float64)
     zd = np.asarray(zd, np.float64)
+    V = zt.shape[1]
+    if not tree_is_valid(parent) or any(not 0 <= int(t) < V for t in np.asarray(node_tokens)[1:]):
+        return -1, [], [], dict(tests=[], draw=None, w=None)
     kids = children_of(parent)
     tests = []
     path = []

@@ -14,6 +14,10 @@ import torch
 
 MARGIN = 1e-6
 MAX_RATE = 1e-4
+# Tree sampling: a test after a rejected sibling compares u with
+# (p(x)/q(x) - c) / W, where W is a sum of float32 residual weights over the
+# whole vocabulary (error up to a few float32 ulps of 1 + c per unit W).
+MARGIN_RESID = 1e-5
 
 
 def to_dev(arr, device="cuda"):
@@ -63,4 +67,62 @@ def classify_sample(gpu_acc, gpu_out, ora_acc, ora_out, infos, margin=MARGIN):
             res["details"].append((b, "draw", y, dist))
         else:
             res["unexplained"].append((b, f"draw: gpu {y} oracle {int(ora_out[b, jo])} distance {dist:.3e}"))
+    return res
+
+
+def _draw_distance(info, y):
+    F, t, w = info["draw"]["F"], info["draw"]["t"], info["w"]
+    if not (0 <= y < len(F)) or not w[y] > 0:
+        return None
+    lo = F[y - 1] if y > 0 else 0.0
+    hi = F[y]
+    return 0.0 if lo <= t < hi else min(abs(t - lo), abs(t - hi))
+
+
+def classify_tree_sample(gpu_acc, gpu_path, gpu_tok, ora_acc, ora_path, ora_tok, infos, parents,
+                         margin=MARGIN, margin_resid=MARGIN_RESID):
+    """Tree sampling: equal outputs, or a first differing decision at an
+    oracle margin: an accept test (first child of its node: |u - r| < margin;
+    a later sibling: < margin_resid) or the final draw (as in
+    classify_sample).  parents [B][N]."""
+    res = dict(exact=0, explained=0, unexplained=[], sequences=len(ora_acc), details=[])
+    for b in range(len(ora_acc)):
+        ja, jo = int(gpu_acc[b]), int(ora_acc[b])
+        gp, gt = np.asarray(gpu_path[b]), np.asarray(gpu_tok[b])
+        if ja == jo and np.array_equal(gp, ora_path[b]) and np.array_equal(gt, ora_tok[b]):
+            res["exact"] += 1
+            continue
+        if ja < 0 or jo < 0:
+            res["unexplained"].append((b, f"validity differs: gpu {ja} oracle {jo}"))
+            continue
+        par = np.asarray(parents[b])
+        gpu_set = set(int(c) for c in gp[:ja])
+        first_child = {}
+        for c in range(1, len(par)):
+            first_child.setdefault(int(par[c]), c)
+        why = None
+        for (c, u, r) in infos[b]["tests"]:
+            if (u < r) != (c in gpu_set):
+                tol = margin if first_child[int(par[c])] == c else margin_resid
+                if abs(u - r) < tol:
+                    why = ("explained", (b, "accept", c, abs(u - r)))
+                else:
+                    why = ("unexplained", (b, f"test of node {c}: |u-r|={abs(u - r):.3e}"))
+                break
+        if why is None:
+            if ja != jo or not np.array_equal(gp, ora_path[b]):
+                why = ("unexplained", (b, "paths differ with every oracle test agreeing"))
+            elif not np.array_equal(gt[:ja], ora_tok[b][:jo]) or np.any(gt[ja + 1:] != -1):
+                why = ("unexplained", (b, "path tokens or padding differ"))
+            else:
+                dist = _draw_distance(infos[b], int(gt[ja]))
+                if dist is not None and dist < margin:
+                    why = ("explained", (b, "draw", int(gt[ja]), dist))
+                else:
+                    why = ("unexplained", (b, f"draw: gpu {int(gt[ja])} oracle {int(ora_tok[b][jo])} {dist}"))
+        if why[0] == "explained":
+            res["explained"] += 1
+            res["details"].append(why[1])
+        else:
+            res["unexplained"].append(why[1])
     return res

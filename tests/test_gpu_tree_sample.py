@@ -1,0 +1,173 @@
+"""Stochastic tree verification on the GPU against the CPU oracle.
+
+[R] "The Complete EAGLE-3 Inference Process", 4. Strict Acceptance (min(1,
+p/q) acceptance with residual correction, on a tree).  Outputs must equal the
+oracle's except where the first differing decision sits at an oracle margin
+(parity.classify_tree_sample); a chain tree must reproduce the chain sampler,
+and the committed tokens must follow the target law (chi-square, no oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_draft_verification_03_amd as L
+import oracle
+from gen import make_workload
+from parity import classify_tree_sample, classify_sample, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, T=None):
+    T = float(w["temperature"]) if T is None else T
+    acc, path, toks = L.verify_tree_sample(to_dev(w["target"]), to_dev(w["draft"]), to_dev(w["node_tokens"]),
+                                           to_dev(np.ascontiguousarray(w["parent"]).astype(np.int32)),
+                                           to_dev(w["uniforms"]), T)
+    return acc.cpu().numpy(), path.cpu().numpy(), toks.cpu().numpy()
+
+
+def _oracle(w, T=None):
+    T = float(w["temperature"]) if T is None else T
+    return oracle.verify_tree_sample(w["target"], w["draft"], w["dtype"], w["node_tokens"], w["parent"],
+                                     w["uniforms"], T)
+
+
+def _parents(w):
+    par = np.asarray(w["parent"])
+    return np.broadcast_to(par, (w["B"], w["N"])) if par.ndim == 1 else par
+
+
+def _check(w, T=None, max_explained=1):
+    g = _run(w, T)
+    o = _oracle(w, T)
+    res = classify_tree_sample(*g, o[0], o[1], o[2], o[3], _parents(w))
+    assert not res["unexplained"], res["unexplained"]
+    assert res["explained"] <= max_explained, res["details"]
+    return g, o
+
+
+@pytest.mark.parametrize("dtype,V,N,tree,noise,T", [
+    ("f32", 1000, 15, "binary", 0.8, 1.0),
+    ("bf16", 777, 31, "random_per_seq", 1.5, 0.7),     # ragged V, per-sequence parents
+    ("bf16", 4096, 9, "chain", 0.5, 1.0),
+    ("f32", 33, 40, "random", 2.0, 1.3),               # tiny ragged V, many siblings
+    ("bf16", 512, 12, "star", 3.0, 1.0),               # 11 siblings: long residual chains
+    ("f32", 300, 21, "wide", 1.0, 0.6),
+    ("bf16", 70001, 7, "star", 2.5, 1.0),              # several draw segments, unaligned
+    ("bf16", 131080, 5, "wide", 2.0, 0.9),             # several draw segments, aligned
+    ("f32", 65540, 6, "random", 1.5, 1.0),
+])
+def test_matches_oracle(dtype, V, N, tree, noise, T):
+    w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
+                      temperature=T, seed=V + N)
+    _check(w)
+
+
+def test_matches_oracle_many_rejections():
+    # far-off drafts: most first children fail, later siblings use residuals
+    w = make_workload("tree_sample63", B=40, N=13, V=2000, dtype="f32", tree="star", draft_noise=4.0, seed=2)
+    (acc, _, _), _ = _check(w)
+    assert np.any(acc == 0) and np.any(acc == 1)
+
+
+def test_full_size():
+    # the benchmark's shapes: 32 sequences, 63-node binary tree, 128256 bf16
+    w = make_workload("tree_sample63", cache=True)
+    _check(w)
+
+
+def test_chain_tree_equals_chain_sampler():
+    # a chain of gamma drafts as a tree: node i+1 carries draft i, its test
+    # takes the chain's u_i, the final draw u_gamma
+    for dt, V, g in (("bf16", 128256, 7), ("f32", 1001, 5)):
+        wl = make_workload("b64g7v128k", B=16, gamma=g, V=V, dtype=dt, seed=V)
+        B = wl["B"]
+        pad = np.zeros_like(wl["draft"][:, :1])
+        wt = dict(dtype=dt, B=B, N=g + 1, V=V, temperature=wl["temperature"], target=wl["target"],
+                  draft=np.concatenate([wl["draft"], pad], axis=1),
+                  node_tokens=np.concatenate([np.zeros((B, 1), np.int32), wl["draft_tokens"]], axis=1),
+                  parent=np.arange(-1, g, dtype=np.int32),
+                  uniforms=np.concatenate([wl["uniforms"][:, g:], wl["uniforms"][:, :g]], axis=1))
+        acc, path, toks = _run(wt)
+        T = float(wl["temperature"])
+        a2, o2 = L.verify_sample(to_dev(wl["target"]), to_dev(wl["draft"]), to_dev(wl["draft_tokens"]),
+                                 to_dev(wl["uniforms"]), T)
+        a2, o2 = a2.cpu().numpy(), o2.cpu().numpy()
+        # the accept tests are the same fp64 computation on the same statistics
+        assert np.array_equal(acc, a2)
+        for b in range(B):
+            assert list(path[b, :acc[b]]) == list(range(1, acc[b] + 1))
+        # final tokens: equal, except at a draw margin of the oracle
+        oacc, oout, infos = oracle.verify_sample(wl["target"], wl["draft"], dt, wl["draft_tokens"],
+                                                 wl["uniforms"], T)
+        res = classify_sample(acc, toks[:, :g + 1], oacc, oout, infos)
+        assert not res["unexplained"] and res["explained"] <= 1, res
+        assert np.sum(toks != o2) <= 1
+
+
+def test_draft_equal_to_target_takes_first_children():
+    w = make_workload("tree_sample63", B=5, N=15, V=3000, dtype="bf16", seed=4)
+    w["draft"] = w["target"].copy()
+    w["uniforms"] = np.minimum(w["uniforms"], np.float32(0.999))
+    acc, path, toks = _run(w)
+    for b in range(5):
+        assert acc[b] == 3 and list(path[b, :3]) == [1, 3, 7]
+        assert list(toks[b, :3]) == [int(w["node_tokens"][b, n]) for n in (1, 3, 7)]
+    _check(w)
+
+
+def test_invalid_trees_and_tokens():
+    w = make_workload("tree_sample63", B=5, N=7, V=100, dtype="f32", seed=5)
+    par = np.broadcast_to(w["parent"], (5, 7)).copy()
+    par[1, 4] = 4                      # not before its child
+    par[2, 0] = 0                      # root with a parent
+    w["parent"] = par
+    w["node_tokens"][3, 6] = 100       # out of range (a leaf that is never tested)
+    w["node_tokens"][4, 1] = -2
+    w["node_tokens"][0, 0] = -7        # the root's token is never read
+    acc, path, toks = _run(w)
+    assert list(acc[1:]) == [-1, -1, -1, -1] and acc[0] >= 0
+    assert np.all(path[1:] == -1) and np.all(toks[1:] == -1)
+    _check(w)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 1), ("bf16", 8), ("f32", 5)])
+def test_edge_shapes(dtype, V):
+    for N, tree in ((1, "binary"), (2, "chain"), (5, "star")):
+        w = make_workload("tree_sample63", B=3, N=N, V=V, dtype=dtype, tree=tree, seed=N * 10 + V)
+        acc, path, toks = _run(w)
+        assert np.all(acc >= 0) and np.all(toks[np.arange(3), acc] >= 0) and np.all(toks[np.arange(3), acc] < V)
+        _check(w)
+
+
+def test_committed_tokens_follow_the_target_law():
+    # 3 i.i.d. siblings under the root (V = 4): the first committed token
+    # must follow p_root whatever the draft; chi-square with 3 degrees of
+    # freedom against the 0.999 quantile (fixed seed)
+    rng = np.random.default_rng(21)
+    B, V, N, T = 120000, 4, 4, 1.0
+    zt = np.array([1.0, 0.2, -0.5, 0.7])
+    zd = np.array([-0.3, 1.1, 0.4, 0.0])
+    q = np.exp(zd / T) / np.exp(zd / T).sum()
+    p = np.exp(zt / T) / np.exp(zt / T).sum()
+    target = np.broadcast_to(zt.astype(np.float32), (B, N, V)).copy()
+    draft = np.broadcast_to(zd.astype(np.float32), (B, N, V)).copy()
+    tokens = np.zeros((B, N), np.int32)
+    tokens[:, 1:] = rng.choice(V, size=(B, N - 1), p=q)
+    w = dict(dtype="f32", B=B, N=N, V=V, temperature=np.float32(T), target=target, draft=draft,
+             node_tokens=tokens, parent=np.array([-1, 0, 0, 0], np.int32),
+             uniforms=rng.random((B, N), dtype=np.float32))
+    acc, path, toks = _run(w)
+    first = toks[:, 0]
+    counts = np.bincount(first, minlength=V)
+    chi2 = float(np.sum((counts - B * p) ** 2 / (B * p)))
+    assert chi2 < 16.27, (counts / B, p, chi2)
+    # and the acceptance rate of the first token equals the exact
+    # multi-draft value: 1 - mass left after three residual steps
+    r, left = p.copy(), 1.0
+    for _ in range(3):
+        res = np.maximum(0.0, r - q)
+        left *= res.sum()
+        r = res / res.sum()
+    rate = float(np.mean(acc >= 1))
+    assert abs(rate - (1.0 - left)) < 4 * np.sqrt(left * (1 - left) / B) + 1e-9, (rate, 1 - left)

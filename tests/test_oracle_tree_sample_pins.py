@@ -144,3 +144,10 @@ def test_invalid_tree():
     d, path, toks, _ = verify_tree_sample_seq(np.zeros((3, 4)), np.zeros((3, 4)), [0, 1, 2], [-1, 2, 0],
                                               [0.5] * 3, 1.0)
     assert d == -1 and path == [] and toks == []
+    # an out-of-range token anywhere below the root, tested or not
+    for bad in (-1, 4):
+        d, path, toks, _ = verify_tree_sample_seq(np.zeros((3, 4)), np.zeros((3, 4)), [7, 1, bad], [-1, 0, 0],
+                                                  [0.5] * 3, 1.0)
+        assert d == -1 and path == [] and toks == []
+    d, _, _, _ = verify_tree_sample_seq(np.zeros((3, 4)), np.zeros((3, 4)), [-5, 1, 3], [-1, 0, 0], [0.5] * 3, 1.0)
+    assert d >= 0                                            # the root's token is never read
