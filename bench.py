@@ -7,8 +7,10 @@ rotates over R >= 4 input replicas (>= 1 GB) so the 256 MB Infinity Cache
 cannot serve them.  Prints ONE JSON line.
 
 Secondary legs (same JSON line, "modes"): greedy verification of the same
-tensors, greedy tree verification (B=32, 63-node binary tree), and the
-EAGLE-style LM-head projection + verification (B=64, gamma=5, d=4096).
+tensors; early-exit sampling; greedy and stochastic tree verification (B=32,
+63-node binary tree); KV-cache compaction to the accepted paths; one EAGLE-2
+tree expansion and the re-ranking into a tree; the EAGLE-style LM-head
+projection + verification (B=64, gamma=5, d=4096).
 """
 import argparse
 import hashlib
@@ -263,6 +265,34 @@ def main():
                                      "frac": round(tbytes / (tms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                      "mean_accept_len": round(tout[0].float().mean().item(), 3)}
         del tt, tt2
+        torch.cuda.empty_cache()
+        # stochastic tree verification: 32 sequences, 63-node binary tree,
+        # target and draft rows bf16, children drawn from their parent's q
+        sw = make_workload("tree_sample63", cache=True)
+        st_, sd_ = d(sw["target"]), d(sw["draft"])
+        sn, sp, su = d(sw["node_tokens"]), d(sw["parent"]), d(sw["uniforms"])
+        sws = L.new_workspace(L.MODE_TREE_SAMPLE, sw["B"], sw["N"], sw["V"], device=dev)
+        sout = (torch.empty(sw["B"], dtype=torch.int32, device=dev),
+                torch.empty((sw["B"], sw["N"]), dtype=torch.int32, device=dev),
+                torch.empty((sw["B"], sw["N"]), dtype=torch.int32, device=dev))
+        sT = float(sw["temperature"])
+
+        def sstep(i):
+            L.verify_tree_sample(st_, sd_, sn, sp, su, sT, ws=sws, out=sout)
+
+        for i in range(args.warmup):
+            sstep(i)
+        sms = time_events(sstep, args.steps, stream)
+        # the verifier reads a swept prefix of nodes plus the nodes its walks
+        # visit; full_sweep_equiv_GBs is the rate a sweep of every node's two
+        # rows would need to finish in the same time
+        sbytes = 2 * sw["B"] * sw["N"] * sw["V"] * 2
+        modes["tree_sample_b32n63v128k"] = {
+            "ms": round(sms, 5), "sequences_per_s": round(sw["B"] / (sms * 1e-3), 1),
+            "full_sweep_equiv_GBs": round(sbytes / (sms * 1e-3) / 1e9, 1),
+            "mean_accept_len": round(sout[0].float().mean().item(), 3),
+            "max_accept_len": int(sout[0].max().item())}
+        del st_, sd_, sws
         torch.cuda.empty_cache()
         # KV compaction to the paths the tree verifier accepted: a cache of
         # 32 layers x (K, V) planes of 8 heads x 128 bf16 per entry

@@ -86,7 +86,8 @@ typedef enum {
   SPEC_MODE_LMHEAD = 3,   /* lmhead_verify:      gamma_or_N = gamma, d     */
   SPEC_MODE_ROWSTATS = 4, /* spec_row_stats / spec_probe_probs: B = rows   */
   SPEC_MODE_TREE_EXPAND = 5, /* spec_tree_expand:  gamma_or_N = K_in       */
-  SPEC_MODE_TREE_SAMPLE = 6  /* spec_verify_tree_sample: gamma_or_N = N    */
+  SPEC_MODE_TREE_SAMPLE = 6  /* spec_verify_tree_sample: gamma_or_N = N,
+                                d = n_sweep                               */
 } spec_mode;
 
 /* Limits checked by every entry point. */
@@ -99,8 +100,10 @@ typedef enum {
 #define SPEC_MAX_BUILD_NODES 2048 /* node-table entries and tree size (build) */
 
 /* Bytes of workspace the call of the given mode needs for these sizes
- * (0 when an argument is out of range).  d is used by SPEC_MODE_LMHEAD only.
- * The LMHEAD workspace holds the float32 logits of all B(2*gamma+1) rows. */
+ * (0 when an argument is out of range).  d is the feature width for
+ * SPEC_MODE_LMHEAD and the call's n_sweep for SPEC_MODE_TREE_SAMPLE; other
+ * modes ignore it.  The LMHEAD workspace holds the float32 logits of all
+ * B(2*gamma+1) rows. */
 size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d);
 
 /* Zero-fill a workspace (a device fill kernel; graph-capture safe).  Not
@@ -245,12 +248,19 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * (inverse CDF in vocabulary order, as in spec_verify_sample).
  *
  * target_logits, draft_logits [B, N, V] (dt): row n of each belongs to node
- *               n; draft row n is the law n's children were drawn from (the
- *               rows of leaves are read but their values never matter).
+ *               n; draft row n is the law n's children were drawn from.
+ *               Only the rows of nodes the walk reaches are read: the target
+ *               row of every visited node, the draft row of every visited
+ *               node with children.
  * node_tokens   [B, N] int32 (node 0's token is not read).
  * parent        [N] (parent_batch_stride = 0) or [B, N] (= N): parent[0] = -1
  *               and 0 <= parent[n] < n.
  * uniforms      [B, N] float32 in [0, 1).
+ * n_sweep       nodes 0 .. n_sweep-1 of every sequence have both rows swept
+ *               across the whole GPU before the walk; deeper visited nodes
+ *               are reduced on demand by their sequence's workgroup.  -1
+ *               picks the prefix from B, N and V.  Outputs do not depend on
+ *               it (both reductions give the same bits); -1 <= n_sweep <= N.
  * accept_len [B] out: number of accepted nodes; -1 when the tree is invalid
  *            or a token of a node n >= 1 lies outside [0, V) (outputs -1).
  * out_path   [B, N] out: accepted nodes (root excluded) in root-to-leaf
@@ -258,13 +268,13 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * out_tokens [B, N] out: their tokens, then the drawn token, then -1.
  * 1 <= N <= SPEC_MAX_TREE_NODES, 1 <= V <= SPEC_MAX_SAMPLE_VOCAB.
  * Logit pointers 16-byte aligned, the others 4-byte aligned.
- * Workspace: spec_workspace_bytes(SPEC_MODE_TREE_SAMPLE, B, N, V, 0).
+ * Workspace: spec_workspace_bytes(SPEC_MODE_TREE_SAMPLE, B, N, V, n_sweep).
  */
 spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits,
                                     spec_dtype dt, const int32_t* node_tokens,
                                     const int32_t* parent, int parent_batch_stride,
                                     const float* uniforms, int B, int N, int V,
-                                    float temperature, int32_t* accept_len,
+                                    float temperature, int n_sweep, int32_t* accept_len,
                                     int32_t* out_path, int32_t* out_tokens, void* ws,
                                     size_t ws_bytes, hipStream_t s);
 

@@ -37,8 +37,8 @@ _SIGS = {
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz,
-                                     _vp]),
+    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
+                                     _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
@@ -176,9 +176,12 @@ def verify_tree(target, node_tokens, parent, ws=None, out=None):
     return out
 
 
-def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None):
+def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None, n_sweep=-1):
     """target, draft [B, N, V]; node_tokens [B, N]; parent [N] or [B, N];
-    uniforms [B, N] -> (accept_len, out_path, out_tokens)."""
+    uniforms [B, N] -> (accept_len, out_path, out_tokens).  n_sweep: nodes
+    whose rows are swept before the walk (-1: automatic); a workspace passed
+    in must be sized with the same n_sweep (new_workspace(MODE_TREE_SAMPLE,
+    B, N, V, n_sweep))."""
     B, N, V = target.shape
     if tuple(draft.shape) != (B, N, V) or dtype_code(draft) != dtype_code(target):
         raise ValueError("draft must match target in shape and dtype")
@@ -188,10 +191,11 @@ def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature
         out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
                torch.empty((B, N), dtype=torch.int32, device=dev))
     acc, path, toks = out
-    w = _workspace(MODE_TREE_SAMPLE, B, N, V, 0, dev, ws)
+    w = _workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep, dev, ws)
     _check(lib.spec_verify_tree_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(node_tokens),
                                        _ptr(parent), stride, _ptr(uniforms), B, N, V, float(temperature),
-                                       _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
+                                       int(n_sweep), _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
+                                       _stream(dev)),
            "spec_verify_tree_sample")
     return out
 

@@ -31,6 +31,20 @@ struct Layout {
   int nseg, nseg2;
 };
 
+// Nodes whose rows the tree sampler sweeps before its walk.  n_sweep >= 0
+// is the caller's choice (at most N); -1 picks as many leading nodes as fit
+// about kTreePresweepBytes of target and draft rows, the point where sweeping
+// a prefix node for every sequence costs about what one on-demand visit of a
+// node costs a walk (a single CU reduces one node's two rows).
+constexpr long long kTreePresweepBytes = 160LL << 20;
+
+long long tree_presweep_nodes(long long B, long long N, long long V, int dt, long long n_sweep) {
+  if (n_sweep >= 0) return n_sweep < N ? n_sweep : N;
+  const long long pair = 2 * V * (dt == DT_BF16 ? 2 : 4);
+  const long long n = kTreePresweepBytes / (B * pair);
+  return n < N ? n : N;
+}
+
 // dt = element type of the rows the sweep reads (the sweep's segment count
 // depends on it); the public size query takes the larger (fp32) layout.
 bool make_layout(int mode, long long B, long long gN, long long V, long long d, int dt, Layout* L) {
@@ -52,10 +66,20 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
       if (gN < 1 || gN > SPEC_MAX_TREE_NODES) return false;
       rows = B * gN;
       break;
-    case SPEC_MODE_TREE_SAMPLE:
-      if (gN < 1 || gN > SPEC_MAX_TREE_NODES) return false;
-      rows = 2 * B * gN;
+    case SPEC_MODE_TREE_SAMPLE: {
+      // the walk's per-sequence partials of one target and one draft row,
+      // then those of the swept prefix (d carries the call's n_sweep); sized
+      // for whichever element type needs more
+      if (gN < 1 || gN > SPEC_MAX_TREE_NODES || d < -1 || d > gN) return false;
+      long long pre = 0;
+      for (int t = 0; t < 2; ++t) {
+        const long long need =
+            2 * B * tree_presweep_nodes(B, gN, V, t, d) * row_sweep_shape((int)V, t).nseg;
+        if (need > pre) pre = need;
+      }
+      rows = 2 * B + (pre + row_sweep_shape((int)V, DT_F32).nseg - 1) / row_sweep_shape((int)V, DT_F32).nseg;
       break;
+    }
     case SPEC_MODE_ROWSTATS:
       rows = B;
       break;
@@ -66,6 +90,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
     if (d < 64 || d % 64 != 0 || d > (1 << 20)) return false;
     dt = DT_F32;
   }
+  if (mode == SPEC_MODE_TREE_SAMPLE) dt = DT_F32;
   const RowSweepShape sh = row_sweep_shape((int)V, dt);
   int seg_elems = 0;
   const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
@@ -388,7 +413,7 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
 
 spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
                                     const int32_t* node_tokens, const int32_t* parent, int parent_batch_stride,
-                                    const float* uniforms, int B, int N, int V, float temperature,
+                                    const float* uniforms, int B, int N, int V, float temperature, int n_sweep,
                                     int32_t* accept_len, int32_t* out_path, int32_t* out_tokens, void* ws,
                                     size_t ws_bytes, hipStream_t s) {
   if (!dtype_ok(dt)) return SPEC_EDTYPE;
@@ -396,6 +421,7 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
       !row_bytes_ok(V, dt))
     return SPEC_EINVAL;
   if (parent_batch_stride != 0 && parent_batch_stride != N) return SPEC_EINVAL;
+  if (n_sweep < -1 || n_sweep > N) return SPEC_EINVAL;
   if (!target_logits || !draft_logits || !node_tokens || !parent || !uniforms || !accept_len || !out_path ||
       !out_tokens)
     return SPEC_EINVAL;
@@ -406,12 +432,10 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   TempConst tc;
   if (!temp_const(temperature, &tc)) return SPEC_EINVAL;
   Layout L;
-  if (!make_layout(SPEC_MODE_TREE_SAMPLE, B, N, V, 0, DT_F32, &L)) return SPEC_EINVAL;
+  if (!make_layout(SPEC_MODE_TREE_SAMPLE, B, N, V, n_sweep, DT_F32, &L)) return SPEC_EINVAL;
   const spec_status w = check_ws(ws, ws_bytes, L);
   if (w != SPEC_OK) return w;
-  const long long rows = (long long)B * N;
-  hipError_t e = row_sweep(target_logits, rows, draft_logits, rows, V, (int)dt, 1, tc, ws, L, s);
-  if (e != hipSuccess) return SPEC_EHIP;
+  const RowSweepShape sh = row_sweep_shape(V, (int)dt);
   TreeSampleParams p;
   p.tgt = target_logits;
   p.drf = draft_logits;
@@ -423,8 +447,11 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   p.N = N;
   p.V = V;
   p.tc = tc;
-  p.part = at<Partial>(ws, L.part);
-  p.nseg_rows = row_sweep_shape(V, (int)dt).nseg;
+  p.nseg = sh.nseg;
+  p.seg_vecs = sh.seg_vecs;
+  p.n_pre = (int)tree_presweep_nodes(B, N, V, (int)dt, n_sweep);
+  p.ws_part = at<Partial>(ws, L.part);
+  p.pre_part = p.ws_part + 2LL * B * sh.nseg;
   p.accept_len = accept_len;
   p.out_path = out_path;
   p.out_tokens = out_tokens;

@@ -29,6 +29,7 @@
 // release/acquire per workgroup costs an L2 write-back and invalidate on
 // this part, so partials are merged after the kernel boundary.
 #include "sv_kernels.hpp"
+#include "sweep_segment.hpp"
 
 #include <limits.h>
 
@@ -36,23 +37,17 @@ namespace sv {
 
 namespace {
 
-#ifndef SV_SWEEP_VPT
-#define SV_SWEEP_VPT 8
-#endif
-constexpr int kVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segment
+constexpr int kVPT = kSweepVPT;   // 16-byte vectors per lane per segment
 
 // STEPNP > 0: one early-exit step (see launch_row_step); STEPNP is the lane
 // group the draw kernel merges a row's partials with, so the step's accept
 // test reproduces the draw's decision bit for bit.
 template <int DT, int WANT, int STEPNP = 0>
 __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
-  constexpr int ES = DT == DT_BF16 ? 2 : 4;
-  constexpr int EPV = 16 / ES;
   __shared__ float sh_m[kBlock / kWave];
   __shared__ double sh_s[kBlock / kWave];
   __shared__ int sh_a[kBlock / kWave];
   __shared__ int sh_alive;
-  const float NEG_INF = -__builtin_huge_valf();
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const long long unit = blockIdx.x;
@@ -104,16 +99,6 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   const bool second = r >= P.rows0;
   const char* base = static_cast<const char*>(second ? P.src1 : P.src0);
   const long long rr = second ? r - P.rows0 : r;
-  const long long V = P.V;
-  const long long e0 = rr * V, e1 = e0 + V;
-  const long long vfirst = (e0 + EPV - 1) / EPV;   // first whole vector of the row
-  const long long vlast = e1 / EPV;                // one past the last whole vector
-  const long long vs = vfirst + (long long)s * P.seg_vecs;
-  long long ve = vs + P.seg_vecs;
-  if (ve > vlast) ve = vlast;
-  const int nv = ve > vs ? (int)(ve - vs) : 0;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base + vs * 16, (uint32_t)nv * 16u);
-
   // the drafted token of this row, if the caller asked for the gather
   long long gx = -1;
   if (P.gather_tokens != nullptr) {
@@ -121,139 +106,12 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
     const long long b = rr / g1, i = rr - b * g1;
     if (i < P.gather_g) {
       const int x = P.gather_tokens[b * P.gather_g + i];
-      if (x >= 0 && (long long)x < V) gx = x;
+      if (x >= 0 && (long long)x < P.V) gx = x;
     }
   }
-
-  v4i raw[kVPT];
-  if (nv > 0) {
-#pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
-      const int q = min(k * kBlock + tid, nv - 1);
-      raw[k] = load16(rsrc, (uint32_t)q * 16u);
-    }
-  }
-  const int neg_pat = DT == DT_BF16 ? (int)0xff80ff80u : (int)0xff800000u;
-#pragma unroll
-  for (int k = 0; k < kVPT; ++k) {
-    if ((k + 1) * kBlock > nv) {            // uniform: only the tail vectors
-      const bool valid = k * kBlock + tid < nv;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) raw[k][q] = valid ? raw[k][q] : neg_pat;
-    }
-  }
-  // Row head / tail elements outside whole vectors (segment 0, wave 0).
-  float ze = NEG_INF;
-  int ie = INT_MAX;
-  if (s == 0 && tid < 2 * EPV) {
-    const long long he = e1 < vfirst * EPV ? e1 : vfirst * EPV;
-    const long long tb = (vlast > vfirst ? vlast : vfirst) * EPV;
-    long long e = -1;
-    if (tid < EPV) {
-      if (e0 + tid < he) e = e0 + tid;
-    } else {
-      if (tb + (tid - EPV) < e1) e = tb + (tid - EPV);
-    }
-    if (e >= 0) {
-      ze = load_elem<DT>(base, e);
-      ie = (int)(e - e0);
-    }
-  }
-  // row-local index of element i of this lane's vector k: lane_base + k*kBlock*EPV + i
-  const int lane_base = (int)((vs + tid) * EPV - e0);
-
-  // pick out z[x] if x lies in this segment's whole vectors or edge elements
-  if (gx >= 0) {
-    const long long gv = (e0 + gx) / EPV;    // vector holding element x
-    if (gv >= vs && gv < ve) {
-      const int q = (int)(gv - vs);
-      if ((q & (kBlock - 1)) == tid) {
-        const int kk = q / kBlock;
-        const int ii = (int)((e0 + gx) - gv * EPV);
-        float zz = 0.f;
-#pragma unroll
-        for (int k = 0; k < kVPT; ++k) {
-          if (k == kk) {
-            float z[EPV];
-            unpack<DT>(raw[k], z);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i)
-              if (i == ii) zz = z[i];
-          }
-        }
-        P.gather_out[r] = zz;
-      }
-    }
-    if (ie == (int)gx) P.gather_out[r] = ze;
-  }
-
-  // workgroup max: every wave's max through LDS (one barrier)
-  float m = ze;
-#pragma unroll
-  for (int k = 0; k < kVPT; ++k) {
-    float z[EPV];
-    unpack<DT>(raw[k], z);
-#pragma unroll
-    for (int i = 0; i < EPV; ++i) m = fmaxf(m, z[i]);
-  }
-  const float Mw = wave_max(m);
-  if (lane == 0) sh_m[wid] = Mw;
-  __syncthreads();
-  float M = sh_m[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / kWave; ++w) M = fmaxf(M, sh_m[w]);
-
-  int idx = INT_MAX;
-  if constexpr ((WANT & 2) != 0) {
-    if (M != NEG_INF && Mw == M) {          // uniform per wave
-#pragma unroll
-      for (int k = kVPT - 1; k >= 0; --k) {
-        float z[EPV];
-        unpack<DT>(raw[k], z);
-#pragma unroll
-        for (int i = EPV - 1; i >= 0; --i)
-          if (z[i] == M) idx = lane_base + k * kBlock * EPV + i;
-      }
-      if (ze == M) idx = min(idx, ie);
-      idx = wave_min(idx);
-    }
-  }
-
-  double S = 0.0;
-  float K = 0.f;
-  if constexpr ((WANT & 1) != 0) {
-    if (M != NEG_INF) {
-      const float c_hi = P.tc.c_hi, c_lo = P.tc.c_lo;
-      K = M * c_hi;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < kVPT; ++k) {
-        float z[EPV];
-        unpack<DT>(raw[k], z);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-          const float a = fmaf(z[i], c_lo, fmaf(z[i], c_hi, -K));
-          acc[i & 3] += __builtin_amdgcn_exp2f(a);
-        }
-      }
-      acc[0] += __builtin_amdgcn_exp2f(fmaf(ze, c_lo, fmaf(ze, c_hi, -K)));
-      S = wave_sum(((double)acc[0] + (double)acc[1]) + ((double)acc[2] + (double)acc[3]));
-    }
-  }
-  if (lane == 0) {
-    sh_s[wid] = S;
-    sh_a[wid] = idx;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    Partial pp;
-    pp.m = M;
-    pp.arg = min(min(sh_a[0], sh_a[1]), min(sh_a[2], sh_a[3]));
-    pp.K = K;
-    pp.pad_ = 0.f;
-    pp.s = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
-    P.part[r * P.nseg + s] = pp;
-  }
+  const Partial pp = sweep_segment<DT, WANT>(base, rr, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a, gx,
+                                             P.gather_out != nullptr ? P.gather_out + r : nullptr);
+  if (tid == 0) P.part[r * P.nseg + s] = pp;
 }
 
 // One wave per row: merge the row's segment partials.

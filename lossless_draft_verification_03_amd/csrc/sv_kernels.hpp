@@ -195,9 +195,8 @@ hipError_t launch_tree_build(const TreeBuildParams& p, hipStream_t s);
 constexpr int kTreeMaxNodes = 4096;           // nodes per tree (verification calls)
 constexpr long long kMaxSampleVocab = 1LL << 25;
 
-// One workgroup per sequence walks its tree after the row sweep over the
-// 2 B N rows (target rows, then draft rows), merging the partials of the
-// rows it visits.
+// One workgroup per sequence walks its tree, computing the row statistics of
+// the nodes it visits on the way (the rows of other nodes are never read).
 struct TreeSampleParams {
   const void* tgt;         // [B, N, V] target rows of the nodes
   const void* drf;         // [B, N, V] draft rows (row n: the law n's children were drawn from)
@@ -207,8 +206,11 @@ struct TreeSampleParams {
   const float* unif;       // [B, N]: u[b][n] tests node n, u[b][0] is the final draw
   int B, N, V;
   TempConst tc;
-  const Partial* part;     // [2 B N][nseg_rows] sweep partials
-  int nseg_rows;
+  int nseg;                // row sweep segments per row (row_sweep_shape)
+  int seg_vecs;
+  int n_pre;               // nodes 0 .. n_pre-1 have their rows swept before the walk
+  Partial* pre_part;       // [2 B n_pre][nseg]: target rows (b, n), then draft rows (b, n)
+  Partial* ws_part;        // [B][2 nseg] partials of the walk, used when nseg exceeds the LDS slots
   int32_t* accept_len;     // [B]
   int32_t* out_path;       // [B, N]
   int32_t* out_tokens;     // [B, N]

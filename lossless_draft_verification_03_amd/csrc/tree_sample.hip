@@ -26,15 +26,29 @@
 // residual is a draw row with rho = c S_t / S_d.  A zero W (impossible in
 // exact arithmetic after a rejection) leaves (c, W) unchanged.
 //
-// k_tree_walk: one 1024-thread workgroup per sequence after the row sweep.
-// It stages the tree in LDS, validates it, gathers every node's token logit
-// from its parent's target and draft rows (one round trip for the whole
-// tree), then walks from the root: merge the node's two row statistics
-// from the sweep's partials, list its children in index order (block scan),
-// test them; a rejection followed by another child costs one pass over the
-// node's two rows for W; the final draw is one pass for the segment masses,
-// then the inverse CDF inside the segment that holds u[0] * total.
+// k_tree_presweep (optional): the rows of the first n_pre nodes of every
+// sequence, one row segment per workgroup across the whole chip.
+// k_tree_walk: one 1024-thread workgroup per sequence.  Beyond the swept
+// prefix only the rows of the nodes the walk visits are read: the
+// verification needs p at every visited node and q at every visited node
+// with children, nothing else.  One CU reduces such a node's two rows in
+// about the time the whole chip sweeps a few dozen rows, so the prefix (the
+// shallow nodes, which most walks pass through) is swept up front and deeper
+// nodes on demand; both use the row sweep's segment reduction, so the
+// statistics, and the outputs, do not depend on n_pre.  The workgroup stages
+// the tree in LDS, validates it and gathers every node's token logit from its
+// parent's target
+// and draft rows (one round trip for the whole tree), then walks from the
+// root.  At each node: list its children in index order (block scan);
+// compute the max and exponential sum of the node's target row (and of its
+// draft row if it has children) with the row sweep's segment reduction, four
+// segments at a time (one per 256-thread quarter), merged in fp64 exactly as
+// the chain sampler merges them; test the children.  A rejection followed by
+// another child costs one pass over the node's two rows for W; the final
+// draw is one pass for the segment masses, then the inverse CDF inside the
+// segment that holds u[0] * total.
 #include "sv_kernels.hpp"
+#include "sweep_segment.hpp"
 
 #include <limits.h>
 
@@ -52,6 +66,8 @@ constexpr int walk_run() { return DT == DT_BF16 ? 32 : 16; }
 template <int DT>
 constexpr int walk_seg() { return kTB * walk_run<DT>(); }
 constexpr int kTChunk = 16;                // segments per LDS reduction round
+constexpr int kTQuarters = kTB / kBlock;   // row sweep segments reduced at once
+constexpr int kTLdsPart = 64;              // sweep partials per row kept in LDS
 constexpr int kTPer = kTreeMaxNodes / kTB; // nodes per thread in the child scan
 constexpr int kTMaxSeg = (int)(((long long)kMaxSampleVocab + kTB * 16 - 1) / (kTB * 16));
 static_assert(kTreeMaxNodes % kTB == 0, "child scan covers the node range exactly");
@@ -64,6 +80,10 @@ struct WalkLds {
   float gd[kTreeMaxNodes];   // draft logit of the same
   int kids[kTreeMaxNodes];   // children of the current node, index order
   double seg[kTMaxSeg];      // segment masses of the last pass
+  Partial part[2 * kTLdsPart];
+  float qm[kTQuarters][kBlock / kWave];
+  double qs[kTQuarters][kBlock / kWave];
+  int qa[kTQuarters][kBlock / kWave];
   double red[kTChunk * kTW];
   double wtot[kTW];
   int wcnt[kTW];
@@ -279,6 +299,28 @@ __device__ __forceinline__ void set_rho(DrawRow& R, double c, double St, double 
   R.rho_lo = (float)(rho - (double)R.rho_hi);
 }
 
+// Rows of the first n_pre nodes of every sequence, swept up front across the
+// whole chip (one segment per workgroup, the row sweep's reduction).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_presweep(TreeSampleParams P) {
+  __shared__ float sh_m[kBlock / kWave];
+  __shared__ double sh_s[kBlock / kWave];
+  __shared__ int sh_a[kBlock / kWave];
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const long long unit = blockIdx.x;
+  const long long row = unit / P.nseg;
+  const int s = (int)(unit - row * P.nseg);
+  const long long half = (long long)P.B * P.n_pre;
+  const bool drow = row >= half;
+  const long long rl = drow ? row - half : row;
+  const long long b = rl / P.n_pre, n = rl - b * P.n_pre;
+  const char* base = static_cast<const char*>(drow ? P.drf : P.tgt);
+  const Partial pp = sweep_segment<DT, 1>(base, b * P.N + n, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a,
+                                          -1, nullptr);
+  if (tid == 0) P.pre_part[row * P.nseg + s] = pp;
+}
+
 template <int DT, bool ALIGNED, int NP>
 __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
@@ -326,19 +368,10 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
   int n = 0, d = 0;
   DrawRow R;
   double c_fb = 0.0;                          // the law to fall back to if the draw row has no mass
+  const int nseg = P.nseg;
+  Partial* part = nseg <= kTLdsPart ? L.part : P.ws_part + (long long)b * 2 * nseg;
+  const int q = wid / (kBlock / kWave), tq = tid & (kBlock - 1), wq = wid & (kBlock / kWave - 1);
   for (;;) {
-    // statistics of node n's target (wave 0) and draft (wave 1) rows
-    if (wid < 2) {
-      const long long r = (wid == 0 ? 0 : (long long)P.B * N) + row0 + n;
-      float M;
-      double S;
-      int a;
-      merge_partials<1, NP>(P.part + r * P.nseg_rows, P.nseg_rows, P.tc, lane & (NP - 1), &M, &S, &a);
-      if (lane == 0) {
-        L.M[wid] = M;
-        L.S[wid] = S;
-      }
-    }
     // children of n in index order: block scan over kTPer nodes per thread
     int flag[kTPer];
     int cnt = 0;
@@ -365,6 +398,33 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
 #pragma unroll
     for (int j = 0; j < kTPer; ++j)
       if (flag[j]) L.kids[pos++] = tid * kTPer + j;
+    // segment partials of node n's target row, and of its draft row if it
+    // has children: swept up front for n < n_pre, else here, kTQuarters
+    // segments per round, one per quarter (a quarter past the last unit
+    // reduces an empty segment, with no loads)
+    const bool pre = n < P.n_pre;
+    const int units = pre ? 0 : nseg * (nk > 0 ? 2 : 1);
+    for (int u0 = 0; u0 < units; u0 += kTQuarters) {
+      const int u = u0 + q;
+      const bool drow = u >= nseg && u < units;
+      const int s = u < units ? (drow ? u - nseg : u) : nseg;
+      const Partial pp = sweep_segment<DT, 1>(drow ? drf : tgt, row0 + n, V, s, P.seg_vecs, P.tc, tq, wq, L.qm[q],
+                                              L.qs[q], L.qa[q], -1, nullptr);
+      if (tq == 0 && u < units) part[u] = pp;
+    }
+    __syncthreads();
+    if (wid < 2 && (wid == 0 || nk > 0)) {
+      float M;
+      double S;
+      int a;
+      const Partial* src = part + wid * nseg;
+      if (pre) src = P.pre_part + ((wid == 0 ? 0 : (long long)P.B * P.n_pre) + (long long)b * P.n_pre + n) * nseg;
+      merge_partials<1, NP>(src, nseg, P.tc, lane & (NP - 1), &M, &S, &a);
+      if (lane == 0) {
+        L.M[wid] = M;
+        L.S[wid] = S;
+      }
+    }
     __syncthreads();
     const float Mt = L.M[0], Md = L.M[1];
     const double St = L.S[0], Sd = L.S[1];
@@ -434,13 +494,18 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
 
 template <int DT, bool ALIGNED, int NP>
 hipError_t launch_walk_np(const TreeSampleParams& p, hipStream_t s) {
+  if (p.n_pre > 0) {
+    const long long grid = 2LL * p.B * p.n_pre * p.nseg;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_tree_presweep<DT>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+  }
   hipLaunchKernelGGL((k_tree_walk<DT, ALIGNED, NP>), dim3((unsigned)p.B), dim3(kTB), 0, s, p);
   return hipGetLastError();
 }
 
 template <int DT, bool ALIGNED>
 hipError_t launch_walk_t(const TreeSampleParams& p, hipStream_t s) {
-  switch (merge_group(p.nseg_rows)) {
+  switch (merge_group(p.nseg)) {
     case 1: return launch_walk_np<DT, ALIGNED, 1>(p, s);
     case 2: return launch_walk_np<DT, ALIGNED, 2>(p, s);
     case 4: return launch_walk_np<DT, ALIGNED, 4>(p, s);
@@ -454,7 +519,8 @@ hipError_t launch_walk_t(const TreeSampleParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_tree_sample(const TreeSampleParams& p, int dt, hipStream_t s) {
-  if (p.B < 1 || p.N < 1 || p.N > kTreeMaxNodes || p.V < 1 || (long long)p.V > kMaxSampleVocab)
+  if (p.B < 1 || p.N < 1 || p.N > kTreeMaxNodes || p.V < 1 || (long long)p.V > kMaxSampleVocab || p.n_pre < 0 ||
+      p.n_pre > p.N)
     return hipErrorInvalidValue;
   const bool aligned = dt == DT_BF16 ? (p.V % 8 == 0) : (p.V % 4 == 0);
   if (dt == DT_BF16) return aligned ? launch_walk_t<DT_BF16, true>(p, s) : launch_walk_t<DT_BF16, false>(p, s);

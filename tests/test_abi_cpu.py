@@ -162,20 +162,25 @@ def test_tree_sample_rejects_invalid_arguments():
     fn = L.lib.spec_verify_tree_sample
 
     def call(**kw):
-        a = dict(t=FAKE, d=FAKE, dt=1, tok=FAKE, par=FAKE, ps=0, u=FAKE, B=2, N=15, V=1000, T=0.7, acc=FAKE,
-                 path=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
+        a = dict(t=FAKE, d=FAKE, dt=1, tok=FAKE, par=FAKE, ps=0, u=FAKE, B=2, N=15, V=1000, T=0.7, ns=-1,
+                 acc=FAKE, path=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
         a.update(kw)
         return fn(a["t"], a["d"], a["dt"], a["tok"], a["par"], a["ps"], a["u"], a["B"], a["N"], a["V"], a["T"],
-                  a["acc"], a["path"], a["out"], a["ws"], a["wsb"], None)
+                  a["ns"], a["acc"], a["path"], a["out"], a["ws"], a["wsb"], None)
     assert call(dt=3) == 2
     assert call(B=0) == 1 and call(N=0) == 1 and call(N=4097) == 1 and call(V=0) == 1
     assert call(V=(1 << 25) + 1) == 1
     assert call(ps=7) == 1                                           # parent stride must be 0 or N
+    assert call(ns=-2) == 1 and call(ns=16) == 1                     # -1 <= n_sweep <= N
     assert call(T=0.0) == 1 and call(T=float("nan")) == 1
     assert call(d=None) == 1 and call(u=None) == 1 and call(path=None) == 1
     assert call(t=FAKE + 8) == 3 and call(d=FAKE + 4) == 3 and call(u=FAKE + 2) == 3
     assert call(ws=None) == 4 and call(ws=FAKE + 16) == 4 and call(wsb=1024) == 4
-    sz = L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256)
+    sz = L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, -1)
     assert sz > 0 and sz % 256 == 0
-    assert sz >= L.workspace_bytes(L.MODE_TREE, 64, 63, 128256)     # 2 B N rows of statistics
+    assert sz >= 2 * 32 * 8 * 24                                     # partials of 2 rows per sequence
+    full = L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, 63)
+    assert full >= 2 * 32 * 63 * 8 * 24 and full >= sz                # every node swept up front
+    assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, 0) <= sz
+    assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, 64) == 0
     assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 4097, 1000) == 0

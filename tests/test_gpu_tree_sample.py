@@ -18,11 +18,11 @@ from parity import classify_tree_sample, classify_sample, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, T=None):
+def _run(w, T=None, n_sweep=-1):
     T = float(w["temperature"]) if T is None else T
     acc, path, toks = L.verify_tree_sample(to_dev(w["target"]), to_dev(w["draft"]), to_dev(w["node_tokens"]),
                                            to_dev(np.ascontiguousarray(w["parent"]).astype(np.int32)),
-                                           to_dev(w["uniforms"]), T)
+                                           to_dev(w["uniforms"]), T, n_sweep=n_sweep)
     return acc.cpu().numpy(), path.cpu().numpy(), toks.cpu().numpy()
 
 
@@ -37,8 +37,8 @@ def _parents(w):
     return np.broadcast_to(par, (w["B"], w["N"])) if par.ndim == 1 else par
 
 
-def _check(w, T=None, max_explained=1):
-    g = _run(w, T)
+def _check(w, T=None, max_explained=1, n_sweep=-1):
+    g = _run(w, T, n_sweep)
     o = _oracle(w, T)
     res = classify_tree_sample(*g, o[0], o[1], o[2], o[3], _parents(w))
     assert not res["unexplained"], res["unexplained"]
@@ -60,7 +60,10 @@ def _check(w, T=None, max_explained=1):
 def test_matches_oracle(dtype, V, N, tree, noise, T):
     w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
                       temperature=T, seed=V + N)
-    _check(w)
+    g, _ = _check(w)
+    # the swept prefix changes where the statistics are reduced, not their bits
+    for ns in (0, N // 2, N):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
 
 
 def test_matches_oracle_many_rejections():
@@ -73,7 +76,9 @@ def test_matches_oracle_many_rejections():
 def test_full_size():
     # the benchmark's shapes: 32 sequences, 63-node binary tree, 128256 bf16
     w = make_workload("tree_sample63", cache=True)
-    _check(w)
+    g, _ = _check(w)
+    for ns in (0, 63):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
 
 
 def test_chain_tree_equals_chain_sampler():
