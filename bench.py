@@ -41,7 +41,7 @@ def parse():
 
 def kernel_source_hash():
     h = hashlib.sha1()
-    for f in ("rowstats.hip", "sv_common.hpp", "sv_kernels.hpp"):
+    for f in ("rowstats.hip", "sweep_segment.hpp", "sv_common.hpp", "sv_kernels.hpp"):
         with open(os.path.join(ROOT, "lossless_draft_verification_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -57,7 +57,7 @@ def measured_traffic():
         return None
     if c.get("source_hash") != kernel_source_hash():
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c.get("sweep_hbm_bytes_per_launch")
 
 
 def time_events(fn, n, stream):
@@ -121,15 +121,14 @@ def main():
     value = B * g / (ms * 1e-3)
     accepted = out[0].float().mean().item()
 
-    # dominant kernel alone: the row sweep over the same 960 rows (the same
-    # kernel instance spec_verify_sample launches first)
-    rs_ws = L.new_workspace(L.MODE_ROWSTATS, rows_t + rows_d, 0, V, device=dev)
-    rs_out = (torch.empty(rows_t + rows_d, dtype=torch.float32, device=dev),
-              torch.empty(rows_t + rows_d, dtype=torch.float64, device=dev),
-              torch.empty(rows_t + rows_d, dtype=torch.int32, device=dev))
+    # dominant kernel alone: the row sweep over the same 960 rows, launched
+    # through spec_row_partials (the same kernel instance spec_verify_sample
+    # launches first, with the same segments, writing the same partials)
+    rs_out = torch.empty((rows_t + rows_d, L.lib.spec_row_segments(V, L.SPEC_BF16), 24), dtype=torch.uint8,
+                         device=dev)
 
     def sweep(i):
-        L.row_stats(reps[i % R][0], T, 1, ws=rs_ws, out=rs_out)
+        L.row_partials(reps[i % R][0], T, 1, out=rs_out)
 
     for i in range(args.warmup):
         sweep(i)
@@ -156,7 +155,8 @@ def main():
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "mean_accept_len": round(accepted, 3),
-        "roofline": {"bound": "hbm", "kernel": "spec_row_stats over the 960 rows: k_row_stats<bf16,sum> + k_row_merge", "achieved": round(k1_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_row_sweep<bf16,sum> over the 960 rows (spec_row_partials)",
+                     "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "bytes_per_launch": k1_bytes,
                      "avg_launch_us": round(k1_ms * 1e3, 2)},
@@ -271,7 +271,7 @@ def main():
         sw = make_workload("tree_sample63", cache=True)
         st_, sd_ = d(sw["target"]), d(sw["draft"])
         sn, sp, su = d(sw["node_tokens"]), d(sw["parent"]), d(sw["uniforms"])
-        sws = L.new_workspace(L.MODE_TREE_SAMPLE, sw["B"], sw["N"], sw["V"], device=dev)
+        sws = L.new_workspace(L.MODE_TREE_SAMPLE, sw["B"], sw["N"], sw["V"], -1, device=dev)   # n_sweep -1
         sout = (torch.empty(sw["B"], dtype=torch.int32, device=dev),
                 torch.empty((sw["B"], sw["N"]), dtype=torch.int32, device=dev),
                 torch.empty((sw["B"], sw["N"]), dtype=torch.int32, device=dev))

@@ -135,6 +135,28 @@ spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V,
                            size_t ws_bytes, hipStream_t s);
 
 /*
+ * spec_row_partials -- the pass of spec_row_stats without its merge, for
+ * callers that combine partial statistics themselves (for example the
+ * vocabulary shards of one row held by several GPUs: shard records merge like
+ * the segments of one row).  Pages: as spec_row_stats.
+ *
+ * Each row is cut into spec_row_segments(V, dt) segments; one 24-byte record
+ * per (row, segment), row-major: float m (segment max); int32 arg (lowest
+ * row-local index holding m, INT32_MAX without want & 2); float K; 4 unused
+ * bytes; double s = sum over the segment of 2^(z c - K), c = log2(e)/T (K and
+ * s are 0 without want & 1).  The row's statistics are M = max m,
+ * out_sum = sum s * 2^(K - M c) (in double), argmax = min arg over the
+ * segments whose m equals M.
+ * partials   [rows][nseg] records, 8-byte aligned; partials_bytes must be at
+ *            least rows * nseg * 24.  No workspace.
+ * want, temperature: as in spec_row_stats.
+ */
+int spec_row_segments(int V, spec_dtype dt);
+spec_status spec_row_partials(const void* logits, spec_dtype dt, int rows, int V,
+                              float temperature, int want, void* partials,
+                              size_t partials_bytes, hipStream_t s);
+
+/*
  * spec_verify_sample -- speculative sampling verification of B sequences.
  * Pages: "EAGLE-3 speculative decoding review", "Speculative Decoding"
  * (3. Accept or Reject) and "Does Using a Small Model's Answer Reduce

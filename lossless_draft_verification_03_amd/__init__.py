@@ -28,7 +28,9 @@ from ._binding import (  # noqa: F401
     lmhead_verify,
     new_tree_table,
     new_workspace,
+    PARTIAL_DTYPE,
     probe_probs,
+    row_partials,
     row_stats,
     tree_build,
     tree_expand,

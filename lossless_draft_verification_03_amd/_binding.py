@@ -33,6 +33,8 @@ _SIGS = {
     "spec_workspace_init": (_i, [_vp, _sz, _vp]),
     "spec_status_str": (ctypes.c_char_p, [_i]),
     "spec_row_stats": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_row_segments": (_i, [_i, _i]),
+    "spec_row_partials": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
@@ -81,11 +83,14 @@ def dtype_code(t):
     raise TypeError(f"logits must be float32 or bf16 (bfloat16 / 16-bit bit patterns), got {t.dtype}")
 
 
-def workspace_bytes(mode, B, gamma_or_N, V, d=0):
+def workspace_bytes(mode, B, gamma_or_N, V, d=None):
+    """d: LM-head width (MODE_LMHEAD) or n_sweep (MODE_TREE_SAMPLE, default -1)."""
+    if d is None:
+        d = -1 if mode == MODE_TREE_SAMPLE else 0
     return lib.spec_workspace_bytes(mode, B, gamma_or_N, V, d)
 
 
-def new_workspace(mode, B, gamma_or_N, V, d=0, device="cuda"):
+def new_workspace(mode, B, gamma_or_N, V, d=None, device="cuda"):
     """A zero-filled workspace for one (mode, sizes) layout."""
     n = workspace_bytes(mode, B, gamma_or_N, V, d)
     if n == 0:
@@ -124,6 +129,21 @@ def row_stats(logits, temperature=1.0, want=3, ws=None, out=None):
     _check(lib.spec_row_stats(_ptr(logits), dtype_code(logits), rows, V, float(temperature), want,
                               _ptr(m), _ptr(s) if want & 1 else None, _ptr(a) if want & 2 else None,
                               _ptr(w), w.numel(), _stream(dev)), "spec_row_stats")
+    return out
+
+
+PARTIAL_DTYPE = (("m", "<f4"), ("arg", "<i4"), ("K", "<f4"), ("pad", "<f4"), ("s", "<f8"))
+
+
+def row_partials(logits, temperature=1.0, want=1, out=None):
+    """Per-segment partial records of [rows, V] logits -> uint8 [rows, nseg, 24]
+    (layout PARTIAL_DTYPE; see spec_row_partials)."""
+    rows, V = logits.shape
+    nseg = lib.spec_row_segments(V, dtype_code(logits))
+    if out is None:
+        out = torch.empty((rows, nseg, 24), dtype=torch.uint8, device=logits.device)
+    _check(lib.spec_row_partials(_ptr(logits), dtype_code(logits), rows, V, float(temperature), want, _ptr(out),
+                                 out.numel(), _stream(logits.device)), "spec_row_partials")
     return out
 
 

@@ -313,6 +313,37 @@ spec_status spec_row_stats(const void* logits, spec_dtype dt, int rows, int V, f
   return hip_status(launch_row_stats(p, (int)dt, s));
 }
 
+int spec_row_segments(int V, spec_dtype dt) {
+  if (!dtype_ok(dt) || V < 1) return 0;
+  return row_sweep_shape(V, (int)dt).nseg;
+}
+
+spec_status spec_row_partials(const void* logits, spec_dtype dt, int rows, int V, float temperature, int want,
+                              void* partials, size_t partials_bytes, hipStream_t s) {
+  static_assert(sizeof(Partial) == 24, "partial record layout");
+  if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (rows < 1 || V < 1 || want < 1 || want > 3 || !row_bytes_ok(V, dt)) return SPEC_EINVAL;
+  if (!logits || !partials) return SPEC_EINVAL;
+  if (!aligned(logits, 16) || !aligned(partials, 8)) return SPEC_EALIGN;
+  TempConst tc;
+  memset(&tc, 0, sizeof(tc));
+  if ((want & 1) && !temp_const(temperature, &tc)) return SPEC_EINVAL;
+  const RowSweepShape sh = row_sweep_shape(V, (int)dt);
+  if ((unsigned long long)partials_bytes / sizeof(Partial) / (unsigned long long)sh.nseg < (unsigned long long)rows)
+    return SPEC_EINVAL;
+  RowStatsParams p;
+  memset(&p, 0, sizeof(p));
+  p.src0 = logits;
+  p.rows0 = rows;
+  p.V = V;
+  p.nseg = sh.nseg;
+  p.seg_vecs = sh.seg_vecs;
+  p.want = want;
+  p.tc = tc;
+  p.part = static_cast<Partial*>(partials);
+  return hip_status(launch_row_sweep(p, (int)dt, s));
+}
+
 spec_status spec_verify_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
                                const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
                                int V, float temperature, int32_t* accept_len, int32_t* out_tokens,

@@ -153,6 +153,28 @@ def test_row_stats_vs_oracle(dt, V, T):
         assert abs(s[r] / exact - 1) < 1e-6, (r, s[r], exact)
 
 
+@pytest.mark.parametrize("dt,V", [("bf16", 128256), ("f32", 32000), ("bf16", 777), ("f32", 5)])
+def test_row_partials_merge_to_row_stats(dt, V):
+    # the sweep's per-segment records, merged on the host in float64 as the
+    # header describes, give spec_row_stats' statistics; max and argmax exactly
+    rng = np.random.default_rng(V + 1)
+    rows, T = 9, 0.8
+    z = rng.normal(0, 2, (rows, V)).astype(np.float32)
+    z[2, :] = np.round(z[2, :])
+    arr = f32_to_bf16_bits(z) if dt == "bf16" else z
+    x = to_dev(arr)
+    m, s, a = (t.cpu().numpy() for t in L.row_stats(x, T, 3))
+    rec = L.row_partials(x, T, 3).cpu().numpy().view(np.dtype(list(L.PARTIAL_DTYPE)))[..., 0]
+    assert rec.shape == (rows, L.lib.spec_row_segments(V, 1 if dt == "bf16" else 0))
+    c = math.log2(math.e) / float(np.float32(T))
+    for r in range(rows):
+        M = rec["m"][r].max()
+        S = float(np.sum(rec["s"][r] * np.exp2(rec["K"][r].astype(np.float64) - float(M) * c)))
+        arg = min(int(x) for x, mm in zip(rec["arg"][r], rec["m"][r]) if mm == M)
+        assert M == m[r] and arg == a[r]
+        assert abs(S / s[r] - 1) < 1e-14, (r, S, s[r])
+
+
 def test_probe_probs_within_tolerance():
     rng = np.random.default_rng(11)
     for dt, V, T in (("bf16", 128256, 0.7), ("f32", 32000, 1.0), ("bf16", 777, 1.3)):
