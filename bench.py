@@ -182,21 +182,44 @@ def main():
                                       "frac": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # early-exit verification on the same replicas, then on a batch with
         # low acceptance (draft noise 3.0) against the full sweep
-        def ee_bytes(acc_h):
+        def ee_blocks(K):
+            # the library's blocks: K positions each, or 1, 2, 4, ... for K = 0
+            out, i0, n = [], 0, (K if K > 0 else 1)
+            while i0 <= g:
+                out.append((i0, min(i0 + n, g + 1)))
+                i0, n = min(i0 + n, g + 1), (K if K > 0 else 2 * n)
+            return out
+
+        def ee_bytes(acc_h, K):
+            # a sequence reads a block iff it accepted every position before the
+            # block; a position has a target row and, below gamma, a draft row
             j = np.clip(acc_h, 0, g)
-            return int(((j + 1) + np.minimum(j + 1, g)).sum()) * V * 2
+            rows = 0
+            for i0, i1 in ee_blocks(K):
+                live = j >= i0
+                rows += int(live.sum()) * ((i1 - i0) + (min(i1, g) - min(i0, g)))
+            return rows * V * 2
+        K_auto = 0
 
         eout = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
 
-        def estep(i):
+        def estep(i, K=0):
             _, t, dr = reps[i % R]
-            L.verify_sample(t, dr, x, u, T, ws=ws, out=eout, early_exit=True)
+            L.verify_sample(t, dr, x, u, T, ws=ws, out=eout, early_exit=True, positions_per_launch=K)
 
+        K_half = (g + 2) // 2                  # two launches
         for i in range(args.warmup):
             estep(i)
+            estep(i, 1)
+            estep(i, K_half)
+        ems1 = time_events(lambda i: estep(i, 1), args.steps, stream)
+        emsh = time_events(lambda i: estep(i, K_half), args.steps, stream)
         ems = time_events(estep, args.steps, stream)
-        ee = {"ms": round(ems, 5), "positions_per_s": round(B * g / (ems * 1e-3), 1),
-              "rows_bytes_read": ee_bytes(eout[0].cpu().numpy()), "full_sweep_ms": round(ms, 5)}
+        ee = {"ms": round(ems, 5), "blocks": ee_blocks(K_auto),
+              "positions_per_s": round(B * g / (ems * 1e-3), 1),
+              "rows_bytes_read": ee_bytes(eout[0].cpu().numpy(), K_auto), "full_sweep_ms": round(ms, 5),
+              "ms_one_position_per_launch": round(ems1, 5),
+              f"ms_{K_half}_positions_per_launch": round(emsh, 5)}
         del reps
         torch.cuda.empty_cache()
         wl = make_workload("b64g7v128k", draft_noise=3.0, seed=5)
@@ -208,17 +231,21 @@ def main():
         del lo_base
         lx, lu = d(wl["draft_tokens"]), d(wl["uniforms"])
 
-        def lstep(i, early):
-            L.verify_sample(lo[i % 4][0], lo[i % 4][1], lx, lu, T, ws=ws, out=eout, early_exit=early)
+        def lstep(i, early, K=0):
+            L.verify_sample(lo[i % 4][0], lo[i % 4][1], lx, lu, T, ws=ws, out=eout, early_exit=early,
+                            positions_per_launch=K)
 
         for i in range(args.warmup):
             lstep(i, False)
             lstep(i, True)
+            lstep(i, True, 1)
         lfull = time_events(lambda i: lstep(i, False), args.steps, stream)
+        lee1 = time_events(lambda i: lstep(i, True, 1), args.steps, stream)
         lee = time_events(lambda i: lstep(i, True), args.steps, stream)
         ee["low_acceptance"] = {"draft_noise": 3.0, "mean_accept_len": round(eout[0].float().mean().item(), 3),
                                 "full_sweep_ms": round(lfull, 5), "early_exit_ms": round(lee, 5),
-                                "rows_bytes_read": ee_bytes(eout[0].cpu().numpy())}
+                                "early_exit_ms_one_position_per_launch": round(lee1, 5),
+                                "rows_bytes_read": ee_bytes(eout[0].cpu().numpy(), K_auto)}
         del lo
         torch.cuda.empty_cache()
         # the same low-acceptance sequences tiled to 256 (4x the bytes per position)
@@ -231,14 +258,18 @@ def main():
         ws4 = L.new_workspace(L.MODE_SAMPLE, B4, g, V, device=dev)
         out4 = (torch.empty(B4, dtype=torch.int32, device=dev), torch.empty((B4, g + 1), dtype=torch.int32, device=dev))
 
-        def l4(i, early):
-            L.verify_sample(lo4[i % 2][0], lo4[i % 2][1], x4, u4, T, ws=ws4, out=out4, early_exit=early)
+        def l4(i, early, K=0):
+            L.verify_sample(lo4[i % 2][0], lo4[i % 2][1], x4, u4, T, ws=ws4, out=out4, early_exit=early,
+                            positions_per_launch=K)
 
         for i in range(2):
             l4(i, False)
             l4(i, True)
-        ee["low_acceptance_b256"] = {"full_sweep_ms": round(time_events(lambda i: l4(i, False), 10, stream), 5),
-                                     "early_exit_ms": round(time_events(lambda i: l4(i, True), 10, stream), 5)}
+            l4(i, True, 1)
+        ee["low_acceptance_b256"] = {
+            "full_sweep_ms": round(time_events(lambda i: l4(i, False), 10, stream), 5),
+            "early_exit_ms": round(time_events(lambda i: l4(i, True), 10, stream), 5),
+            "early_exit_ms_one_position_per_launch": round(time_events(lambda i: l4(i, True, 1), 10, stream), 5)}
         modes["early_exit_b64g7v128k"] = ee
         del lo4, ws4
         torch.cuda.empty_cache()

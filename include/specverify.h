@@ -184,24 +184,28 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
 /*
  * spec_verify_sample_early_exit -- spec_verify_sample with the rows swept in
  * position order: target and draft row i of a sequence are read only if its
- * positions 0 .. i-1 were all accepted.
+ * positions before the block holding i were all accepted.
  * Pages: as spec_verify_sample; "EAGLE-3 speculative decoding review",
  * "Speculative Decoding" (3. Accept or Reject: stop at the first rejection
  * and discard every later draft token) -- the rows after a rejection cannot
  * change the outcome, so they need not be read.
  * Same arguments, workspace and outputs as spec_verify_sample, and the same
- * results bit for bit (the per-position test uses the same merged statistics
- * and the same ratio as the final accept scan).  gamma + 1 dependent sweeps
- * replace one: it reads about (1 + E[accept_len]) / (gamma + 1) of the bytes
- * and pays a launch latency per position, so it pays off when acceptance is
- * low.
+ * results bit for bit (the tests between blocks use the same merged
+ * statistics and the same ratio as the final accept scan).
+ * positions_per_launch  K: positions 0..gamma are swept in blocks of K, one
+ *   launch per block; a sequence's next block is read only if every position
+ *   of its earlier blocks was accepted.  K = gamma + 1 is one full sweep.
+ *   Smaller K reads fewer rows and pays one launch latency (about 5 us) per
+ *   block.  0 picks blocks of 1, 2, 4, ... positions: within twice the rows of
+ *   K = 1 whatever the acceptance, in ceil(log2(gamma + 2)) launches.
+ *   0 <= K <= gamma + 1.
  */
 spec_status spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits,
                                           spec_dtype dt, const int32_t* draft_tokens,
                                           const float* uniforms, int B, int gamma, int V,
-                                          float temperature, int32_t* accept_len,
-                                          int32_t* out_tokens, void* ws, size_t ws_bytes,
-                                          hipStream_t s);
+                                          float temperature, int positions_per_launch,
+                                          int32_t* accept_len, int32_t* out_tokens, void* ws,
+                                          size_t ws_bytes, hipStream_t s);
 
 /*
  * spec_verify_greedy -- greedy verification of B sequences.

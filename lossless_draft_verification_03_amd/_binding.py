@@ -36,7 +36,7 @@ _SIGS = {
     "spec_row_segments": (_i, [_i, _i]),
     "spec_row_partials": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
-    "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
@@ -147,10 +147,12 @@ def row_partials(logits, temperature=1.0, want=1, out=None):
     return out
 
 
-def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, out=None, early_exit=False):
+def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, out=None, early_exit=False,
+                  positions_per_launch=0):
     """target [B, g+1, V], draft [B, g, V] -> (accept_len [B], out_tokens [B, g+1]).
-    early_exit: sweep the rows in position order and skip those after a
-    sequence's first rejection (same results)."""
+    early_exit: sweep the rows in blocks of positions_per_launch positions (0:
+    automatic) and skip a sequence's later blocks after a rejection (same
+    results)."""
     B, g1, V = target.shape
     g = g1 - 1
     dev = target.device
@@ -160,9 +162,15 @@ def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, o
         out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g1), dtype=torch.int32, device=dev))
     acc, toks = out
     w = _workspace(MODE_SAMPLE, B, g, V, 0, dev, ws)
-    fn = lib.spec_verify_sample_early_exit if early_exit else lib.spec_verify_sample
-    _check(fn(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens), _ptr(uniforms), B, g, V,
-              float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)), "spec_verify_sample")
+    if early_exit:
+        _check(lib.spec_verify_sample_early_exit(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens),
+                                                 _ptr(uniforms), B, g, V, float(temperature),
+                                                 int(positions_per_launch), _ptr(acc), _ptr(toks), _ptr(w),
+                                                 w.numel(), _stream(dev)), "spec_verify_sample_early_exit")
+    else:
+        _check(lib.spec_verify_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(draft_tokens),
+                                      _ptr(uniforms), B, g, V, float(temperature), _ptr(acc), _ptr(toks), _ptr(w),
+                                      w.numel(), _stream(dev)), "spec_verify_sample")
     return out
 
 

@@ -359,20 +359,27 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
 
 spec_status spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits, spec_dtype dt,
                                           const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
-                                          int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
-                                          void* ws, size_t ws_bytes, hipStream_t s) {
+                                          int V, float temperature, int positions_per_launch, int32_t* accept_len,
+                                          int32_t* out_tokens, void* ws, size_t ws_bytes, hipStream_t s) {
   TempConst tc;
   Layout L;
   const spec_status st = check_sample_args(target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V,
                                            temperature, accept_len, out_tokens, ws, ws_bytes, &tc, &L);
   if (st != SPEC_OK) return st;
+  if (positions_per_launch < 0 || positions_per_launch > gamma + 1) return SPEC_EINVAL;
+  const int K = positions_per_launch;
   RowStatsParams r = sample_sweep_params(target_logits, draft_logits, draft_tokens, B, gamma, V, (int)dt, tc, ws, L);
   r.step_B = B;
   r.step_unif = uniforms;
   r.step_alive = at<int>(ws, L.rarg);  // [B, gamma+1]; the sampler leaves this region unused
-  for (int i = 0; i <= gamma; ++i) {
-    r.step = i;
+  // blocks of K positions, or of 1, 2, 4, ... positions for K = 0
+  for (int i0 = 0, prev = -1, len = K > 0 ? K : 1; i0 <= gamma; len = K > 0 ? K : 2 * len) {
+    r.step = i0;
+    r.step_end = i0 + len < gamma + 1 ? i0 + len : gamma + 1;
+    r.step_prev = prev;
     if (launch_row_step(r, (int)dt, s) != hipSuccess) return SPEC_EHIP;
+    prev = i0;
+    i0 = r.step_end;
   }
   return draw_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc, accept_len,
                  out_tokens, ws, L, s);

@@ -57,43 +57,54 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
     r = unit / P.nseg;
     s = (int)(unit - r * P.nseg);
   } else {
-    // unit -> (sequence b, target or draft row of position i, segment)
-    const int i = P.step, g = P.gather_g;
-    const int per = i < g ? 2 : 1;
+    // unit -> (sequence b, row k of the block, segment); row k is position
+    // step + k/2, target (k even) or draft (k odd); the bonus position g has
+    // a target row only, and it can only be the block's last row
+    const int i0 = P.step, i1 = P.step_end, ip = P.step_prev, g = P.gather_g;
+    const int per = 2 * (i1 - i0) - (i1 > g ? 1 : 0);
     const long long b = unit / (per * P.nseg);
     const int rem = (int)(unit - b * per * P.nseg);
-    const int kind = rem / P.nseg;
-    s = rem - kind * P.nseg;
+    const int k = rem / P.nseg;
+    s = rem - k * P.nseg;
+    const int i = i0 + k / 2, kind = k & 1;
     const long long ab = b * (g + 1);
     r = kind == 0 ? ab + i : P.rows0 + b * g + i;
-    // Row i is needed only if positions 0 .. i-1 were all accepted: the
-    // previous step recorded whether 0 .. i-2 were, and position i-1 is
-    // tested here from its rows' partials and gathered logits.
+    // The block is needed only if positions 0 .. i0-1 were all accepted: the
+    // previous block recorded whether 0 .. ip-1 were, and positions
+    // ip .. i0-1 are tested here from their rows' partials and gathered
+    // logits, one position per group of STEPNP lanes, each group merging as
+    // the draw kernel does.
     if (wid == 0) {
       int al = 1;
-      if (i > 0) {
-        al = P.step_alive[ab + i - 1];
-        const int x = P.gather_tokens[b * g + i - 1];
-        if (al && (x < 0 || x >= P.V)) al = 0;
+      if (ip >= 0) {
+        al = P.step_alive[ab + ip];
         if (al) {
-          float Mt, Md;
-          double St, Sd;
-          int a;
-          merge_partials<1, STEPNP>(P.part + (ab + i - 1) * P.nseg, P.nseg, P.tc, lane & (STEPNP - 1), &Mt, &St,
-                                    &a);
-          merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + i - 1) * P.nseg, P.nseg, P.tc, lane & (STEPNP - 1),
-                                    &Md, &Sd, &a);
-          al = sample_rejects(P.gather_out[ab + i - 1], P.gather_out[P.rows0 + b * g + i - 1], Mt, St, Md, Sd,
-                              P.step_unif[ab + i - 1], P.tc)
-                   ? 0
-                   : 1;
+          constexpr int G = kWave / STEPNP;
+          const int gq = lane / STEPNP, gl = lane & (STEPNP - 1);
+          for (int c0 = ip; c0 < i0; c0 += G) {
+            const int ii = c0 + gq;
+            const bool live = ii < i0;        // uniform per lane group
+            bool rej = false;
+            if (live) {
+              const int x = P.gather_tokens[b * g + ii];
+              float Mt, Md;
+              double St, Sd;
+              int a;
+              merge_partials<1, STEPNP>(P.part + (ab + ii) * P.nseg, P.nseg, P.tc, gl, &Mt, &St, &a);
+              merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + ii) * P.nseg, P.nseg, P.tc, gl, &Md, &Sd, &a);
+              rej = x < 0 || x >= P.V ||
+                    sample_rejects(P.gather_out[ab + ii], P.gather_out[P.rows0 + b * g + ii], Mt, St, Md, Sd,
+                                   P.step_unif[ab + ii], P.tc);
+            }
+            if (__ballot(rej)) al = 0;
+          }
         }
       }
       if (lane == 0) sh_alive = al;
     }
     __syncthreads();
     const int alive = sh_alive;
-    if (kind == 0 && s == 0 && tid == 0) P.step_alive[ab + i] = alive;
+    if (k == 0 && s == 0 && tid == 0) P.step_alive[ab + i0] = alive;
     if (!alive) return;
   }
   const bool second = r >= P.rows0;
@@ -143,7 +154,8 @@ hipError_t launch_sweep_t(const RowStatsParams& p, hipStream_t s) {
 
 template <int DT, int NP>
 hipError_t launch_step_np(const RowStatsParams& p, hipStream_t s) {
-  const int per = p.step < p.gather_g ? 2 : 1;
+  if (p.step < 0 || p.step_end <= p.step || p.step_end > p.gather_g + 1 || p.step_prev >= p.step) return hipErrorInvalidValue;
+  const int per = 2 * (p.step_end - p.step) - (p.step_end > p.gather_g ? 1 : 0);
   const long long grid = (long long)p.step_B * per * p.nseg;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;

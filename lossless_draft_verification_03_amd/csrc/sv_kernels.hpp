@@ -32,10 +32,15 @@ struct RowStatsParams {
   float* out_max; // [rows]
   double* out_sum;// [rows] (want & 1)
   int* out_arg;   // [rows] (want & 2)
-  // early-exit step (launch_row_step): position `step` of B sequences, target
-  // row (b, step) and draft row (b, step), swept only while every earlier
-  // position was accepted; alive[b][i] (i <= gamma) records that
+  // early-exit block (launch_row_step): positions step .. step_end-1 of B
+  // sequences, their target and draft rows, swept only while every earlier
+  // position was accepted; alive[b][step] records that.  step_prev is the
+  // previous block's first position (-1 for the first block): the block's
+  // workgroups test positions step_prev .. step-1 from the previous block's
+  // partials
   int step;
+  int step_end;
+  int step_prev;
   int step_B;
   const float* step_unif;  // [B, gamma+1]
   int* step_alive;         // [B, gamma+1]
