@@ -12,14 +12,17 @@
 //
 // A node's score is its cumulative draft log-probability (fp64), the root 0.
 //
-//  k_topk_sweep  one workgroup per (frontier row, 8192-logit segment): the
+//  k_topk_sweep  one workgroup per (frontier row, 32768-logit segment): the
 //                segment max, the sum of 2^((z - max) c) and its k largest
-//                logits (equal logits: lower index first).  Each lane keeps
-//                its own max, exp-sum and two best logits in one pass over its
-//                32 registers; one wave then picks the segment's top k from
-//                the 256 lanes' pairs in k rounds of a wave argmax.  A lane's
-//                third best matters only once both of its candidates are
-//                taken; it is then rescanned from the row.
+//                logits (equal logits: lower index first).  The segment is
+//                streamed in four 8192-logit chunks, the next chunk's loads
+//                in flight while one is processed; each lane keeps its max,
+//                exp-sum (rescaled when the max grows) and two best logits.
+//                One wave then picks the segment's top k from the 256 lanes'
+//                pairs in k rounds, each one 64-bit wave max over packed
+//                (value, index) keys.  A lane's third best matters only once
+//                both of its candidates are taken; the wave then rescans that
+//                lane's elements together.
 //  k_expand      one workgroup per sequence, one wave per frontier row:
 //                merges each row's segments (max, fp64 sum, the k best of the segment lists),
 //                forms log q = ((z - M) c - log2 S) ln 2 for the k tokens,
@@ -44,9 +47,52 @@ namespace sv {
 
 namespace {
 
-constexpr int kTreeRun = 32;  // logits per lane per segment
+constexpr int kTreeRun = 32;     // logits per lane per chunk
+constexpr int kTreeChunks = 4;   // chunks per segment, streamed with the next one in flight
+constexpr int kTreeChunk = kBlock * kTreeRun;
 constexpr int kExpandBlock = 1024;  // one wave per frontier row (up to 16 at a time)
 constexpr int kBuildBlock = 1024;
+
+// Candidate keys: (value desc, index asc) as one unsigned 64-bit order.
+// The high word maps the float's bits to an unsigned order that rises with
+// the value (sign flipped for positives, all bits for negatives); the low
+// word is ~index, so among equal values the lower index has the larger key.
+// Key 0 is below every real candidate and marks an empty slot.  -0 is keyed
+// as +0, since the two compare equal (the index decides between them).
+__device__ __forceinline__ unsigned long long cand_key(float v, int idx) {
+  unsigned u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  const unsigned mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)mono << 32) | (unsigned)(~(unsigned)idx);
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const unsigned mono = (unsigned)(k >> 32);
+  return __uint_as_float((mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono);
+}
+__device__ __forceinline__ int key_index(unsigned long long k) { return (int)(~(unsigned)k); }
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)x);
+  const unsigned hi = (unsigned)dpp_i<CTRL>((int)(unsigned)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// 64-bit unsigned max over a full wave (the wave reductions' DPP pattern).
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+  x = umax64(x, dpp_u64<kDppXor1>(x));
+  x = umax64(x, dpp_u64<kDppXor2>(x));
+  x = umax64(x, dpp_u64<kDppHalfMirror>(x));
+  x = umax64(x, dpp_u64<kDppMirror>(x));
+  return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
 
 __device__ __forceinline__ bool topk_before(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
@@ -55,11 +101,43 @@ __device__ __forceinline__ bool topk_before(float v, int i, float w, int j) {
 // (v, i) < (w, j) in the candidate order: larger value first, then lower index
 __device__ __forceinline__ bool ord_lt(float v, int i, float w, int j) { return (v > w) | ((v == w) & (i < j)); }
 
+// Element of register q of lane t in chunk ch of the segment starting at e0:
+// chunk ch covers [e0 + ch * kTreeChunk, +kTreeChunk); register q of lane t
+// is element ((q / EPV) * kBlock + t) * EPV + q % EPV of it (vector q / EPV of
+// the lane; coalesced).
+template <int EPV>
+__device__ __forceinline__ long long topk_elem(long long e0, int ch, int q, int t) {
+  return e0 + (long long)ch * kTreeChunk + (long long)(((q / EPV) * kBlock + t) * EPV + (q % EPV));
+}
+
+// Issue this lane's 16-byte loads of chunk ch (whole vectors inside
+// [e0, e1), offsets clamped into the chunk); returns how many of the lane's
+// registers hold elements of the segment.
+template <int DT>
+__device__ __forceinline__ int topk_issue(const char* rowp, long long e0, long long e1, int ch, int tid, v4i* vv) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  constexpr int KV = kTreeRun / EPV;
+  const long long cb = e0 + (long long)ch * kTreeChunk;
+  const long long ce = cb + kTreeChunk < e1 ? cb + kTreeChunk : e1;
+  const int nvec = ce > cb ? (int)((ce - cb) / EPV) : 0;
+  if (nvec <= 0) return 0;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(rowp + cb * ES, (uint32_t)nvec * 16u);
+#pragma unroll
+  for (int k = 0; k < KV; ++k) vv[k] = load16(r, (uint32_t)min(k * kBlock + tid, nvec - 1) * 16u);
+  int nv = 0;
+#pragma unroll
+  for (int k = 0; k < KV; ++k) nv += k * kBlock + tid < nvec ? 1 : 0;
+  return nv * EPV;
+}
+
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int KV = kTreeRun / EPV;
+  constexpr int kLaneElems = kTreeRun * kTreeChunks;   // one source lane's elements of the segment
+  static_assert(kLaneElems % kWave == 0, "a rescan splits a lane's elements evenly over the wave");
   __shared__ float sh_lm[kBlock], sh_ls[kBlock], sh_c1v[kBlock], sh_c2v[kBlock];
   __shared__ int sh_c1i[kBlock], sh_c2i[kBlock];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -82,82 +160,98 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
   const long long e0 = (long long)s * P.seg_elems;
   const long long e1 = e0 + P.seg_elems < V ? e0 + P.seg_elems : V;
   const char* rowp = static_cast<const char*>(P.logits) + row * V * ES;
-  // This lane's elements: register q holds element e0 + pos(q) with
-  // pos(q) = ((q / EPV) * kBlock + tid) * EPV + q % EPV (vector k = q / EPV of
-  // the lane; coalesced), so q order is index order.  Elements past the
-  // segment read as -inf and are never taken (all comparisons are strict).
-  float z[kTreeRun];
-  int nin;  // registers 0 .. nin-1 hold this lane's elements of the segment
-  if constexpr (ALIGNED) {
-    const int nvec = (int)((e1 - e0) / EPV);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(rowp + e0 * ES, (uint32_t)nvec * 16u);
-    v4i vv[KV];
-#pragma unroll
-    for (int k = 0; k < KV; ++k) vv[k] = load16(r, (uint32_t)min(k * kBlock + tid, nvec - 1) * 16u);
-    int nv = 0;
-#pragma unroll
-    for (int k = 0; k < KV; ++k) {
-      unpack<DT>(vv[k], z + k * EPV);
-      const bool in = k * kBlock + tid < nvec;
-      nv += in ? 1 : 0;
-      if (!in)
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) z[k * EPV + i] = NINF;
-    }
-    nin = nv * EPV;
-  } else {
-    int n = 0;
-#pragma unroll
-    for (int k = 0; k < KV; ++k)
-#pragma unroll
-      for (int i = 0; i < EPV; ++i) {
-        const long long e = e0 + (long long)(k * kBlock + tid) * EPV + i;
-        z[k * EPV + i] = e < e1 ? load_elem<DT>(rowp, e) : NINF;
-        n += e < e1 ? 1 : 0;
-      }
-    nin = n;
-  }
-  auto gidx = [&](int q) { return (int)(e0 + ((q / EPV) * kBlock + tid) * EPV + (q % EPV)); };
-  // one pass: the lane's two best elements (value desc, then q asc); q = -1
-  // marks an empty slot.  The first two elements seed the pair, so strict
-  // comparisons settle ties by position from then on; elements past nin are
-  // -inf and never displace anything.
+  // One pass over the lane's chunks: its two best elements (value desc, then
+  // index asc; slots hold chunk * kTreeRun + q, -1 when empty) and its
+  // exponential sum against its running max.  The lane's first two elements
+  // seed the pair, so strict comparisons settle ties by position from then
+  // on; elements past the segment are -inf and never displace anything.
   float b1v = NINF, b2v = NINF;
   int b1q = -1, b2q = -1;
-  if (nin >= 1) {
-    b1v = z[0];
-    b1q = 0;
-  }
-  if (nin >= 2) {
-    const bool sw = z[1] > z[0];
-    b1v = sw ? z[1] : z[0];
-    b1q = sw ? 1 : 0;
-    b2v = sw ? z[0] : z[1];
-    b2q = sw ? 0 : 1;
-  }
-#pragma unroll
-  for (int q = 2; q < kTreeRun; ++q) {
-    const bool c1 = z[q] > b1v;
-    const bool c2 = z[q] > b2v;
-    b2v = c1 ? b1v : (c2 ? z[q] : b2v);
-    b2q = c1 ? b1q : (c2 ? q : b2q);
-    b1v = c1 ? z[q] : b1v;
-    b1q = c1 ? q : b1q;
-  }
-  // lane sum of 2^((z - m) c) relative to its own max m = b1v
+  float ls = 0.f, lm = NINF;
   const float c = P.tc.c_hi;
-  float ls = 0.f;
-  if (b1v > NINF) {
+  v4i cur[KV];
+  int ncur = 0;
+  if constexpr (ALIGNED) ncur = topk_issue<DT>(rowp, e0, e1, 0, tid, cur);
+#pragma unroll 1
+  for (int ch = 0; ch < kTreeChunks; ++ch) {
+    float z[kTreeRun];
+    int nin;
+    v4i nxt[KV];
+    int nnxt = 0;
+    if constexpr (ALIGNED) {
+      if (ch + 1 < kTreeChunks) nnxt = topk_issue<DT>(rowp, e0, e1, ch + 1, tid, nxt);
 #pragma unroll
-    for (int q = 0; q < kTreeRun; ++q) ls += __builtin_amdgcn_exp2f((z[q] - b1v) * c);
+      for (int k = 0; k < KV; ++k) unpack<DT>(cur[k], z + k * EPV);
+      // a chunk wholly inside the segment (uniform) needs no masking
+      if (e0 + (long long)(ch + 1) * kTreeChunk > e1) {
+#pragma unroll
+        for (int q = 0; q < kTreeRun; ++q) z[q] = q < ncur ? z[q] : NINF;
+      }
+      nin = ncur;
+    } else {
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < kTreeRun; ++q) {
+        const long long e = topk_elem<EPV>(e0, ch, q, tid);
+        z[q] = e < e1 ? load_elem<DT>(rowp, e) : NINF;
+        n += e < e1 ? 1 : 0;
+      }
+      nin = n;
+    }
+    const float z0 = z[0], z1 = z[1];
+    if (ch == 0) {
+      // the lane's first two elements seed the pair
+      if (nin >= 1) {
+        b1v = z[0];
+        b1q = 0;
+      }
+      if (nin >= 2) {
+        const bool sw = z[1] > z[0];
+        b1v = sw ? z[1] : z[0];
+        b1q = sw ? 1 : 0;
+        b2v = sw ? z[0] : z[1];
+        b2q = sw ? 0 : 1;
+      }
+      z[0] = NINF;                           // consumed by the seeding
+      z[1] = NINF;
+    }
+    const int cbase = ch * kTreeRun;
+#pragma unroll
+    for (int q = 0; q < kTreeRun; ++q) {
+      const bool c1 = z[q] > b1v;
+      const bool c2 = z[q] > b2v;
+      b2v = c1 ? b1v : (c2 ? z[q] : b2v);
+      b2q = c1 ? b1q : (c2 ? cbase + q : b2q);
+      b1v = c1 ? z[q] : b1v;
+      b1q = c1 ? cbase + q : b1q;
+    }
+    z[0] = z0;                               // the seeded elements count in the sum
+    z[1] = z1;
+    // exponential sum against the running max b1v (rescaled when it grows)
+    if (b1v > NINF) {
+      if (b1v > lm) {
+        ls = lm > NINF ? ls * __builtin_amdgcn_exp2f((lm - b1v) * c) : 0.f;
+        lm = b1v;
+      }
+      float cs = 0.f;
+#pragma unroll
+      for (int q = 0; q < kTreeRun; ++q) cs += __builtin_amdgcn_exp2f((z[q] - lm) * c);
+      ls += cs;
+    }
+    if constexpr (ALIGNED) {
+#pragma unroll
+      for (int k = 0; k < KV; ++k) cur[k] = nxt[k];
+      ncur = nnxt;
+    }
   }
+  auto code_idx = [&](int code) -> int { return (int)topk_elem<EPV>(e0, code / kTreeRun, code % kTreeRun, tid); };
   // publish the lane's (max, sum) and its two candidates
-  sh_lm[tid] = b1v;
+  sh_lm[tid] = lm;
   sh_ls[tid] = ls;
   sh_c1v[tid] = b1v;
-  sh_c1i[tid] = b1q >= 0 ? gidx(b1q) : INT_MAX;
+  sh_c1i[tid] = b1q >= 0 ? code_idx(b1q) : INT_MAX;
   sh_c2v[tid] = b2v;
-  sh_c2i[tid] = b2q >= 0 ? gidx(b2q) : INT_MAX;
+  sh_c2i[tid] = b2q >= 0 ? code_idx(b2q) : INT_MAX;
   __syncthreads();
   if (wid != 0) return;
   // wave 0: segment (max, sum) from the 256 lanes
@@ -168,65 +262,54 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
   float s4 = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lm = sh_lm[lane + j * kWave];
-    s4 += lm > NINF ? sh_ls[lane + j * kWave] * __builtin_amdgcn_exp2f((lm - M) * c) : 0.f;
+    const float lmj = sh_lm[lane + j * kWave];
+    s4 += lmj > NINF ? sh_ls[lane + j * kWave] * __builtin_amdgcn_exp2f((lmj - M) * c) : 0.f;
   }
   const double S = wave_sum((double)s4);
   // wave 0: the segment's top k.  Lane l owns source lanes l + 64 j (j < 4)
-  // and their two candidates; a source lane's third best is only needed when
-  // both of its candidates were taken, and is then rescanned from the row.
-  float cv[8];
-  int ci[8];
+  // and their two candidates' keys; each round takes the wave's largest key.
+  // A source lane's third best is needed only when both of its candidates
+  // were taken; the whole wave then rescans that lane's elements.
+  unsigned long long ck[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cv[2 * j] = sh_c1v[lane + j * kWave];
-    ci[2 * j] = sh_c1i[lane + j * kWave];
-    cv[2 * j + 1] = sh_c2v[lane + j * kWave];
-    ci[2 * j + 1] = sh_c2i[lane + j * kWave];
+    const int i1 = sh_c1i[lane + j * kWave], i2 = sh_c2i[lane + j * kWave];
+    ck[2 * j] = i1 != INT_MAX ? cand_key(sh_c1v[lane + j * kWave], i1) : 0ull;
+    ck[2 * j + 1] = i2 != INT_MAX ? cand_key(sh_c2v[lane + j * kWave], i2) : 0ull;
   }
   for (int r = 0; r < P.k; ++r) {
-    float bv = NINF;
-    int bi = INT_MAX, bs = 0;
+    unsigned long long best = ck[0];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const bool better = ci[t] != INT_MAX && (bi == INT_MAX || ord_lt(cv[t], ci[t], bv, bi));
-      bv = better ? cv[t] : bv;
-      bi = better ? ci[t] : bi;
-      bs = better ? t : bs;
-    }
-    const float gv = wave_max(bi == INT_MAX ? NINF : bv);
-    const int gi = wave_min(bi != INT_MAX && bv == gv ? bi : INT_MAX);
+    for (int t = 1; t < 8; ++t) best = umax64(best, ck[t]);
+    const unsigned long long g = wave_max_u64(best);
     if (lane == 0) {
-      out->v[r] = gv;
-      out->idx[r] = gi;
+      out->v[r] = g ? key_value(g) : NINF;
+      out->idx[r] = g ? key_index(g) : INT_MAX;
     }
-    if (gi != INT_MAX && bi == gi) {
-      // consumed: a first candidate leaves its second in play; a second
-      // candidate is replaced by the source lane's next best
+    if (g == 0) continue;                                   // uniform
+    // keys are unique: one lane owns the taken key, in slot ts
+    const unsigned long long own = __ballot(best == g);
+    const int ol = (int)__ffsll((long long)own) - 1;
+    int ts = 0;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t != bs) continue;
-        if ((t & 1) == 0) {
-          ci[t] = INT_MAX;
-        } else {
-          const int src = lane + (t >> 1) * kWave;   // source thread of the segment
-          float v = NINF;
-          int vi = INT_MAX;
-          for (int q = 0; q < kTreeRun; ++q) {
-            const long long e = e0 + (long long)((q / EPV) * kBlock + src) * EPV + (q % EPV);
-            if (e >= e1) continue;
-            const float zq = load_elem<DT>(rowp, e);
-            const int ei = (int)e;
-            if (ord_lt(gv, gi, zq, ei) && (vi == INT_MAX || ord_lt(zq, ei, v, vi))) {
-              v = zq;
-              vi = ei;
-            }
-          }
-          cv[t] = v;
-          ci[t] = vi;
+    for (int t = 1; t < 8; ++t) ts = ck[t] == g ? t : ts;
+    const int tso = __builtin_amdgcn_readlane(ts, ol);
+    unsigned long long nb = 0ull;                          // a first candidate leaves its slot empty
+    if (tso & 1) {                                         // uniform: a second candidate was taken
+      const int src = ol + (tso >> 1) * kWave;
+#pragma unroll
+      for (int j = 0; j < kLaneElems / kWave; ++j) {
+        const int qq = lane * (kLaneElems / kWave) + j;
+        const long long e = topk_elem<EPV>(e0, qq / kTreeRun, qq % kTreeRun, src);
+        if (e < e1) {
+          const unsigned long long kq = cand_key(load_elem<DT>(rowp, e), (int)e);
+          if (kq < g) nb = umax64(nb, kq);
         }
       }
+      nb = wave_max_u64(nb);
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ck[t] = (lane == ol && t == tso) ? nb : ck[t];
   }
   if (lane == 0) {
     out->m = M;
@@ -508,8 +591,9 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
 }  // namespace
 
 int tree_expand_segments(int V, int* seg_elems) {
-  const long long n = ((long long)V + kBlock * kTreeRun - 1) / (kBlock * kTreeRun);
-  *seg_elems = kBlock * kTreeRun;
+  constexpr long long seg = (long long)kTreeChunk * kTreeChunks;
+  const long long n = ((long long)V + seg - 1) / seg;
+  *seg_elems = (int)seg;
   return (int)(n < 1 ? 1 : n);
 }
 
