@@ -440,23 +440,23 @@ struct NodeRec {
   int flag;   // counted (drafted, then kept)
 };
 
-// For this thread's node (score ms, key mk): how many nodes q < n with
-// flag != 0 come before it in the order lt.  Every thread reads the same
-// record at a time (an LDS broadcast), eight records per wait.
+// For one node (score ms, key mk): how many nodes q0 <= q < q1 with flag != 0
+// come before it in the order lt.  The threads of a wave read the same
+// records (LDS broadcasts), eight per wait; comparisons are branch-free.
 template <class Lt>
-__device__ int count_before(int n, const NodeRec* rec, double ms, int mk, Lt lt) {
+__device__ int count_range(const NodeRec* rec, int q0, int q1, double ms, int mk, Lt lt) {
   int cnt = 0;
-  int q = 0;
-  for (; q + 8 <= n; q += 8) {
+  int q = q0;
+  for (; q + 8 <= q1; q += 8) {
     NodeRec r[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) r[t] = rec[q + t];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) cnt += (r[t].flag && lt(r[t].s, r[t].key, ms, mk)) ? 1 : 0;
+    for (int t = 0; t < 8; ++t) cnt += (int)((r[t].flag != 0) & lt(r[t].s, r[t].key, ms, mk));
   }
-  for (; q < n; ++q) {
+  for (; q < q1; ++q) {
     const NodeRec r = rec[q];
-    cnt += (r.flag && lt(r.s, r.key, ms, mk)) ? 1 : 0;
+    cnt += (int)((r.flag != 0) & lt(r.s, r.key, ms, mk));
   }
   return cnt;
 }
@@ -471,7 +471,6 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
   const long long tb = (long long)b * P.cap;
   const int NO = P.M + 1;
   const double NINF = -__builtin_huge_val();
-  constexpr int kPer = kBuildMaxNodes / kBuildBlock;
   __shared__ int sh_nk;
   if (tid == 0) sh_nk = 0;
   for (int p = tid; p < n; p += kBuildBlock) {
@@ -494,32 +493,37 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
   }
   bad = __syncthreads_or(bad);
   if (!bad) {
-    // keep the M best drafted nodes by (score desc, depth asc, index asc)
-    int kept[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kBuildBlock;
-      kept[u] = 0;
-      if (p >= n) continue;
-      if (p == 0) {
-        kept[u] = 1;
-        continue;
-      }
+    // keep the M best drafted nodes by (score desc, depth asc, index asc):
+    // a drafted node's rank counts the drafted nodes before it, T threads
+    // per node each over a range of the table, summed in pos[] (the depths
+    // there are no longer needed: the keys carry them)
+    for (int p = tid; p < n; p += kBuildBlock) pos[p] = 0;
+    __syncthreads();
+    const int T = n < kBuildBlock ? kBuildBlock / n : 1;
+    const int L = (n + T - 1) / T;
+    for (int w = tid; w < n * T; w += kBuildBlock) {
+      const int p = w / T, c = w - p * T;
       const NodeRec me = rec[p];
-      if (!me.flag) continue;
-      const int rank = count_before(n, rec, me.s, me.key,
-                                    [](double s, int kk, double ms, int mk) { return s > ms || (s == ms && kk < mk); });
-      kept[u] = rank < P.M ? 1 : 0;
+      if (p == 0 || !me.flag) continue;
+      const int q0 = c * L, q1 = q0 + L < n ? q0 + L : n;
+      const int cnt = count_range(rec, q0, q1, me.s, me.key, [](double s, int kk, double ms, int mk) {
+        return (s > ms) | ((s == ms) & (kk < mk));
+      });
+      if (cnt) atomicAdd(&pos[p], cnt);
     }
     __syncthreads();
+    // kept: the root and ranks below M; a kept drafted node's rank is its
+    // slot in the list of kept nodes (opar[], until the parents go there)
     int cnt = 0;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kBuildBlock;
-      if (p < n) {
-        rec[p].flag = kept[u];
-        cnt += (p != 0 && kept[u]) ? 1 : 0;
+    for (int p = tid; p < n; p += kBuildBlock) {
+      int k = p == 0 ? 1 : 0;
+      if (p != 0 && rec[p].flag) {
+        const int r = pos[p];
+        k = r < P.M ? 1 : 0;
+        if (k) opar[r] = p;
       }
+      rec[p].flag = k;
+      cnt += (p != 0 && k) ? 1 : 0;
     }
     if (cnt) atomicAdd(&sh_nk, cnt);
     __syncthreads();
@@ -532,24 +536,20 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
   const int nkept = sh_nk;
   const int nout = bad ? 0 : 1 + nkept;
   if (!bad) {
-    // output position: (depth asc, score desc, index asc) among the kept
-    int o[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kBuildBlock;
-      o[u] = -1;
-      if (p >= n) continue;
+    // output position: the root first, then (depth asc, score desc, index
+    // asc) counted over the kept drafted nodes only
+    for (int p = tid; p < n; p += kBuildBlock) pos[p] = p == 0 ? 0 : -1;
+    __syncthreads();
+    for (int i = tid; i < nkept; i += kBuildBlock) {
+      const int p = opar[i];
       const NodeRec me = rec[p];
-      if (!me.flag) continue;
-      o[u] = count_before(n, rec, me.s, me.key, [](double s, int kk, double ms, int mk) {
-        const int d = kk / kBuildMaxNodes, md = mk / kBuildMaxNodes;
-        return d < md || (d == md && (s > ms || (s == ms && kk < mk)));
-      });
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kBuildBlock;
-      if (p < n) pos[p] = o[u];
+      int o = 1;
+      for (int j = 0; j < nkept; ++j) {
+        const NodeRec r = rec[opar[j]];
+        const unsigned d = (unsigned)r.key / kBuildMaxNodes, md = (unsigned)me.key / kBuildMaxNodes;
+        o += (int)((d < md) | ((d == md) & ((r.s > me.s) | ((r.s == me.s) & (r.key < me.key)))));
+      }
+      pos[p] = o;
     }
     __syncthreads();
     for (int p = tid; p < n; p += kBuildBlock) {

@@ -132,6 +132,24 @@ def test_tree_build_matches_oracle(M):
         assert W == bits.shape[1]
 
 
+def test_tree_build_large_table():
+    # more table entries than workgroup threads (1553 > 1024): one thread
+    # per node, two nodes per thread; a budget that keeps a third of them
+    B, V, T, k, K, D, M = 2, 300, 1.0, 16, 16, 7, 600
+    res = _oracle_tables(8, B, V, "f32", T, k, K, D)
+    cap = res[0][1]
+    assert cap > 1024
+    n, opar, otok, odep, oidx, omask = (x.cpu().numpy() for x in L.tree_build(_gpu_table([r[0] for r in res], cap),
+                                                                                cap, M))
+    for b, (table, n_nodes, _) in enumerate(res):
+        want = build_tree(table, n_nodes, M)
+        nn = want["n"]
+        assert n[b] == nn == M + 1
+        assert list(opar[b, :nn]) == list(want["parent"])
+        assert list(oidx[b, :nn]) == list(want["table_index"])
+        assert list(odep[b, :nn]) == list(want["depth"])
+
+
 def test_tree_build_rejects_broken_tables():
     res = _oracle_tables(4, 3, 200, "f32", 1.0, 3, 3, 3)
     cap = res[0][1]
