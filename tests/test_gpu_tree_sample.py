@@ -66,6 +66,24 @@ def test_matches_oracle(dtype, V, N, tree, noise, T):
         assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
 
 
+def test_large_vocabulary_uses_workspace_partials():
+    # more than 64 sweep segments per row: the walk keeps its partials in
+    # the workspace instead of LDS
+    w = make_workload("tree_sample63", B=2, N=5, V=600001, dtype="f32", tree="star", draft_noise=2.0,
+                      temperature=1.0, seed=12)
+    assert L.lib.spec_row_segments(600001, 0) > 64
+    g, _ = _check(w)
+    assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=0), g))
+
+
+def test_largest_tree():
+    # 4096 nodes: a star of 4095 children (long residual chains) and a chain
+    for tree, noise in (("star", 3.0), ("chain", 0.3)):
+        w = make_workload("tree_sample63", B=2, N=L.MAX_TREE_NODES, V=97, dtype="f32", tree=tree,
+                          draft_noise=noise, temperature=1.0, seed=13)
+        _check(w)
+
+
 def test_matches_oracle_many_rejections():
     # far-off drafts: most first children fail, later siblings use residuals
     w = make_workload("tree_sample63", B=40, N=13, V=2000, dtype="f32", tree="star", draft_noise=4.0, seed=2)
