@@ -210,6 +210,25 @@ def test_edge_shapes_sample_greedy(dt, B, g, V):
         assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(out.cpu().numpy(), oout)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_vocabulary_beyond_64_segments(dt):
+    # V = 1100003: more than 64 sweep segments per row (merges loop over
+    # segments in 64-lane groups) and more than 64 draw segments (the draw
+    # locates its segment over several 64-segment chunks)
+    V = 1100003
+    assert L.lib.spec_row_segments(V, 1 if dt == "bf16" else 0) > 64
+    w = make_workload("tiny", B=2, gamma=2, V=V, dtype=dt, seed=17)
+    _check_sample(w)
+    acc, out = L.verify_greedy(to_dev(w["target"]), to_dev(w["draft_tokens"]))
+    oacc, oout = oracle.verify_greedy(w["target"], dt, w["draft_tokens"])
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(out.cpu().numpy(), oout)
+    par = np.array([-1, 0, 0], np.int32)
+    tok = np.concatenate([np.zeros((2, 1), np.int32), w["draft_tokens"]], axis=1)
+    acc, path, toks = L.verify_tree(to_dev(w["target"]), to_dev(tok), to_dev(par))
+    oacc, opath, otoks = oracle.verify_tree(w["target"], dt, tok, par)
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(toks.cpu().numpy(), otoks)
+
+
 def test_neg_inf_and_one_hot_targets_sample_equals_greedy():
     rng = np.random.default_rng(3)
     B, g, V = 16, 5, 300
