@@ -40,10 +40,18 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of what the row sweep kernel is built from: its sources and the
+    parameter struct it takes (other structs in the shared header do not
+    change its code)."""
+    import re
+    csrc = os.path.join(ROOT, "lossless_draft_verification_03_amd", "csrc")
     h = hashlib.sha1()
-    for f in ("rowstats.hip", "sweep_segment.hpp", "sv_common.hpp", "sv_kernels.hpp"):
-        with open(os.path.join(ROOT, "lossless_draft_verification_03_amd", "csrc", f), "rb") as fh:
+    for f in ("rowstats.hip", "sweep_segment.hpp", "sv_common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(csrc, "sv_kernels.hpp")) as fh:
+        m = re.search(r"struct RowStatsParams \{.*?\n\};", fh.read(), re.S)
+    h.update(m.group(0).encode() if m else b"")
     return h.hexdigest()[:16]
 
 
