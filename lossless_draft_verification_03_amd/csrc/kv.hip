@@ -12,9 +12,10 @@
 //
 // One kernel, one thread per (sequence, plane, 16-byte column of an entry).
 // Every thread checks its sequence's path (it must rise strictly from 1 and
-// stay inside the cache; a short, cached read) and thread (plane 0, column
-// 0) writes new_len (or -1).  Then the thread walks the path in depth order
-// and moves its column of node n_t's entry to slot L_b + t.  A thread owns
+// stay inside the cache; a short, cached read, eight entries per round
+// trip) and thread (plane 0, column 0) writes new_len (or -1).  Then the
+// thread walks the path in depth order and moves its column of node n_t's
+// entry to slot L_b + t.  A thread owns
 // the same column of every entry of its (sequence, plane), so the one
 // overlap -- a slot read at depth t and written at a later depth t' (when
 // n_t = t') -- is ordered by the thread's own program order; a slot written
@@ -44,12 +45,21 @@ __global__ __launch_bounds__(kKvBlock) void k_kv_compact(KvParams P) {
   const int32_t* pp = P.path ? P.path + b * P.path_stride : nullptr;
   bool ok = d >= 0 && L >= 0 && (long long)L + 1 + d <= P.S;
   if (ok && pp) {
+    // batches of independent loads, then the comparisons (no early exit
+    // between the loads of a batch)
     ok = d <= P.path_stride;
     int prev = 0;
-    for (int t = 0; ok && t < d; ++t) {
-      const int n = pp[t];
-      ok = n > prev;
-      prev = n;
+    for (int t0 = 0; ok && t0 < d; t0 += kKvBatch) {
+      int n[kKvBatch];
+#pragma unroll
+      for (int k = 0; k < kKvBatch; ++k) n[k] = t0 + k < d ? pp[t0 + k] : 0;
+#pragma unroll
+      for (int k = 0; k < kKvBatch; ++k) {
+        if (t0 + k < d) {
+          ok = ok && n[k] > prev;
+          prev = n[k];
+        }
+      }
     }
     ok = ok && (long long)L + prev < P.S;
   }
