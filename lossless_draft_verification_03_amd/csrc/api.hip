@@ -101,7 +101,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   L->rsum = o;   o = up(o + (size_t)rows * 8);
   L->rarg = o;   o = up(o + (size_t)rows * 4);
   L->gath = o;   o = up(o + (size_t)rows * 4);
-  L->segsum = o; o = up(o + (size_t)seqs * nseg2 * 8);
+  L->segsum = o; o = up(o + (size_t)seqs * nseg2 * kDrawSub * 8);
   L->hcat = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)d * 2);
   L->logits = o;

@@ -18,13 +18,18 @@
 //               ratio formed from one fp64 exponent (z(x_i) was picked out by
 //               the sweep); a ballot gives the first rejection j.  All of
 //               them reach the same j; workgroup (b, 0) records it.  Then the
-//               draw weights of one segment of row j are summed in fp64:
+//               draw weights of one segment of row j are summed in fp64, each
+//               wave over its own contiguous quarter (a sub-segment):
 //                 j <  gamma : w = max(0, p_j - q_j)  (as S_t w = max(0, e_t - rho e_d))
 //                 j == gamma : w = p_gamma            (as S_t w = e_t)
-//  k_draw_pick  one workgroup per sequence: locate the segment holding
-//               u[b][gamma] * total, rescan it with one contiguous run per
-//               lane (weights kept in registers), block-scan the lane sums in
-//               fp64 and walk the crossing lane's run.
+//  k_draw_pick  one workgroup per sequence: wave 0 locates the sub-segment
+//               holding u[b][gamma] * total among the B x 4 nseg masses, the
+//               block rescans those 2048 elements with one contiguous run per
+//               lane (weights kept in registers), block-scans the lane sums
+//               in fp64 and the crossing lane walks its run.
+// The weights cost about 26 VALU slots per element (two double-float
+// exponents), so the mass pass is VALU-bound chip-wide and the pick's rescan
+// VALU-bound on its one CU; the sub-segments cut the rescan to a quarter.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -33,8 +38,10 @@ namespace sv {
 
 namespace {
 
-constexpr int kRun = 32;   // elements per lane in the draw's rescan (multiple of 8)
-constexpr int kSegElems = kBlock * kRun;
+constexpr int kRun = 8;                             // elements per lane in the pick's rescan
+constexpr int kSubElems = kBlock * kRun;            // 2048: one wave's share of a segment
+constexpr int kSegElems = kDrawSub * kSubElems;     // 8192: one mass workgroup
+static_assert(kDrawSub * kWave == kBlock, "one sub-segment per wave");
 
 template <int DT>
 __device__ __forceinline__ float weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
@@ -57,66 +64,69 @@ __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
   return R;
 }
 
-// Sum of the draw weights over elements [e_beg, e_end) of the draw row,
-// lane-interleaved, fp64 accumulation; returns the lane's partial.
-template <int DT, bool ALIGNED>
-__device__ double segment_partial(const DrawRow& R, long long e_beg, long long e_end,
-                                  const TempConst& tc, int tid) {
+// Sum of the draw weights over elements [s0, s1) of the draw row (at most
+// kSubElems), lane-interleaved over one wave, fp64 accumulation; returns the
+// wave's total in every lane (fixed combination order).
+template <int DT, bool ALIGNED, bool RESID>
+__device__ double sub_partial(const DrawRow& R, long long s0, long long s1, const TempConst& tc, int lane) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   double acc = 0.0;
   if constexpr (ALIGNED) {
-    // A segment is at most kBlock * KV whole vectors; every lane issues its
-    // KV loads (offsets clamped into the segment) before computing.
-    constexpr int KV = kRun / EPV;
-    const int nvec = (int)((e_end - e_beg) / EPV);
-    if (nvec <= 0) return 0.0;
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + e_beg * ES, (uint32_t)nvec * 16u);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + e_beg * ES, (uint32_t)nvec * 16u);
-    v4i vt[KV], vd[KV];
+    // every lane issues its KV loads (offsets clamped into the range) before
+    // computing
+    constexpr int KV = kSubElems / EPV / kWave;
+    const int nvec = (int)((s1 - s0) / EPV);
+    if (nvec > 0) {
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + s0 * ES, (uint32_t)nvec * 16u);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + s0 * ES, (uint32_t)nvec * 16u);
+      v4i vt[KV], vd[KV];
 #pragma unroll
-    for (int k = 0; k < KV; ++k) {
-      const uint32_t off = (uint32_t)min(k * kBlock + tid, nvec - 1) * 16u;
-      vt[k] = load16(rt, off);
-      if (R.resid) vd[k] = load16(rd, off);
-    }
+      for (int k = 0; k < KV; ++k) {
+        const uint32_t off = (uint32_t)min(k * kWave + lane, nvec - 1) * 16u;
+        vt[k] = load16(rt, off);
+        if constexpr (RESID) vd[k] = load16(rd, off);
+      }
 #pragma unroll
-    for (int k = 0; k < KV; ++k) {
-      if (k * kBlock + tid >= nvec) continue;
-      float zt[EPV], zd[EPV];
-      unpack<DT>(vt[k], zt);
-      if (R.resid) unpack<DT>(vd[k], zd);
+      for (int k = 0; k < KV; ++k) {
+        if (k * kWave + lane >= nvec) continue;
+        float zt[EPV], zd[EPV];
+        unpack<DT>(vt[k], zt);
+        if constexpr (RESID) unpack<DT>(vd[k], zd);
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) acc += (double)weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+        for (int i = 0; i < EPV; ++i) acc += (double)draw_weight_r<DT, RESID>(R, zt[i], RESID ? zd[i] : 0.f, tc);
+      }
     }
   } else {
-    for (long long e = e_beg + tid; e < e_end; e += kBlock) {
+    for (long long e = s0 + lane; e < s1; e += kWave) {
       const float zt = load_elem<DT>(R.t, e);
-      const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
-      acc += (double)weight<DT>(R, zt, zd, tc);
+      const float zd = RESID ? load_elem<DT>(R.d, e) : 0.f;
+      acc += (double)draw_weight_r<DT, RESID>(R, zt, zd, tc);
     }
   }
-  return acc;
+  return wave_sum(acc);
 }
 
-// Block-wide fp64 sum with a fixed combination order.
-__device__ double block_sum(double x, double* sh4, int tid) {
-  x = wave_sum(x);
-  __syncthreads();
-  if ((tid & (kWave - 1)) == 0) sh4[tid / kWave] = x;
-  __syncthreads();
-  const double t = (sh4[0] + sh4[1]) + (sh4[2] + sh4[3]);
-  __syncthreads();
-  return t;
+// Sub-segment masses of segment s of the draw row: wave w sums sub-segment
+// 4 s + w and lane 0 stores it.
+template <int DT, bool ALIGNED>
+__device__ void segment_masses(const DrawRow& R, long long V, int s, const TempConst& tc, int wid, int lane,
+                               double* sub) {
+  const long long s0 = min((long long)s * kSegElems + (long long)wid * kSubElems, V);
+  const long long s1 = min(s0 + kSubElems, V);
+  const double m = R.resid ? sub_partial<DT, ALIGNED, true>(R, s0, s1, tc, lane)
+                           : sub_partial<DT, ALIGNED, false>(R, s0, s1, tc, lane);
+  if (lane == 0) sub[s * kDrawSub + wid] = m;
 }
 
 template <int DT, bool ALIGNED, int NP>
 __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
-  __shared__ double sh4[4];
   __shared__ float sh_M[2 * 64];
   __shared__ double sh_S[2 * 64];
   __shared__ DrawInfo sh_di;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // wid is wave-uniform; readfirstlane lets the compiler keep what derives
+  // from it (buffer descriptors) in scalar registers
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.x / P.nseg, s = blockIdx.x - b * P.nseg;
   const int g = P.g;
   const long long V = P.V;
@@ -183,40 +193,38 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
   }
   if (di.j < 0) return;                       // uniform
   const DrawRow R = draw_row<DT>(P, b, di);
-  const long long sb = (long long)s * P.seg_elems;
-  const long long se = sb + P.seg_elems < V ? sb + P.seg_elems : V;
-  const double part = block_sum(segment_partial<DT, ALIGNED>(R, sb, se, P.tc, tid), sh4, tid);
-  if (tid == 0) P.segsum[(long long)b * P.nseg + s] = part;
+  segment_masses<DT, ALIGNED>(R, V, s, P.tc, wid, lane, P.segsum + (long long)b * P.nseg * kDrawSub);
 }
 
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
-  __shared__ double sh4[4];
   __shared__ double sh_wtot[4];
   __shared__ int sh_first[4];
   __shared__ long long sh_y;
   __shared__ double sh_base, sh_thr;
   __shared__ int sh_k, sh_fallback;
-  extern __shared__ double sh_seg[];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  // wid is wave-uniform; readfirstlane lets the compiler keep what derives
+  // from it (buffer descriptors) in scalar registers
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.x;
   const int g = P.g;
   const long long V = P.V;
   const long long ubase = (long long)b * (g + 1);
-  // everything this kernel reads first, issued together
+  const int nsub = P.nseg * kDrawSub;
+  double* const sub = P.segsum + (long long)b * nsub;
+  // everything this kernel reads first, issued together (the masses are
+  // read before j is known; they are ignored when j < 0)
   const DrawInfo di = P.info[b];
   const float u = P.unif[ubase + g];
-  const double* seg = P.segsum + (long long)b * P.nseg;
-  for (int t = tid; t < P.nseg; t += kBlock) sh_seg[t] = seg[t];
-  __syncthreads();
+  const double m0 = wid == 0 && lane < nsub ? sub[lane] : 0.0;
   if (di.j < 0) return;                       // k_draw_mass (b, 0) wrote the -1s
   DrawRow R = draw_row<DT>(P, b, di);
   if (wid == 0) {
-    double total = 0.0;
-    for (int c0 = 0; c0 < P.nseg; c0 += kWave)
-      total += wave_sum(c0 + lane < P.nseg ? sh_seg[c0 + lane] : 0.0);
+    // total in a fixed order (chunks of 64, the first kept in registers)
+    double total = wave_sum(m0);
+    for (int c0 = kWave; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
     if (lane == 0) {
       sh_fallback = total > 0.0 ? 0 : 1;
       sh_thr = (double)u * total;
@@ -226,20 +234,15 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   if (sh_fallback) {
     // A zero residual cannot follow a rejection in exact arithmetic; if
     // rounding produces one, draw from p_j (this workgroup recomputes the
-    // row's segment masses alone).
+    // row's sub-segment masses alone, in place; the barrier makes them
+    // visible to wave 0).
     R.resid = false;
     R.d = R.t;
-    for (int t = 0; t < P.nseg; ++t) {
-      const long long b0 = (long long)t * P.seg_elems;
-      const long long b1 = b0 + P.seg_elems < V ? b0 + P.seg_elems : V;
-      const double m = block_sum(segment_partial<DT, ALIGNED>(R, b0, b1, P.tc, tid), sh4, tid);
-      if (tid == 0) sh_seg[t] = m;
-    }
+    for (int t = 0; t < P.nseg; ++t) segment_masses<DT, ALIGNED>(R, V, t, P.tc, wid, lane, sub);
     __syncthreads();
     if (wid == 0) {
       double total = 0.0;
-      for (int c0 = 0; c0 < P.nseg; c0 += kWave)
-        total += wave_sum(c0 + lane < P.nseg ? sh_seg[c0 + lane] : 0.0);
+      for (int c0 = 0; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
       if (lane == 0) sh_thr = (double)u * total;
     }
     __syncthreads();
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   if (wid == 0) {
     double base;
     int fb;
-    const int k = locate_segment(sh_seg, P.nseg, sh_thr, lane, &base, &fb);
+    const int k = locate_segment(sub, nsub, sh_thr, lane, &base, &fb);
     if (lane == 0) {
       sh_k = k;
       sh_base = base;
@@ -256,9 +259,9 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
     }
   }
   __syncthreads();
-  const long long kb = (long long)sh_k * P.seg_elems;
-  const long long ke = kb + P.seg_elems < V ? kb + P.seg_elems : V;
-  // this lane's run [rb, re) inside segment k, weights kept in registers
+  const long long kb = (long long)__builtin_amdgcn_readfirstlane(sh_k) * kSubElems;   // uniform (LDS)
+  const long long ke = kb + kSubElems < V ? kb + kSubElems : V;
+  // this lane's run [rb, re) inside sub-segment k, weights kept in registers
   const long long rb0 = kb + (long long)tid * kRun;
   const long long rb = rb0 < ke ? rb0 : ke;
   const long long re = rb + kRun < ke ? rb + kRun : ke;
@@ -349,7 +352,7 @@ template <int DT, bool ALIGNED, int NP>
 hipError_t launch_sample_np(const SampleParams& p, hipStream_t s) {
   hipLaunchKernelGGL((k_draw_mass<DT, ALIGNED, NP>), dim3((unsigned)((long long)p.B * p.nseg)), dim3(kBlock), 0, s,
                      p);
-  hipLaunchKernelGGL((k_draw_pick<DT, ALIGNED>), dim3((unsigned)p.B), dim3(kBlock), (size_t)p.nseg * 8, s, p);
+  hipLaunchKernelGGL((k_draw_pick<DT, ALIGNED>), dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
@@ -377,7 +380,6 @@ int sample_draw_segments(int V, int* seg_elems) {
 
 hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s) {
   if ((long long)p.B * p.nseg > 0x7fffffffLL) return hipErrorInvalidValue;
-  if ((size_t)p.nseg * 8 > 48 * 1024) return hipErrorInvalidValue;
   const bool aligned = dt == DT_BF16 ? (p.V % 8 == 0) : (p.V % 4 == 0);
   if (dt == DT_BF16) return aligned ? launch_sample_t<DT_BF16, true>(p, s) : launch_sample_t<DT_BF16, false>(p, s);
   return aligned ? launch_sample_t<DT_F32, true>(p, s) : launch_sample_t<DT_F32, false>(p, s);

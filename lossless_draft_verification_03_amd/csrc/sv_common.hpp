@@ -242,14 +242,22 @@ struct DrawRow {
   bool resid;
 };
 
+template <int DT, bool RESID>
+__device__ __forceinline__ float draw_weight_r(const DrawRow& R, float zt, float zd, const TempConst& tc) {
+  const float et = exp_rel<DT>(zt, R.Mt, tc);
+  if constexpr (!RESID) {
+    return et;
+  } else {
+    const float ed = exp_rel<DT>(zd, R.Md, tc);
+    float w = fmaf(-ed, R.rho_hi, et);
+    w = fmaf(-ed, R.rho_lo, w);
+    return fmaxf(w, 0.f);
+  }
+}
+// The same weight with R.resid read at run time.
 template <int DT>
 __device__ __forceinline__ float draw_weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
-  const float et = exp_rel<DT>(zt, R.Mt, tc);
-  if (!R.resid) return et;
-  const float ed = exp_rel<DT>(zd, R.Md, tc);
-  float w = fmaf(-ed, R.rho_hi, et);
-  w = fmaf(-ed, R.rho_lo, w);
-  return fmaxf(w, 0.f);
+  return R.resid ? draw_weight_r<DT, true>(R, zt, zd, tc) : draw_weight_r<DT, false>(R, zt, zd, tc);
 }
 
 // Wave-parallel location of the segment holding thr: lanes scan the segment

@@ -71,14 +71,17 @@ struct SampleParams {
   int nseg_rows;
   const float* gathered;  // [rows] z[row][x] picked out by the sweep
   int B, g, V;
-  int nseg;               // draw segments per row
-  int seg_elems;          // elements per draw segment (multiple of 8)
+  int nseg;               // draw segments per row (one mass workgroup each)
+  int seg_elems;          // elements per draw segment (kDrawSub sub-segments)
   TempConst tc;
   DrawInfo* info;         // [B]
-  double* segsum;         // [B][nseg]
+  double* segsum;         // [B][nseg * kDrawSub] sub-segment masses
   int* accept_len;        // [B]
   int* out_tokens;        // [B, g+1]
 };
+// Each draw segment is summed as kDrawSub contiguous sub-segments, one per
+// wave; the pick rescans one sub-segment.
+constexpr int kDrawSub = 4;
 int sample_draw_segments(int V, int* seg_elems);
 hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s);
 

@@ -257,6 +257,27 @@ def test_q_equals_p_accepts_all():
     assert not res["unexplained"]
 
 
+@pytest.mark.parametrize("dt,V,B,g", [("bf16", 20000, 16, 3), ("f32", 20000, 16, 3), ("bf16", 9001, 1, 1),
+                                      ("f32", 2047, 1, 1)])
+def test_zero_residual_falls_back_to_p(dt, V, B, g):
+    """q = p with u[0] = 1: the accept test u < p/q = 1 fails, so position 0
+    is rejected and the residual max(0, p - q) is zero everywhere; the draw
+    then comes from p_0.  V spans several draw segments and sub-segments
+    with a ragged tail.  With an unaligned V the target and draft rows of
+    one position start at different 16-byte offsets unless both are row 0,
+    and a different summation order can leave p/q = 1 + 1 ulp; those cases
+    use one sequence and one position."""
+    w = make_workload("tiny", B=B, gamma=g, V=V, dtype=dt, seed=13)
+    w["draft"] = np.ascontiguousarray(w["target"][:, :-1])
+    w["uniforms"][:, 0] = 1.0
+    acc, out = _run_sample(w)
+    oacc, oout, infos = _oracle_sample(w)
+    assert np.all(oacc == 0) and np.all(acc == 0)
+    res = classify_sample(acc, out, oacc, oout, infos)
+    assert not res["unexplained"], res["unexplained"][:5]
+    assert res["explained"] == 0
+
+
 def test_invalid_draft_tokens_flag_sequence():
     w = make_workload("tiny", B=4, gamma=3, V=50, seed=1)
     w["draft_tokens"][1, 2] = 50
