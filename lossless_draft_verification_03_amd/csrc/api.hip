@@ -101,7 +101,10 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   L->rsum = o;   o = up(o + (size_t)rows * 8);
   L->rarg = o;   o = up(o + (size_t)rows * 4);
   L->gath = o;   o = up(o + (size_t)rows * 4);
-  L->segsum = o; o = up(o + (size_t)seqs * nseg2 * kDrawSub * 8);
+  // the linear draw's sub-segment masses; the tree walk's in the tree sampler
+  const size_t segsum_bytes = mode == SPEC_MODE_TREE_SAMPLE ? (size_t)B * tree_walk_subsegments(V, DT_F32) * 8
+                                                            : (size_t)seqs * nseg2 * kDrawSub * 8;
+  L->segsum = o; o = up(o + segsum_bytes);
   L->hcat = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)d * 2);
   L->logits = o;
@@ -490,6 +493,7 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   p.n_pre = (int)tree_presweep_nodes(B, N, V, (int)dt, n_sweep);
   p.ws_part = at<Partial>(ws, L.part);
   p.pre_part = p.ws_part + 2LL * B * sh.nseg;
+  p.ws_sub = at<double>(ws, L.segsum);
   p.accept_len = accept_len;
   p.out_path = out_path;
   p.out_tokens = out_tokens;

@@ -205,6 +205,14 @@ constexpr long long kMaxSampleVocab = 1LL << 25;
 
 // One workgroup per sequence walks its tree, computing the row statistics of
 // the nodes it visits on the way (the rows of other nodes are never read).
+// The tree walk's draw segments (1024 threads x 32 bf16 or 16 fp32 elements)
+// and the kTreeWalkSub sub-segments of each whose masses its final draw keeps.
+constexpr int kTreeWalkSub = 16;
+__host__ __device__ constexpr long long tree_walk_seg(int dt) { return dt == DT_BF16 ? 32768 : 16384; }
+__host__ __device__ inline long long tree_walk_subsegments(long long V, int dt) {
+  return (V + tree_walk_seg(dt) - 1) / tree_walk_seg(dt) * kTreeWalkSub;
+}
+
 struct TreeSampleParams {
   const void* tgt;         // [B, N, V] target rows of the nodes
   const void* drf;         // [B, N, V] draft rows (row n: the law n's children were drawn from)
@@ -219,6 +227,7 @@ struct TreeSampleParams {
   int n_pre;               // nodes 0 .. n_pre-1 have their rows swept before the walk
   Partial* pre_part;       // [2 B n_pre][nseg]: target rows (b, n), then draft rows (b, n)
   Partial* ws_part;        // [B][2 nseg] partials of the walk, used when nseg exceeds the LDS slots
+  double* ws_sub;          // [B][tree_walk_subsegments(V, dt)] sub-segment masses of the final draw
   int32_t* accept_len;     // [B]
   int32_t* out_path;       // [B, N]
   int32_t* out_tokens;     // [B, N]

@@ -71,6 +71,9 @@ constexpr int kTLdsPart = 64;              // sweep partials per row kept in LDS
 constexpr int kTPer = kTreeMaxNodes / kTB; // nodes per thread in the child scan
 constexpr int kTMaxSeg = (int)(((long long)kMaxSampleVocab + kTB * 16 - 1) / (kTB * 16));
 static_assert(kTreeMaxNodes % kTB == 0, "child scan covers the node range exactly");
+static_assert(kTW == kTreeWalkSub && walk_seg<DT_BF16>() == tree_walk_seg(DT_BF16) &&
+                  walk_seg<DT_F32>() == tree_walk_seg(DT_F32),
+              "the workspace's sub-segment layout matches the walk");
 
 struct WalkLds {
   int par[kTreeMaxNodes];
@@ -95,29 +98,34 @@ struct WalkLds {
   int nk, k, fallback;
 };
 
-// One segment's draw weights, lane-interleaved 16-byte vectors, fp64
-// accumulation; returns this thread's partial.
+// Wave wid's share of one segment's draw weights: the wid-th of kTW
+// contiguous sub-segments of [e0, e1), lane-interleaved 16-byte vectors, fp64
+// accumulation; returns this lane's partial.
 template <int DT, bool ALIGNED>
-__device__ double walk_seg_partial(const DrawRow& R, long long e0, long long e1, const TempConst& tc, int tid) {
+__device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1, const TempConst& tc, int wid,
+                                   int lane) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
+  constexpr int SUB = walk_seg<DT>() / kTW;
+  const long long s0 = min(e0 + (long long)wid * SUB, e1);
+  const long long s1 = min(s0 + SUB, e1);
   double acc = 0.0;
   if constexpr (ALIGNED) {
-    constexpr int KV = walk_run<DT>() / EPV;
-    const int nvec = (int)((e1 - e0) / EPV);
+    constexpr int KV = SUB / EPV / kWave;
+    const int nvec = (int)((s1 - s0) / EPV);
     if (nvec <= 0) return 0.0;
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + e0 * ES, (uint32_t)nvec * 16u);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + e0 * ES, (uint32_t)nvec * 16u);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + s0 * ES, (uint32_t)nvec * 16u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + s0 * ES, (uint32_t)nvec * 16u);
     v4i vt[KV], vd[KV];
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      const uint32_t off = (uint32_t)min(k * kTB + tid, nvec - 1) * 16u;
+      const uint32_t off = (uint32_t)min(k * kWave + lane, nvec - 1) * 16u;
       vt[k] = load16(rt, off);
       if (R.resid) vd[k] = load16(rd, off);
     }
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      if (k * kTB + tid >= nvec) continue;
+      if (k * kWave + lane >= nvec) continue;
       float zt[EPV], zd[EPV];
       unpack<DT>(vt[k], zt);
       if (R.resid) unpack<DT>(vd[k], zd);
@@ -125,7 +133,7 @@ __device__ double walk_seg_partial(const DrawRow& R, long long e0, long long e1,
       for (int i = 0; i < EPV; ++i) acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
     }
   } else {
-    for (long long e = e0 + tid; e < e1; e += kTB) {
+    for (long long e = s0 + lane; e < s1; e += kWave) {
       const float zt = load_elem<DT>(R.t, e);
       const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
       acc += (double)draw_weight<DT>(R, zt, zd, tc);
@@ -135,19 +143,26 @@ __device__ double walk_seg_partial(const DrawRow& R, long long e0, long long e1,
 }
 
 // Segment masses of the draw row into L.seg and their total (segment order,
-// fixed combination order throughout).  Every thread of the block calls it.
+// fixed combination order throughout); if sub is not null, also every
+// segment's kTW sub-segment masses into sub[segment * kTW + sub-segment]
+// (global memory, read back by this workgroup after a barrier).  Every
+// thread of the block calls it.
 template <int DT, bool ALIGNED>
-__device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, WalkLds& L, int tid) {
+__device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, WalkLds& L, int tid,
+                            double* sub) {
   constexpr int SEG = walk_seg<DT>();
-  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nseg = (int)((V + SEG - 1) / SEG);
   for (int s0 = 0; s0 < nseg; s0 += kTChunk) {
     const int s1 = min(s0 + kTChunk, nseg);
     for (int s = s0; s < s1; ++s) {
       const long long e0 = (long long)s * SEG;
       const long long e1 = e0 + SEG < V ? e0 + SEG : V;
-      const double a = wave_sum(walk_seg_partial<DT, ALIGNED>(R, e0, e1, tc, tid));
-      if (lane == 0) L.red[(s - s0) * kTW + wid] = a;
+      const double a = wave_sum(walk_sub_partial<DT, ALIGNED>(R, e0, e1, tc, wid, lane));
+      if (lane == 0) {
+        L.red[(s - s0) * kTW + wid] = a;
+        if (sub != nullptr) sub[s * kTW + wid] = a;
+      }
     }
     __syncthreads();
     if (tid < s1 - s0) {
@@ -166,76 +181,51 @@ __device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, 
   return L.total;
 }
 
-// Inverse-CDF draw over the masses the last mass_pass left in L.seg: the
-// first element whose cumulative weight exceeds thr, or the last element
-// with positive weight if rounding leaves none.
+// Inverse-CDF draw over the masses the last mass_pass left in L.seg and in
+// sub: the first element whose cumulative weight exceeds thr, or the last
+// element with positive weight if rounding leaves none.  The segment, then
+// its sub-segment, are located with wave scans; the block rescans that
+// sub-segment, RUN elements per thread.
 template <int DT, bool ALIGNED>
 __device__ long long walk_pick(const DrawRow& R, long long V, double thr, const TempConst& tc, WalkLds& L,
-                               int tid) {
-  constexpr int ES = DT == DT_BF16 ? 2 : 4;
-  constexpr int EPV = 16 / ES;
-  constexpr int RUN = walk_run<DT>();
+                               int tid, const double* sub) {
   constexpr int SEG = walk_seg<DT>();
+  constexpr int SUB = SEG / kTW;
+  constexpr int RUN = SUB / kTB;
+  static_assert(RUN >= 1 && RUN * kTB == SUB, "one sub-segment per block rescan");
   const int lane = tid & (kWave - 1), wid = tid / kWave;
   const int nseg = (int)((V + SEG - 1) / SEG);
   if (wid == 0) {
     double base;
     int fb;
     const int k = locate_segment(L.seg, nseg, thr, lane, &base, &fb);
+    double base2;
+    int fb2;
+    const int k2 = locate_segment(sub + (long long)k * kTW, kTW, thr - base, lane, &base2, &fb2);
     if (lane == 0) {
-      L.k = k;
-      L.base = base;
-      L.fallback = fb;
+      L.k = k * kTW + k2;
+      L.base = base + base2;
+      L.fallback = fb | fb2;
       L.y = -1;
     }
   }
   __syncthreads();
-  const long long kb = (long long)L.k * SEG;
-  const long long ke = kb + SEG < V ? kb + SEG : V;
+  const long long kb = (long long)__builtin_amdgcn_readfirstlane(L.k) * SUB;
+  const long long ke = kb + SUB < V ? kb + SUB : V;
   const long long rb0 = kb + (long long)tid * RUN;
   const long long rb = rb0 < ke ? rb0 : ke;
   const long long re = rb + RUN < ke ? rb + RUN : ke;
   float w[RUN];
-  if constexpr (ALIGNED) {
-    constexpr int KV = RUN / EPV;
-    const int nvec = (int)((re - rb) / EPV);
-    const int segvec = (int)((ke - kb) / EPV);
-    const int lane_vec0 = (int)((rb - kb) / EPV);
-    if (nvec > 0) {
-      const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + kb * ES, (uint32_t)segvec * 16u);
-      const __amdgpu_buffer_rsrc_t rd = make_rsrc(R.d + kb * ES, (uint32_t)segvec * 16u);
-      v4i vt[KV], vd[KV];
 #pragma unroll
-      for (int k = 0; k < KV; ++k) {
-        const uint32_t off = (uint32_t)(lane_vec0 + min(k, nvec - 1)) * 16u;
-        vt[k] = load16(rt, off);
-        if (R.resid) vd[k] = load16(rd, off);
-      }
-#pragma unroll
-      for (int k = 0; k < KV; ++k) {
-        float zt[EPV], zd[EPV];
-        unpack<DT>(vt[k], zt);
-        if (R.resid) unpack<DT>(vd[k], zd);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i)
-          w[k * EPV + i] = k < nvec ? draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc) : 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < RUN; ++e) w[e] = 0.f;
+  for (int e = 0; e < RUN; ++e) {
+    const long long ee = rb + e;
+    float v = 0.f;
+    if (ee < re) {
+      const float zt = load_elem<DT>(R.t, ee);
+      const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
+      v = draw_weight<DT>(R, zt, zd, tc);
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < RUN; ++e) {
-      const long long ee = rb + e;
-      float v = 0.f;
-      if (ee < re) {
-        const float zt = load_elem<DT>(R.t, ee);
-        const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
-        v = draw_weight<DT>(R, zt, zd, tc);
-      }
-      w[e] = v;
-    }
+    w[e] = v;
   }
   double T4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -325,7 +315,9 @@ template <int DT, bool ALIGNED, int NP>
 __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   __shared__ WalkLds L;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  // wid is wave-uniform; readfirstlane keeps what derives from it (the row
+  // a quarter sweeps, its buffer descriptors) in scalar registers
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.x;
   const int N = P.N;
   const long long V = P.V;
@@ -455,7 +447,7 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
         break;
       }
       set_rho(R, cn, St, Sd);
-      const double Wn = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid) / St;
+      const double Wn = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, nullptr) / St;
       if (Wn > 0.0) {
         cc = cn;
         W = Wn;
@@ -472,16 +464,17 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
   }
 
   // final draw from R (fallback: the law before the last residual, then p)
-  double total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+  double* const sub = P.ws_sub + (long long)b * tree_walk_subsegments(P.V, DT);
+  double total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
   if (!(total > 0.0) && R.resid) {
     set_rho(R, c_fb, L.S[0], L.S[1]);
-    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
   }
   if (!(total > 0.0) && R.resid) {
     set_rho(R, 0.0, L.S[0], L.S[1]);
-    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid);
+    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
   }
-  const long long y = walk_pick<DT, ALIGNED>(R, V, (double)L.u[0] * total, P.tc, L, tid);
+  const long long y = walk_pick<DT, ALIGNED>(R, V, (double)L.u[0] * total, P.tc, L, tid, sub);
   for (int c = tid; c < N; c += kTB) {
     if (c >= d) out_path[c] = -1;
     if (c > d) out_tok[c] = -1;
