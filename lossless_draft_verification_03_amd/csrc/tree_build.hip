@@ -94,6 +94,52 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
   return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
 }
 
+// bf16 candidates of one segment fit one unsigned 32-bit order: the value's
+// 16 bits mapped as above in the high half, 0xFFFF - (index within the
+// segment) in the low half (a segment holds at most 32768 logits, so a real
+// key is never 0).  Same order, half the width of each wave reduction.
+__device__ __forceinline__ unsigned cand_key16(float v, int li) {
+  unsigned u = __float_as_uint(v) >> 16;
+  u = u == 0x8000u ? 0u : u;
+  const unsigned mono = (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
+  return (mono << 16) | (0xFFFFu - (unsigned)li);
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
+  x = max(x, (unsigned)dpp_i<kDppXor1>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppXor2>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppHalfMirror>((int)x));
+  x = max(x, (unsigned)dpp_i<kDppMirror>((int)x));
+  const unsigned a = (unsigned)__builtin_amdgcn_readlane((int)x, 0), b = (unsigned)__builtin_amdgcn_readlane((int)x, 16);
+  const unsigned c = (unsigned)__builtin_amdgcn_readlane((int)x, 32), d = (unsigned)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+static_assert(kTreeChunk * kTreeChunks <= 0x8000, "segment-local indices fit the low half of a 32-bit key");
+
+// Candidate keys of a segment starting at element e0, by element type.
+template <int DT>
+struct TopkKey;
+template <>
+struct TopkKey<DT_BF16> {
+  using T = unsigned;
+  static __device__ __forceinline__ T make(float v, int e, long long e0) { return cand_key16(v, (int)(e - e0)); }
+  static __device__ __forceinline__ float value(T k) {
+    const unsigned mono = k >> 16;
+    const unsigned u = (mono & 0x8000u) ? (mono & 0x7FFFu) : (~mono & 0xFFFFu);
+    return __uint_as_float(u << 16);
+  }
+  static __device__ __forceinline__ int index(T k, long long e0) { return (int)(e0 + (0xFFFFu - (k & 0xFFFFu))); }
+  static __device__ __forceinline__ T wmax(T x) { return wave_max_u32(x); }
+};
+template <>
+struct TopkKey<DT_F32> {
+  using T = unsigned long long;
+  static __device__ __forceinline__ T make(float v, int e, long long) { return cand_key(v, e); }
+  static __device__ __forceinline__ float value(T k) { return key_value(k); }
+  static __device__ __forceinline__ int index(T k, long long) { return key_index(k); }
+  static __device__ __forceinline__ T wmax(T x) { return wave_max_u64(x); }
+};
+
 __device__ __forceinline__ bool topk_before(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
@@ -216,14 +262,16 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
       z[1] = NINF;
     }
     const int cbase = ch * kTreeRun;
+    // with b1v >= b2v the new second value is the middle of (b1v, b2v, z):
+    // one med3 and one max for the values, the strict compares for the slots
 #pragma unroll
     for (int q = 0; q < kTreeRun; ++q) {
       const bool c1 = z[q] > b1v;
       const bool c2 = z[q] > b2v;
-      b2v = c1 ? b1v : (c2 ? z[q] : b2v);
       b2q = c1 ? b1q : (c2 ? cbase + q : b2q);
-      b1v = c1 ? z[q] : b1v;
       b1q = c1 ? cbase + q : b1q;
+      b2v = __builtin_amdgcn_fmed3f(b1v, b2v, z[q]);
+      b1v = fmaxf(b1v, z[q]);
     }
     z[0] = z0;                               // the seeded elements count in the sum
     z[1] = z1;
@@ -270,21 +318,23 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
   // and their two candidates' keys; each round takes the wave's largest key.
   // A source lane's third best is needed only when both of its candidates
   // were taken; the whole wave then rescans that lane's elements.
-  unsigned long long ck[8];
+  using KT = TopkKey<DT>;
+  using Key = typename KT::T;
+  Key ck[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i1 = sh_c1i[lane + j * kWave], i2 = sh_c2i[lane + j * kWave];
-    ck[2 * j] = i1 != INT_MAX ? cand_key(sh_c1v[lane + j * kWave], i1) : 0ull;
-    ck[2 * j + 1] = i2 != INT_MAX ? cand_key(sh_c2v[lane + j * kWave], i2) : 0ull;
+    ck[2 * j] = i1 != INT_MAX ? KT::make(sh_c1v[lane + j * kWave], i1, e0) : (Key)0;
+    ck[2 * j + 1] = i2 != INT_MAX ? KT::make(sh_c2v[lane + j * kWave], i2, e0) : (Key)0;
   }
   for (int r = 0; r < P.k; ++r) {
-    unsigned long long best = ck[0];
+    Key best = ck[0];
 #pragma unroll
-    for (int t = 1; t < 8; ++t) best = umax64(best, ck[t]);
-    const unsigned long long g = wave_max_u64(best);
+    for (int t = 1; t < 8; ++t) best = best > ck[t] ? best : ck[t];
+    const Key g = KT::wmax(best);
     if (lane == 0) {
-      out->v[r] = g ? key_value(g) : NINF;
-      out->idx[r] = g ? key_index(g) : INT_MAX;
+      out->v[r] = g ? KT::value(g) : NINF;
+      out->idx[r] = g ? KT::index(g, e0) : INT_MAX;
     }
     if (g == 0) continue;                                   // uniform
     // keys are unique: one lane owns the taken key, in slot ts
@@ -294,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
 #pragma unroll
     for (int t = 1; t < 8; ++t) ts = ck[t] == g ? t : ts;
     const int tso = __builtin_amdgcn_readlane(ts, ol);
-    unsigned long long nb = 0ull;                          // a first candidate leaves its slot empty
+    Key nb = 0;                                            // a first candidate leaves its slot empty
     if (tso & 1) {                                         // uniform: a second candidate was taken
       const int src = ol + (tso >> 1) * kWave;
 #pragma unroll
@@ -302,11 +352,11 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
         const int qq = lane * (kLaneElems / kWave) + j;
         const long long e = topk_elem<EPV>(e0, qq / kTreeRun, qq % kTreeRun, src);
         if (e < e1) {
-          const unsigned long long kq = cand_key(load_elem<DT>(rowp, e), (int)e);
-          if (kq < g) nb = umax64(nb, kq);
+          const Key kq = KT::make(load_elem<DT>(rowp, e), (int)e, e0);
+          if (kq < g) nb = nb > kq ? nb : kq;
         }
       }
-      nb = wave_max_u64(nb);
+      nb = KT::wmax(nb);
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) ck[t] = (lane == ol && t == tso) ? nb : ck[t];
