@@ -43,10 +43,6 @@ constexpr int kSubElems = kBlock * kRun;            // 2048: one wave's share of
 constexpr int kSegElems = kDrawSub * kSubElems;     // 8192: one mass workgroup
 static_assert(kDrawSub * kWave == kBlock, "one sub-segment per wave");
 
-template <int DT>
-__device__ __forceinline__ float weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
-  return draw_weight<DT>(R, zt, zd, tc);
-}
 
 template <int DT>
 __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
@@ -289,7 +285,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
         if (R.resid) unpack<DT>(vd[k], zd);
 #pragma unroll
         for (int i = 0; i < EPV; ++i)
-          w[k * EPV + i] = k < nvec ? weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, P.tc) : 0.f;
+          w[k * EPV + i] = k < nvec ? draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, P.tc) : 0.f;
       }
     } else {
 #pragma unroll
@@ -303,7 +299,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
       if (ee < re) {
         const float zt = load_elem<DT>(R.t, ee);
         const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
-        v = weight<DT>(R, zt, zd, P.tc);
+        v = draw_weight<DT>(R, zt, zd, P.tc);
       }
       w[e] = v;
     }

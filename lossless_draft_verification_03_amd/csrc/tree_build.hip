@@ -140,12 +140,11 @@ struct TopkKey<DT_F32> {
   static __device__ __forceinline__ T wmax(T x) { return wave_max_u64(x); }
 };
 
+// (v, i) comes before (w, j) in the candidate order: larger value first,
+// then lower index
 __device__ __forceinline__ bool topk_before(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
-
-// (v, i) < (w, j) in the candidate order: larger value first, then lower index
-__device__ __forceinline__ bool ord_lt(float v, int i, float w, int j) { return (v > w) | ((v == w) & (i < j)); }
 
 // Element of register q of lane t in chunk ch of the segment starting at e0:
 // chunk ch covers [e0 + ch * kTreeChunk, +kTreeChunk); register q of lane t
