@@ -57,6 +57,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 32, NS = 4;
 constexpr int kChunksPerStage = BM * BK / 8;      // 1024 16-byte chunks (A and W alike)
@@ -251,7 +252,9 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   auto mfma = [&](auto Hc, int q) {
     constexpr int H = decltype(Hc)::value;
     const int i = q >> 2, j = q & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[H][i], fb[H][j], acc[i][j], 0, 0, 0);
+    // W fragment as the MFMA's first operand: acc[i][j] holds the 32 x 32
+    // block transposed, vocabulary along the registers (see the epilogue)
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[H][j], fa[H][i], acc[i][j], 0, 0, 0);
   };
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
@@ -334,20 +337,39 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   // no load may still be writing LDS when the workgroup ends
   wait_vm<0>();
 
-  // Output layout of the 32 x 32 MFMA: lane l holds column l % 32 and rows
-  // 8 (r / 4) + 4 (l / 32) + r % 4 for r = 0..15.
+  // Output layout (W fragment first): lane l holds feature row l % 32 of
+  // block i and the vocabulary columns 8 q + 4 (l / 32) + t of block j in
+  // registers 4 q + t (q, t = 0..3), so each group of four registers is four
+  // consecutive logits of one row.  When the wave's 128 columns lie inside V
+  // and rows keep 16-byte alignment (V % 4 == 0; C is 16-byte aligned), each
+  // group is one 16-byte store; otherwise (a ragged last tile) element stores.
+  const long long c0 = n0 + wn * 128;
+  const bool vec = (N & 3) == 0 && c0 + 128 <= N;   // uniform per wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (row >= M) continue;
+    float* const crow = P.C + (long long)row * N + c0 + 4 * (lane >> 5);
+    if (vec) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long col = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= N) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) P.C[(long long)row * N + col] = acc[i][j][r];
-      }
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * q + t];
+          *reinterpret_cast<f32x4*>(crow + j * 32 + 8 * q) = v;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const long long col = c0 + j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (col < N) crow[j * 32 + 8 * (r >> 2) + (r & 3)] = acc[i][j][r];
+        }
     }
+  }
 }
 
 }  // namespace
