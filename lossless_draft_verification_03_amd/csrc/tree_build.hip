@@ -19,12 +19,14 @@
 //                in flight while one is processed; each lane keeps its max,
 //                exp-sum (rescaled when the max grows) and two best logits.
 //                One wave then picks the segment's top k from the 256 lanes'
-//                pairs in k rounds, each one 64-bit wave max over packed
-//                (value, index) keys.  A lane's third best matters only once
+//                pairs in k rounds, each one wave max over packed
+//                (value, index) keys (32 bits for bf16 rows, 64 for fp32).  A lane's third best matters only once
 //                both of its candidates are taken; the wave then rescans that
 //                lane's elements together.
 //  k_expand      one workgroup per sequence, one wave per frontier row:
-//                merges each row's segments (max, fp64 sum, the k best of the segment lists),
+//                merges each row's segments (max, fp64 sum, the k best of
+//                the segment lists: by rank counting when the lists hold at
+//                most 64 entries, else in k rounds),
 //                forms log q = ((z - M) c - log2 S) ln 2 for the k tokens,
 //                writes the children to the node table (frontier slot f,
 //                rank r at table position off + f k + r) and picks the next
@@ -37,8 +39,8 @@
 //                breaks the invariants the expansion keeps (parents before
 //                children, depth = parent depth + 1, kept parents) is
 //                reported with n = -1.
-// The sweep streams every frontier row once: HBM-bound like the verify
-// sweep.  The other two kernels touch kilobytes.
+// The sweep reads every frontier row once; the other two kernels touch
+// kilobytes.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -50,7 +52,7 @@ namespace {
 constexpr int kTreeRun = 32;     // logits per lane per chunk
 constexpr int kTreeChunks = 4;   // chunks per segment, streamed with the next one in flight
 constexpr int kTreeChunk = kBlock * kTreeRun;
-constexpr int kExpandBlock = 1024;  // one wave per frontier row (up to 16 at a time)
+constexpr int kExpandBlock = 512;   // one wave per frontier row (up to 8 at a time)
 constexpr int kBuildBlock = 1024;
 
 // Candidate keys: (value desc, index asc) as one unsigned 64-bit order.
@@ -368,40 +370,95 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
 
 __global__ __launch_bounds__(kExpandBlock) void k_expand(TreeExpandParams P) {
   __shared__ double sc[kCandMax];
+  __shared__ int sh_rank[kCandMax];
   __shared__ int sh_count;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = blockIdx.x;
   const int k = P.k;
   const long long tb = (long long)b * P.cap;
   const int ncand = P.K_in * k;
+  const float NINF = -__builtin_huge_valf();
   if (tid == 0) sh_count = 0;
+  for (int c = tid; c < ncand; c += blockDim.x) sh_rank[c] = 0;
   const int nw = blockDim.x / kWave;
+  // With at most 64 list entries per row, lane c holds entry c % k of segment
+  // c / k and its rank among them gives its output slot directly; otherwise
+  // the lists merge in k rounds.
+  const int nent = P.nseg * k;
+  const bool by_rank = nent <= kWave;
   for (int f = wid; f < P.K_in; f += nw) {
     const long long row = (long long)b * P.K_in + f;
-    const int pn = P.frontier[row];
-    if (pn < 0 || pn >= P.off) {  // empty slot (entries past the written table count as empty)
-      for (int r = lane; r < k; r += kWave) {
-        const long long pos = tb + P.off + (long long)f * k + r;
-        P.parent[pos] = -1;
-        P.token[pos] = -1;
-        P.score[pos] = -__builtin_huge_val();
-        P.depth[pos] = -1;
-        sc[f * k + r] = -__builtin_huge_val();
-      }
-      continue;
-    }
     const TopkPart* pr = P.part + row * P.nseg;
+    // Everything below reads the row's partials whether or not the slot is
+    // live (the sweep writes an empty record for a dead slot), so these loads
+    // do not wait for the frontier entry; a dead slot's outputs are empty.
+    const int pn = P.frontier[row];
+    float cv = NINF;
+    int ci = INT_MAX;
+    int cj = -1;                                  // the entry's place in its list
+    if (by_rank && lane < nent) {
+      const int s = lane / k;
+      cj = lane - s * k;
+      cv = pr[s].v[cj];
+      ci = pr[s].idx[cj];
+    }
+    // the segments' (max, sum) records: one per lane when they fit a wave
+    float sm = NINF, ss = 0.f;
+    if (P.nseg <= kWave && lane < P.nseg) {
+      sm = pr[lane].m;
+      ss = pr[lane].s;
+    }
+    // the parent's score and depth (the only loads that wait for the frontier)
+    const bool live = pn >= 0 && pn < P.off;  // entries past the written table count as empty
+    const double ps = P.score[tb + (live ? pn : 0)];
+    const int pd = P.depth[tb + (live ? pn : 0)];
     // row max and fp64 sum over the segments
-    float m = -__builtin_huge_valf();
-    for (int t = lane; t < P.nseg; t += kWave) m = fmaxf(m, pr[t].m);
+    float m = sm;
+    for (int t = lane + kWave; t < P.nseg; t += kWave) m = fmaxf(m, pr[t].m);
+    if (P.nseg > kWave) m = fmaxf(m, pr[lane].m);
     const float M = wave_max(m);
-    double S = 0.0;
-    for (int t = lane; t < P.nseg; t += kWave)
-      if (pr[t].s > 0.f) S += (double)pr[t].s * exp2_f64(((double)pr[t].m - (double)M) * P.tc.c64);
+    double S = ss > 0.f ? (double)ss * exp2_f64(((double)sm - (double)M) * P.tc.c64) : 0.0;
+    if (P.nseg > kWave) {
+      S = 0.0;
+      for (int t = lane; t < P.nseg; t += kWave) {
+        const float tm = pr[t].m, ts = pr[t].s;
+        if (ts > 0.f) S += (double)ts * exp2_f64(((double)tm - (double)M) * P.tc.c64);
+      }
+    }
     S = wave_sum(S);
     const double l2S = log2(S);
-    const double ps = P.score[tb + pn];
-    const int pd = P.depth[tb + pn];
+    // child r of the row: token i with logit v (i == INT_MAX: none)
+    auto put = [&](int r, float v, int i) {
+      const long long pos = tb + P.off + (long long)f * k + r;
+      const bool real = live && i != INT_MAX;
+      double sv = -__builtin_huge_val();
+      if (real && v > NINF) sv = ps + (((double)v - (double)M) * P.tc.c64 - l2S) * kLn2;
+      P.parent[pos] = real ? pn : -1;
+      P.token[pos] = real ? i : -1;
+      P.score[pos] = sv;
+      P.depth[pos] = real ? pd + 1 : -1;
+      sc[f * k + r] = sv;
+    };
+    if (by_rank) {
+      // rank = entries before this one in (value desc, index asc), as 64-bit
+      // keys (0: empty entry); equal keys (only empty entries) go by lane, so
+      // the ranks are a permutation and ranks 0..k-1 fill every slot once.
+      // The k-th best entry is no worse than the best of the segments' k-th
+      // entries (each segment has k entries at least that good), so only
+      // entries at or above that bound can rank below k, and every entry
+      // before one of them is one of them: the counts run over those alone.
+      const unsigned long long key = (ci != INT_MAX) ? cand_key(cv != cv ? NINF : cv, ci) : 0ull;
+      const unsigned long long bound = wave_max_u64(cj == k - 1 ? key : 0ull);
+      const bool cand = lane < nent && key >= bound;
+      int rank = 0;
+      for (unsigned long long mm = __ballot(cand); mm; mm &= mm - 1) {
+        const int c2 = __builtin_ctzll(mm);
+        const unsigned long long w = readlane_u64(key, c2);
+        rank += (int)((w > key) | ((w == key) & (c2 < lane)));
+      }
+      if (cand && rank < k) put(rank, cv, ci);
+      continue;
+    }
     // the k best of the segments' lists (each sorted, best first), k rounds
     float pv = __builtin_huge_valf();
     int pi = -1;
@@ -413,12 +470,12 @@ __global__ __launch_bounds__(kExpandBlock) void k_expand(TreeExpandParams P) {
 #pragma unroll
       for (int j = 0; j < kTopkMax; ++j) {
         const bool in = lane < P.nseg && j < k;
-        hv[j] = in ? pr[in ? lane : 0].v[j] : -__builtin_huge_valf();
+        hv[j] = in ? pr[in ? lane : 0].v[j] : NINF;
         hi[j] = in ? pr[in ? lane : 0].idx[j] : INT_MAX;
       }
     }
     for (int r = 0; r < k; ++r) {
-      float v = -__builtin_huge_valf();
+      float v = NINF;
       int ix = INT_MAX;
       if (onefold) {
         v = hv[0];
@@ -430,11 +487,11 @@ __global__ __launch_bounds__(kExpandBlock) void k_expand(TreeExpandParams P) {
         for (int c = lane; c < nl; c += kWave) {
           const int t = c / kTopkMax, j = c % kTopkMax;
           if (j >= k) continue;
-          const float cv = pr[t].v[j];
-          const int ci = pr[t].idx[j];
-          if (ci != INT_MAX && topk_before(pv, pi, cv, ci) && topk_before(cv, ci, v, ix)) {
-            v = cv;
-            ix = ci;
+          const float cv2 = pr[t].v[j];
+          const int ci2 = pr[t].idx[j];
+          if (ci2 != INT_MAX && topk_before(pv, pi, cv2, ci2) && topk_before(cv2, ci2, v, ix)) {
+            v = cv2;
+            ix = ci2;
           }
         }
       }
@@ -449,34 +506,35 @@ __global__ __launch_bounds__(kExpandBlock) void k_expand(TreeExpandParams P) {
           hv[j] = hv[j + 1];
           hi[j] = hi[j + 1];
         }
-        hv[kTopkMax - 1] = -__builtin_huge_valf();
+        hv[kTopkMax - 1] = NINF;
         hi[kTopkMax - 1] = INT_MAX;
       }
-      if (lane == 0) {
-        const long long pos = tb + P.off + (long long)f * k + r;
-        double lq = -__builtin_huge_val();
-        if (wv > -__builtin_huge_valf()) lq = (((double)wv - (double)M) * P.tc.c64 - l2S) * kLn2;
-        const double sv = ps + lq;
-        P.parent[pos] = wi == INT_MAX ? -1 : pn;
-        P.token[pos] = wi == INT_MAX ? -1 : wi;
-        P.score[pos] = wi == INT_MAX ? -__builtin_huge_val() : sv;
-        P.depth[pos] = wi == INT_MAX ? -1 : pd + 1;
-        sc[f * k + r] = wi == INT_MAX ? -__builtin_huge_val() : sv;
-      }
+      if (lane == 0) put(r, wv, wi);
     }
   }
   __syncthreads();
-  // next frontier: rank among the children with a finite score
-  for (int c = tid; c < ncand; c += blockDim.x) {
+  // next frontier: rank among the children with a finite score, the
+  // comparisons of one child split over a power-of-two group of threads
+  const int nt = blockDim.x;
+  const int lp = ncand >= nt ? 0 : 31 - __builtin_clz((unsigned)(nt / ncand));
+  const int parts = 1 << lp;
+  for (int it = tid; it < (ncand << lp); it += nt) {
+    const int c = it >> lp;
     const double v = sc[c];
     if (!(v > -__builtin_huge_val())) continue;
-    int rank = 0;
-    for (int c2 = 0; c2 < ncand; ++c2) {
+    int cnt = 0;
+    for (int c2 = it & (parts - 1); c2 < ncand; c2 += parts) {
       const double w = sc[c2];
-      rank += (w > v || (w == v && c2 < c)) ? 1 : 0;
+      cnt += (int)((w > v) | ((w == v) & (c2 < c)));
     }
-    atomicAdd(&sh_count, 1);
-    if (rank < P.K_out) P.next_frontier[(long long)b * P.K_out + rank] = P.off + c;
+    if (cnt) atomicAdd(&sh_rank[c], cnt);
+  }
+  __syncthreads();
+  for (int c = tid; c < ncand; c += nt) {
+    const bool fin = sc[c] > -__builtin_huge_val();
+    const unsigned long long fm = __ballot(fin);
+    if (fin && lane == __builtin_ctzll(fm)) atomicAdd(&sh_count, __popcll(fm));
+    if (fin && sh_rank[c] < P.K_out) P.next_frontier[(long long)b * P.K_out + sh_rank[c]] = P.off + c;
   }
   __syncthreads();
   for (int t = sh_count + tid; t < P.K_out; t += blockDim.x) P.next_frontier[(long long)b * P.K_out + t] = -1;

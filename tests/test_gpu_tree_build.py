@@ -61,9 +61,17 @@ def _check_frontier(got, table, want, off, ncand, K_out):
     raise AssertionError((got, want))
 
 
-@pytest.mark.parametrize("dtype,V", [("bf16", 20000), ("f32", 9001), ("bf16", 777)])
-def test_tree_expand_step_matches_oracle(dtype, V):
-    B, k, K_in, K_out, T = 5, 5, 4, 6, 0.8
+# The expansion merges the segments' top-k lists (32768-logit segments) by
+# rank counting when they hold at most 64 entries, else in k rounds over
+# lists held one per lane (up to 64 segments) or scanned (more segments).
+@pytest.mark.parametrize("dtype,V,k,K_in,B", [
+    ("bf16", 20000, 5, 4, 5), ("f32", 9001, 5, 4, 5), ("bf16", 777, 5, 4, 5),
+    ("bf16", 128256, 16, 2, 2),              # 4 segments x 16 = 64 entries: rank counting
+    ("bf16", 136000, 16, 2, 2),              # 5 x 16 = 80 entries: rounds, lists in lanes
+    ("f32", 64 * 32768 + 1000, 2, 2, 2),     # 65 segments: rounds, lists scanned
+])
+def test_tree_expand_step_matches_oracle(dtype, V, k, K_in, B):
+    K_out, T = 6, 0.8
     cap = 1 + k + K_in * k
     # depth 1 (the root) by the oracle, so both sides start from the same table
     tables, frontiers = [], []
