@@ -540,30 +540,32 @@ __global__ __launch_bounds__(kExpandBlock) void k_expand(TreeExpandParams P) {
   for (int t = sh_count + tid; t < P.K_out; t += blockDim.x) P.next_frontier[(long long)b * P.K_out + t] = -1;
 }
 
-// One node of the table as the build kernel ranks it.
-struct NodeRec {
-  double s;   // score
-  int key;    // depth * kBuildMaxNodes + table index
-  int flag;   // counted (drafted, then kept)
-};
-
-// For one node (score ms, key mk): how many nodes q0 <= q < q1 with flag != 0
-// come before it in the order lt.  The threads of a wave read the same
-// records (LDS broadcasts), eight per wait; comparisons are branch-free.
-template <class Lt>
-__device__ int count_range(const NodeRec* rec, int q0, int q1, double ms, int mk, Lt lt) {
+// For one node (score ms, key mk): how many nodes q0 <= q < q1 come before
+// it by (score desc, key asc); a node not counted has a NaN score, which no
+// comparison passes.  The threads of a wave read the same scores (LDS
+// broadcasts), eight per wait; the keys are read only for a batch in which
+// some lane meets an equal score (its own, at least once).
+__device__ int count_before(const double* rs, const int* rkey, int q0, int q1, double ms, int mk) {
   int cnt = 0;
   int q = q0;
   for (; q + 8 <= q1; q += 8) {
-    NodeRec r[8];
+    double r[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) r[t] = rec[q + t];
+    for (int t = 0; t < 8; ++t) r[t] = rs[q + t];
+    bool eq = false;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) cnt += (int)((r[t].flag != 0) & lt(r[t].s, r[t].key, ms, mk));
+    for (int t = 0; t < 8; ++t) {
+      cnt += (int)(r[t] > ms);
+      eq |= r[t] == ms;
+    }
+    if (__ballot(eq)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cnt += (int)((r[t] == ms) & (rkey[q + t] < mk));
+    }
   }
   for (; q < q1; ++q) {
-    const NodeRec r = rec[q];
-    cnt += (int)((r.flag != 0) & lt(r.s, r.key, ms, mk));
+    const double r = rs[q];
+    cnt += (int)((r > ms) | ((r == ms) & (rkey[q] < mk)));
   }
   return cnt;
 }
@@ -571,31 +573,33 @@ __device__ int count_range(const NodeRec* rec, int q0, int q1, double ms, int mk
 __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
   extern __shared__ double tb_lds[];
   const int n = P.n_nodes, tid = threadIdx.x, b = blockIdx.x;
-  NodeRec* rec = reinterpret_cast<NodeRec*>(tb_lds);  // [n]
-  int* par = reinterpret_cast<int*>(rec + n);         // [n] table parent
-  int* pos = par + n;                                 // [n] output position or -1
-  int* opar = pos + n;                                // [M + 1] output parent
+  double* rs = tb_lds;                                // [n] score (NaN once a node is not ranked)
+  int* rkey = reinterpret_cast<int*>(rs + n);         // [n] depth * kBuildMaxNodes + table index
+  int* flag = rkey + n;                               // [n] drafted, then kept
+  int* par = flag + n;                                // [n] table parent
+  int* pos = par + n;                                 // [n] depth, then rank, then output position
+  int* opar = pos + n;                                // [M + 1] kept nodes by rank, then output parents
   const long long tb = (long long)b * P.cap;
   const int NO = P.M + 1;
   const double NINF = -__builtin_huge_val();
   __shared__ int sh_nk;
   if (tid == 0) sh_nk = 0;
   for (int p = tid; p < n; p += kBuildBlock) {
-    rec[p].s = P.score[tb + p];
+    rs[p] = P.score[tb + p];
     par[p] = P.parent[tb + p];
-    pos[p] = P.depth[tb + p];  // depth, for now
+    pos[p] = P.depth[tb + p];
   }
   __syncthreads();
   // drafted nodes, keys, and the invariants of a table the expansion wrote
   bool bad = false;
   for (int p = tid; p < n; p += kBuildBlock) {
     const int q = par[p];
-    const bool drafted = p >= 1 && q >= 0 && rec[p].s > NINF;
-    rec[p].flag = drafted ? 1 : 0;
-    rec[p].key = pos[p] * kBuildMaxNodes + p;
+    const bool drafted = p >= 1 && q >= 0 && rs[p] > NINF;
+    flag[p] = drafted ? 1 : 0;
+    rkey[p] = pos[p] * kBuildMaxNodes + p;
     if (p == 0) bad |= q != -1 || pos[0] != 0;
     else if (drafted)
-      bad |= q >= p || (q != 0 && !(par[q] >= 0 && rec[q].s > NINF)) || pos[p] != pos[q] + 1 || pos[p] < 1 ||
+      bad |= q >= p || (q != 0 && !(par[q] >= 0 && rs[q] > NINF)) || pos[p] != pos[q] + 1 || pos[p] < 1 ||
              pos[p] >= (1 << 19);
   }
   bad = __syncthreads_or(bad);
@@ -604,18 +608,18 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
     // a drafted node's rank counts the drafted nodes before it, T threads
     // per node each over a range of the table, summed in pos[] (the depths
     // there are no longer needed: the keys carry them)
-    for (int p = tid; p < n; p += kBuildBlock) pos[p] = 0;
+    for (int p = tid; p < n; p += kBuildBlock) {
+      pos[p] = 0;
+      if (!flag[p]) rs[p] = __builtin_nan("");
+    }
     __syncthreads();
     const int T = n < kBuildBlock ? kBuildBlock / n : 1;
     const int L = (n + T - 1) / T;
     for (int w = tid; w < n * T; w += kBuildBlock) {
       const int p = w / T, c = w - p * T;
-      const NodeRec me = rec[p];
-      if (p == 0 || !me.flag) continue;
+      if (!flag[p]) continue;
       const int q0 = c * L, q1 = q0 + L < n ? q0 + L : n;
-      const int cnt = count_range(rec, q0, q1, me.s, me.key, [](double s, int kk, double ms, int mk) {
-        return (s > ms) | ((s == ms) & (kk < mk));
-      });
+      const int cnt = count_before(rs, rkey, q0, q1, rs[p], rkey[p]);
       if (cnt) atomicAdd(&pos[p], cnt);
     }
     __syncthreads();
@@ -624,12 +628,12 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
     int cnt = 0;
     for (int p = tid; p < n; p += kBuildBlock) {
       int k = p == 0 ? 1 : 0;
-      if (p != 0 && rec[p].flag) {
+      if (p != 0 && flag[p]) {
         const int r = pos[p];
         k = r < P.M ? 1 : 0;
         if (k) opar[r] = p;
       }
-      rec[p].flag = k;
+      flag[p] = k;
       cnt += (p != 0 && k) ? 1 : 0;
     }
     if (cnt) atomicAdd(&sh_nk, cnt);
@@ -637,26 +641,34 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
     // kept nodes' parents must be kept (true for scores the expansion wrote)
     bool open = false;
     for (int p = tid; p < n; p += kBuildBlock)
-      if (p != 0 && rec[p].flag && !rec[par[p]].flag) open = true;
+      if (p != 0 && flag[p] && !flag[par[p]]) open = true;
     bad = __syncthreads_or(open);
   }
   const int nkept = sh_nk;
   const int nout = bad ? 0 : 1 + nkept;
   if (!bad) {
     // output position: the root first, then (depth asc, score desc, index
-    // asc) counted over the kept drafted nodes only
+    // asc) counted over the kept drafted nodes only, each node's comparisons
+    // split over a power-of-two group of threads
     for (int p = tid; p < n; p += kBuildBlock) pos[p] = p == 0 ? 0 : -1;
     __syncthreads();
-    for (int i = tid; i < nkept; i += kBuildBlock) {
-      const int p = opar[i];
-      const NodeRec me = rec[p];
-      int o = 1;
-      for (int j = 0; j < nkept; ++j) {
-        const NodeRec r = rec[opar[j]];
-        const unsigned d = (unsigned)r.key / kBuildMaxNodes, md = (unsigned)me.key / kBuildMaxNodes;
-        o += (int)((d < md) | ((d == md) & ((r.s > me.s) | ((r.s == me.s) & (r.key < me.key)))));
+    for (int i = tid; i < nkept; i += kBuildBlock) pos[opar[i]] = 1;
+    __syncthreads();
+    const int lp = (nkept == 0 || nkept >= kBuildBlock) ? 0 : 31 - __builtin_clz((unsigned)(kBuildBlock / nkept));
+    for (int w = tid; w < (nkept << lp); w += kBuildBlock) {
+      const int p = opar[w >> lp];
+      const double ms = rs[p];
+      const int mk = rkey[p];
+      const unsigned md = (unsigned)mk / kBuildMaxNodes;
+      int o = 0;
+      for (int j = w & ((1 << lp) - 1); j < nkept; j += 1 << lp) {
+        const int q = opar[j];
+        const double s = rs[q];
+        const int kq = rkey[q];
+        const unsigned d = (unsigned)kq / kBuildMaxNodes;
+        o += (int)((d < md) | ((d == md) & ((s > ms) | ((s == ms) & (kq < mk)))));
       }
-      pos[p] = o;
+      if (o) atomicAdd(&pos[p], o);
     }
     __syncthreads();
     for (int p = tid; p < n; p += kBuildBlock) {
@@ -668,7 +680,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_tree_build(TreeBuildParams P) {
       P.out_parent[ob] = po;
       P.out_index[ob] = p;
       P.out_token[ob] = P.token[tb + p];
-      P.out_depth[ob] = rec[p].key / kBuildMaxNodes;
+      P.out_depth[ob] = rkey[p] / kBuildMaxNodes;
     }
     __syncthreads();
   }
@@ -722,7 +734,7 @@ hipError_t launch_tree_expand(const TreeExpandParams& p, hipStream_t s) {
 }
 
 hipError_t launch_tree_build(const TreeBuildParams& p, hipStream_t s) {
-  const size_t lds = (size_t)p.n_nodes * (16 + 4 + 4) + (size_t)(p.M + 1) * 4;
+  const size_t lds = (size_t)p.n_nodes * (8 + 4 * 4) + (size_t)(p.M + 1) * 4;
   if (p.n_nodes > kBuildMaxNodes || p.M + 1 > kBuildMaxNodes || lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tree_build, dim3((unsigned)p.B), dim3(kBuildBlock), lds, s, p);
   return hipGetLastError();

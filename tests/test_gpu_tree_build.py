@@ -245,3 +245,40 @@ def test_tree_expand_full_size_sampled():
         assert np.array_equal(gtok[b, sl], tables[b]["token"][sl])
         assert np.max(np.abs(gs[b, sl] - tables[b]["score"][sl])) < SCORE_TOL
         _check_frontier(nf[b], tables[b], want, off, K_in * k, K_out)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_expand_clustered_and_tied_topk(dtype):
+    # Row 0: the k best logits are all elements of one lane of the segment
+    # sweep (lane 0 of segment 0: 16-byte vectors 0, 256, 512, ... of the
+    # first chunks), so that lane's second, third, ... best are taken in turn.
+    # Row 1: equal maxima spread over waves and segments (lower index first).
+    # Row 2: -inf everywhere but a few entries.  Row 3: all equal.
+    B, K_in, V, k, K_out, T = 1, 4, 128256, 16, 8, 1.0
+    epv = 8 if dtype == "bf16" else 4
+    lane0 = [v * 256 * epv + i for v in range(8) for i in range(epv)][:k]
+    rng = np.random.default_rng(21)
+    rows = rng.normal(0, 1.0, (K_in, V))
+    rows[0, lane0] = 9.0 + np.arange(k) * 0.25
+    tied = [3, 300, 5000, 20000, 33000, 70000, 100000, 128000, 128255, 40, 41, 2047, 2048, 65536, 98304, 131071 % V]
+    rows[1, tied] = 7.0
+    rows[2, :] = -np.inf
+    rows[2, [7, 77777, 128255]] = [1.0, 2.0, 1.0]
+    rows[3, :] = 0.5
+    raw = f32_to_bf16_bits(rows.astype(np.float32)) if dtype == "bf16" else rows.astype(np.float32)
+    cap = 1 + K_in + K_in * k
+    t = new_table(cap, 0)
+    for f in range(K_in):
+        t["parent"][1 + f], t["token"][1 + f], t["score"][1 + f], t["depth"][1 + f] = 0, f, -0.5 * f, 1
+    frontier = np.arange(1, K_in + 1, dtype=np.int32)[None, :]
+    gt = _gpu_table([t], cap)
+    nf = L.tree_expand(to_dev(raw[None]), to_dev(frontier), gt, 1 + K_in, T, k, K_out).cpu().numpy()
+    gp, gtok, gs, gd = (x.cpu().numpy() for x in gt)
+    want = expand_step(t, frontier[0], _decode(raw, dtype), T, k, K_out, 1 + K_in)
+    sl = slice(1 + K_in, 1 + K_in + K_in * k)
+    assert np.array_equal(gtok[0, sl], t["token"][sl])
+    assert np.array_equal(gp[0, sl], t["parent"][sl]) and np.array_equal(gd[0, sl], t["depth"][sl])
+    fin = np.isfinite(t["score"][sl])
+    assert np.array_equal(np.isfinite(gs[0, sl]), fin)
+    assert np.max(np.abs(gs[0, sl][fin] - t["score"][sl][fin])) < SCORE_TOL
+    _check_frontier(nf[0], t, want, 1 + K_in, K_in * k, K_out)
