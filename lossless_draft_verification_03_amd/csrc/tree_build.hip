@@ -16,13 +16,16 @@
 //                segment max, the sum of 2^((z - max) c) and its k largest
 //                logits (equal logits: lower index first).  The segment is
 //                streamed in four 8192-logit chunks, the next chunk's loads
-//                in flight while one is processed; each lane keeps its max,
-//                exp-sum (rescaled when the max grows) and two best logits.
-//                One wave then picks the segment's top k from the 256 lanes'
-//                pairs in k rounds, each one wave max over packed
-//                (value, index) keys (32 bits for bf16 rows, 64 for fp32).  A lane's third best matters only once
-//                both of its candidates are taken; the wave then rescans that
-//                lane's elements together.
+//                in flight while one is processed; each lane keeps only its
+//                max and exp-sum (rescaled when the max grows).  Wave 0 then
+//                finds T, the k-th largest lane max: every top-k logit is at
+//                or above T and lies in a lane whose max reaches T.  Those
+//                lanes (usually k to k + 2) are reread, their logits at or
+//                above T collected in LDS and ranked.  When ties or -inf rows
+//                make that set large, a second pass keeps each lane's two
+//                best logits and one wave picks the top k in k rounds over
+//                packed (value, index) keys, rescanning a lane once both of
+//                its candidates are taken.
 //  k_expand      one workgroup per sequence, one wave per frontier row:
 //                merges each row's segments (max, fp64 sum, the k best of
 //                the segment lists: by rank counting when the lists hold at
@@ -132,6 +135,7 @@ struct TopkKey<DT_BF16> {
   }
   static __device__ __forceinline__ int index(T k, long long e0) { return (int)(e0 + (0xFFFFu - (k & 0xFFFFu))); }
   static __device__ __forceinline__ T wmax(T x) { return wave_max_u32(x); }
+  static __device__ __forceinline__ T readlane(T x, int l) { return (T)__builtin_amdgcn_readlane((int)x, l); }
 };
 template <>
 struct TopkKey<DT_F32> {
@@ -140,6 +144,7 @@ struct TopkKey<DT_F32> {
   static __device__ __forceinline__ float value(T k) { return key_value(k); }
   static __device__ __forceinline__ int index(T k, long long) { return key_index(k); }
   static __device__ __forceinline__ T wmax(T x) { return wave_max_u64(x); }
+  static __device__ __forceinline__ T readlane(T x, int l) { return readlane_u64(x, l); }
 };
 
 // (v, i) comes before (w, j) in the candidate order: larger value first,
@@ -178,51 +183,25 @@ __device__ __forceinline__ int topk_issue(const char* rowp, long long e0, long l
   return nv * EPV;
 }
 
-template <int DT, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
+constexpr int kLaneElems = kTreeRun * kTreeChunks;   // one lane's elements of a segment
+constexpr int kFastLanes = 16;     // candidate lanes the threshold rescan takes (else the pair pass)
+constexpr int kFastList = kWave;   // logits at or above the threshold it ranks (else the pair pass)
+
+// Stream lane tid's elements of the segment [e0, e1), chunk by chunk, the
+// next chunk's loads in flight while fn(ch, z) runs on the current one.
+// z[q] is element topk_elem(e0, ch, q, tid), -inf past the segment.
+template <int DT, bool ALIGNED, class F>
+__device__ __forceinline__ void topk_stream(const char* rowp, long long e0, long long e1, int tid, F&& fn) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int KV = kTreeRun / EPV;
-  constexpr int kLaneElems = kTreeRun * kTreeChunks;   // one source lane's elements of the segment
-  static_assert(kLaneElems % kWave == 0, "a rescan splits a lane's elements evenly over the wave");
-  __shared__ float sh_lm[kBlock], sh_ls[kBlock], sh_c1v[kBlock], sh_c2v[kBlock];
-  __shared__ int sh_c1i[kBlock], sh_c2i[kBlock];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const long long row = blockIdx.x / P.nseg;
-  const int s = (int)(blockIdx.x - row * P.nseg);
-  TopkPart* out = P.part + blockIdx.x;
-  const long long V = P.V;
   const float NINF = -__builtin_huge_valf();
-  if (P.frontier[row] < 0) {
-    if (tid < kTopkMax) {
-      out->v[tid] = NINF;
-      out->idx[tid] = INT_MAX;
-    }
-    if (tid == 0) {
-      out->m = NINF;
-      out->s = 0.f;
-    }
-    return;
-  }
-  const long long e0 = (long long)s * P.seg_elems;
-  const long long e1 = e0 + P.seg_elems < V ? e0 + P.seg_elems : V;
-  const char* rowp = static_cast<const char*>(P.logits) + row * V * ES;
-  // One pass over the lane's chunks: its two best elements (value desc, then
-  // index asc; slots hold chunk * kTreeRun + q, -1 when empty) and its
-  // exponential sum against its running max.  The lane's first two elements
-  // seed the pair, so strict comparisons settle ties by position from then
-  // on; elements past the segment are -inf and never displace anything.
-  float b1v = NINF, b2v = NINF;
-  int b1q = -1, b2q = -1;
-  float ls = 0.f, lm = NINF;
-  const float c = P.tc.c_hi;
   v4i cur[KV];
   int ncur = 0;
   if constexpr (ALIGNED) ncur = topk_issue<DT>(rowp, e0, e1, 0, tid, cur);
 #pragma unroll 1
   for (int ch = 0; ch < kTreeChunks; ++ch) {
     float z[kTreeRun];
-    int nin;
     v4i nxt[KV];
     int nnxt = 0;
     if constexpr (ALIGNED) {
@@ -234,25 +213,51 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
 #pragma unroll
         for (int q = 0; q < kTreeRun; ++q) z[q] = q < ncur ? z[q] : NINF;
       }
-      nin = ncur;
     } else {
-      int n = 0;
 #pragma unroll
       for (int q = 0; q < kTreeRun; ++q) {
         const long long e = topk_elem<EPV>(e0, ch, q, tid);
         z[q] = e < e1 ? load_elem<DT>(rowp, e) : NINF;
-        n += e < e1 ? 1 : 0;
       }
-      nin = n;
     }
-    const float z0 = z[0], z1 = z[1];
+    fn(ch, z);
+    if constexpr (ALIGNED) {
+#pragma unroll
+      for (int k = 0; k < KV; ++k) cur[k] = nxt[k];
+      ncur = nnxt;
+    }
+  }
+}
+
+// The segment's top k when the threshold rescan cannot take it (more than
+// kFastLanes lanes reach the threshold, which takes ties or -inf rows, or
+// more than kFastList logits do): a second pass in which each lane keeps its
+// two best elements, then k rounds of a wave max over packed keys in wave 0.
+// A lane's third best matters only once both of its candidates are taken;
+// the wave then rescans that lane's elements together.  Every thread of the
+// workgroup calls it; the results go to out->v, out->idx.
+template <int DT, bool ALIGNED>
+__device__ void topk_pairs(const TreeExpandParams& P, const char* rowp, long long e0, long long e1, int tid,
+                           TopkPart* out, float* sh_c1v, float* sh_c2v, int* sh_c1i, int* sh_c2i) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const float NINF = -__builtin_huge_valf();
+  // the lane's two best elements (value desc, then index asc; slots hold
+  // chunk * kTreeRun + q, -1 when empty).  The lane's first two elements
+  // seed the pair, so strict comparisons settle ties by position from then
+  // on; elements past the segment are -inf and never displace anything.
+  float b1v = NINF, b2v = NINF;
+  int b1q = -1, b2q = -1;
+  topk_stream<DT, ALIGNED>(rowp, e0, e1, tid, [&](int ch, float (&z)[kTreeRun]) {
     if (ch == 0) {
-      // the lane's first two elements seed the pair
-      if (nin >= 1) {
+      // the lane's first two elements (one 16-byte vector) seed the pair
+      const long long f0 = topk_elem<EPV>(e0, 0, 0, tid);
+      if (f0 < e1) {
         b1v = z[0];
         b1q = 0;
       }
-      if (nin >= 2) {
+      if (f0 + 1 < e1) {
         const bool sw = z[1] > z[0];
         b1v = sw ? z[1] : z[0];
         b1q = sw ? 1 : 0;
@@ -274,51 +279,15 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
       b2v = __builtin_amdgcn_fmed3f(b1v, b2v, z[q]);
       b1v = fmaxf(b1v, z[q]);
     }
-    z[0] = z0;                               // the seeded elements count in the sum
-    z[1] = z1;
-    // exponential sum against the running max b1v (rescaled when it grows)
-    if (b1v > NINF) {
-      if (b1v > lm) {
-        ls = lm > NINF ? ls * __builtin_amdgcn_exp2f((lm - b1v) * c) : 0.f;
-        lm = b1v;
-      }
-      float cs = 0.f;
-#pragma unroll
-      for (int q = 0; q < kTreeRun; ++q) cs += __builtin_amdgcn_exp2f((z[q] - lm) * c);
-      ls += cs;
-    }
-    if constexpr (ALIGNED) {
-#pragma unroll
-      for (int k = 0; k < KV; ++k) cur[k] = nxt[k];
-      ncur = nnxt;
-    }
-  }
+  });
   auto code_idx = [&](int code) -> int { return (int)topk_elem<EPV>(e0, code / kTreeRun, code % kTreeRun, tid); };
-  // publish the lane's (max, sum) and its two candidates
-  sh_lm[tid] = lm;
-  sh_ls[tid] = ls;
   sh_c1v[tid] = b1v;
   sh_c1i[tid] = b1q >= 0 ? code_idx(b1q) : INT_MAX;
   sh_c2v[tid] = b2v;
   sh_c2i[tid] = b2q >= 0 ? code_idx(b2q) : INT_MAX;
   __syncthreads();
   if (wid != 0) return;
-  // wave 0: segment (max, sum) from the 256 lanes
-  float m4 = NINF;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) m4 = fmaxf(m4, sh_lm[lane + j * kWave]);
-  const float M = wave_max(m4);
-  float s4 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lmj = sh_lm[lane + j * kWave];
-    s4 += lmj > NINF ? sh_ls[lane + j * kWave] * __builtin_amdgcn_exp2f((lmj - M) * c) : 0.f;
-  }
-  const double S = wave_sum((double)s4);
-  // wave 0: the segment's top k.  Lane l owns source lanes l + 64 j (j < 4)
-  // and their two candidates' keys; each round takes the wave's largest key.
-  // A source lane's third best is needed only when both of its candidates
-  // were taken; the whole wave then rescans that lane's elements.
+  // lane l owns source lanes l + 64 j (j < 4) and their two candidates' keys
   using KT = TopkKey<DT>;
   using Key = typename KT::T;
   Key ck[8];
@@ -361,6 +330,169 @@ __global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) ck[t] = (lane == ol && t == tso) ? nb : ck[t];
+  }
+}
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_topk_sweep(TreeExpandParams P) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  constexpr int EPV = 16 / ES;
+  static_assert(kLaneElems % kWave == 0, "a rescan splits a lane's elements evenly over the wave");
+  static_assert(kBlock / kWave * kWave == kBlock && kBlock == 4 * kWave, "wave 0 owns four lanes' records per lane");
+  __shared__ float sh_lm[kBlock], sh_ls[kBlock], sh_c1v[kBlock], sh_c2v[kBlock];
+  __shared__ int sh_c1i[kBlock], sh_c2i[kBlock];
+  __shared__ int sh_cl[kFastLanes];                 // candidate lanes of the threshold rescan
+  __shared__ float sh_lv[kFastList];                // logits at or above the threshold
+  __shared__ int sh_li[kFastList];
+  __shared__ int sh_nc, sh_cnt;
+  __shared__ float sh_T;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const long long row = blockIdx.x / P.nseg;
+  const int s = (int)(blockIdx.x - row * P.nseg);
+  TopkPart* out = P.part + blockIdx.x;
+  const long long V = P.V;
+  const float NINF = -__builtin_huge_valf();
+  if (P.frontier[row] < 0) {
+    if (tid < kTopkMax) {
+      out->v[tid] = NINF;
+      out->idx[tid] = INT_MAX;
+    }
+    if (tid == 0) {
+      out->m = NINF;
+      out->s = 0.f;
+    }
+    return;
+  }
+  if (tid == 0) {
+    sh_nc = 0;
+    sh_cnt = 0;
+  }
+  const long long e0 = (long long)s * P.seg_elems;
+  const long long e1 = e0 + P.seg_elems < V ? e0 + P.seg_elems : V;
+  const char* rowp = static_cast<const char*>(P.logits) + row * V * ES;
+  // One pass over the lane's chunks: its max and its exponential sum
+  // against its running max (rescaled when the max grows).
+  float ls = 0.f, lm = NINF;
+  const float c = P.tc.c_hi;
+  topk_stream<DT, ALIGNED>(rowp, e0, e1, tid, [&](int, float (&z)[kTreeRun]) {
+    float cm = z[0];
+#pragma unroll
+    for (int q = 1; q < kTreeRun; ++q) cm = fmaxf(cm, z[q]);
+    if (cm > lm) {
+      ls = lm > NINF ? ls * __builtin_amdgcn_exp2f((lm - cm) * c) : 0.f;
+      lm = cm;
+    }
+    if (lm > NINF) {
+      float cs = 0.f;
+#pragma unroll
+      for (int q = 0; q < kTreeRun; ++q) cs += __builtin_amdgcn_exp2f((z[q] - lm) * c);
+      ls += cs;
+    }
+  });
+  sh_lm[tid] = lm;
+  sh_ls[tid] = ls;
+  __syncthreads();
+  // wave 0: the segment's (max, sum), and the threshold T, the k-th largest
+  // lane max counted with multiplicity.  At least k lanes hold a logit at or
+  // above T, so every logit of the segment's top k is at or above T and lies
+  // in a lane whose max reaches T: the candidate lanes.
+  using KT = TopkKey<DT>;
+  using Key = typename KT::T;
+  float M = NINF;
+  double S = 0.0;
+  if (wid == 0) {
+    float lmj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lmj[j] = sh_lm[lane + j * kWave];
+    M = wave_max(fmaxf(fmaxf(lmj[0], lmj[1]), fmaxf(lmj[2], lmj[3])));
+    float s4 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s4 += lmj[j] > NINF ? sh_ls[lane + j * kWave] * __builtin_amdgcn_exp2f((lmj[j] - M) * c) : 0.f;
+    S = wave_sum((double)s4);
+    // k rounds over (lane max, lane) keys, one instance taken per round
+    Key kk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kk[j] = KT::make(lmj[j], (int)e0 + lane + j * kWave, e0);
+    Key g = 0;
+    for (int r = 0; r < P.k; ++r) {
+      const Key b01 = kk[0] > kk[1] ? kk[0] : kk[1], b23 = kk[2] > kk[3] ? kk[2] : kk[3];
+      g = KT::wmax(b01 > b23 ? b01 : b23);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kk[j] = kk[j] == g ? (Key)0 : kk[j];
+    }
+    const float T = KT::value(g);
+    int nc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool sel = lmj[j] >= T;
+      const unsigned long long m = __ballot(sel);
+      const int at = nc + (int)__popcll(m & ((1ull << lane) - 1ull));
+      if (sel && at < kFastLanes) sh_cl[at] = lane + j * kWave;
+      nc += (int)__popcll(m);
+    }
+    if (lane == 0) {
+      sh_nc = nc;
+      sh_T = T;
+    }
+  }
+  __syncthreads();
+  const int nc = sh_nc;
+  bool fast = nc <= kFastLanes;
+  if (fast) {
+    // rescan the candidate lanes; collect their logits at or above T
+    const float T = sh_T;
+    auto keep = [&](float v, long long gi) {
+      if (v >= T) {
+        const int at = atomicAdd(&sh_cnt, 1);
+        if (at < kFastList) {
+          sh_lv[at] = v;
+          sh_li[at] = (int)gi;
+        }
+      }
+    };
+    if constexpr (ALIGNED) {
+      // one 16-byte vector per item: vector (ch, k) of candidate lane src
+      constexpr int KV = kTreeRun / EPV, kLaneVecs = kTreeChunks * KV;
+      for (int it = tid; it < nc * kLaneVecs; it += kBlock) {
+        const int src = sh_cl[it / kLaneVecs], vj = it % kLaneVecs;
+        const long long gb = topk_elem<EPV>(e0, vj / KV, (vj % KV) * EPV, src);
+        if (gb < e1) {                                     // whole vectors: in or out of the segment
+          float z[EPV];
+          unpack<DT>(*reinterpret_cast<const v4i*>(rowp + gb * ES), z);
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) keep(z[i], gb + i);
+        }
+      }
+    } else {
+      for (int e = tid; e < nc * kLaneElems; e += kBlock) {
+        const int src = sh_cl[e / kLaneElems], qq = e % kLaneElems;
+        const long long gi = topk_elem<EPV>(e0, qq / kTreeRun, qq % kTreeRun, src);
+        if (gi < e1) keep(load_elem<DT>(rowp, gi), gi);
+      }
+    }
+    __syncthreads();
+    fast = sh_cnt <= kFastList;
+  }
+  if (fast) {
+    if (wid != 0) return;
+    // rank the collected logits (lane c holds entry c) by (value desc, index asc)
+    using KT = TopkKey<DT>;
+    using Key = typename KT::T;
+    const int cnt = sh_cnt;
+    const Key key = lane < cnt ? KT::make(sh_lv[lane], sh_li[lane], e0) : (Key)0;
+    int rank = 0;
+    for (int c2 = 0; c2 < cnt; ++c2) rank += (int)(KT::readlane(key, c2) > key);
+    if (lane < cnt && rank < P.k) {
+      out->v[rank] = KT::value(key);
+      out->idx[rank] = KT::index(key, e0);
+    }
+    for (int r = cnt + lane; r < P.k; r += kWave) {       // fewer logits than k in the segment
+      out->v[r] = NINF;
+      out->idx[r] = INT_MAX;
+    }
+  } else {
+    topk_pairs<DT, ALIGNED>(P, rowp, e0, e1, tid, out, sh_c1v, sh_c2v, sh_c1i, sh_c2i);
+    if (wid != 0) return;
   }
   if (lane == 0) {
     out->m = M;
