@@ -282,3 +282,39 @@ def test_tree_expand_clustered_and_tied_topk(dtype):
     assert np.array_equal(np.isfinite(gs[0, sl]), fin)
     assert np.max(np.abs(gs[0, sl][fin] - t["score"][sl][fin])) < SCORE_TOL
     _check_frontier(nf[0], t, want, 1 + K_in, K_in * k, K_out)
+
+
+def test_tree_expand_largest_frontier():
+    # 64 frontier rows x 16 children = 1024 candidates (the per-sequence
+    # limits): eight waves loop over the rows, and every thread ranks two
+    # children for the next frontier of 64
+    B, K_in, V, k, K_out, T = 2, 64, 3000, 16, 64, 0.9
+    cap = 1 + K_in + K_in * k
+    rng = np.random.default_rng(33)
+    tables = []
+    for b in range(B):
+        t = new_table(cap, b)
+        for f in range(K_in):
+            t["parent"][1 + f], t["token"][1 + f] = 0, f
+            t["score"][1 + f], t["depth"][1 + f] = -0.01 * (f % 7), 1
+        tables.append(t)
+    frontier = np.tile(np.arange(1, K_in + 1, dtype=np.int32), (B, 1))
+    frontier[1, 5] = -1                                  # an empty slot
+    rows = rng.normal(0, 1.5, (B, K_in, V))
+    rows[0, :, 17] = 4.0                                 # equal logits across rows
+    raw = f32_to_bf16_bits(rows.astype(np.float32))
+    gt = _gpu_table(tables, cap)
+    nf = L.tree_expand(to_dev(raw), to_dev(frontier), gt, 1 + K_in, T, k, K_out).cpu().numpy()
+    gp, gtok, gs, gd = (x.cpu().numpy() for x in gt)
+    off = 1 + K_in
+    flips = 0
+    for b in range(B):
+        want = expand_step(tables[b], frontier[b], _decode(raw[b], "bf16"), T, k, K_out, off)
+        sl = slice(off, off + K_in * k)
+        assert np.array_equal(gtok[b, sl], tables[b]["token"][sl])
+        assert np.array_equal(gp[b, sl], tables[b]["parent"][sl]) and np.array_equal(gd[b, sl], tables[b]["depth"][sl])
+        fin = np.isfinite(tables[b]["score"][sl])
+        assert np.array_equal(np.isfinite(gs[b, sl]), fin)
+        assert np.max(np.abs(gs[b, sl][fin] - tables[b]["score"][sl][fin])) < SCORE_TOL
+        flips += _check_frontier(nf[b], tables[b], want, off, K_in * k, K_out)
+    assert flips <= 1
