@@ -15,7 +15,9 @@
 //
 // Workgroup tile 256 x 256, K step 32, four waves in a 2 x 2 grid of
 // 128 x 128 wave tiles, each a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 with
-// 256 fp32 accumulators per lane.
+// 256 fp32 accumulators per lane.  When at most 192 rows remain for the last
+// M tile it is 192 x 256 instead (96 x 128 wave tiles, 3 x 4 MFMA blocks),
+// so M = 704 does not issue the MFMAs of 768 rows.
 //
 // Operand staging: the global loads write straight into LDS (buffer loads
 // with the LDS destination; lane i of one such load fills bytes 16 i .. 16 i
@@ -118,62 +120,62 @@ constexpr int kWDvElem = 0;  // W[K][N], N % 8 != 0: element loads through regis
 constexpr int kWDvDma = 1;   // W[K][N]: LDS-DMA, transposing LDS reads
 constexpr int kWVd = 2;      // W[N][K]: LDS-DMA, plain LDS reads (like A)
 
-template <int WL>
-__global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int ntiles) {
-  // one LDS object per ring slot: the A stage, then the W stage
-  __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BM * BK], s1[2 * BM * BK], s2[2 * BM * BK],
-      s3[2 * BM * BK];
-  uint16_t* const SA[NS] = {s0, s1, s2, s3};
-  uint16_t* const SB[NS] = {s0 + BM * BK, s1 + BM * BK, s2 + BM * BK, s3 + BM * BK};
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+// One workgroup tile: rows m0 .. m0 + 64 MI - 1 of C (MI = 4: 256 rows; MI =
+// 3: 192 rows, the last M tile when at most 192 rows remain, so that M = 704
+// issues the MFMAs of 704 rows rather than 768), columns n0 .. n0 + 255.
+// The four waves form a 2 x 2 grid of (32 MI) x 128 wave tiles.
+template <int WL, int MI>
+__device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long long n0, uint16_t* const* SA,
+                                            uint16_t* const* SB, int lane, int wid) {
+  constexpr int TM = 64 * MI;                  // rows of the tile
+  constexpr int LA = TM * BK / 8 / 256;        // A loads per wave and K step (= MI)
+  static_assert(MI == 3 || MI == 4, "tile heights 192 and 256");
   const int wm = wid >> 1, wn = wid & 1;
-  // XCD-aware tile order: slot s on XCD x takes N tile (s / mtiles) * 8 + x
-  const int w = blockIdx.x;
-  const int xcd = w % kXcd, slot = w / kXcd;
-  const int mt = slot % mtiles;
-  const int nt = (slot / mtiles) * kXcd + xcd;
-  if (nt >= ntiles) return;
-  const int m0 = mt * BM;
-  const long long n0 = (long long)nt * BN;
   const int M = P.M, K = P.K;
   const long long N = P.N;
 
   // A rows past M read as zero through the descriptor bound
-  const int arows = min(BM, M - m0);
+  const int arows = min(TM, M - m0);
   const v4i ra = rsrc_words(P.A + (long long)m0 * K, (uint32_t)((long long)arows * K * 2));
   const uint16_t* const wtile = P.W + n0;
   const long long wtotal = (long long)K * N - n0;  // elements of W from wtile on
 
-  // Chunk p of a stage (p = 64 (4 wid + t) + lane) is what this lane fetches
-  // in its t-th load of the step.
-  uint32_t aoff[kLoadsPerWave], boff[kLoadsPerWave];
+  // Chunk p of a stage (p = 64 (L wid + t) + lane, L loads per wave) is what
+  // this lane fetches in its t-th load of the step: aoff for the A stage (LA
+  // loads), voff for a W[N][K] stage and boff for a W[K][N] stage (four
+  // loads each).
+  uint32_t aoff[LA], voff[kLoadsPerWave], boff[kLoadsPerWave];
+#pragma unroll
+  for (int t = 0; t < LA; ++t) {
+    const int p = (wid * LA + t) * 64 + lane;
+    const int ra_ = p >> 2, pca = p & 3;
+    aoff[t] = (uint32_t)(ra_ * K * 2 + 16 * (pca ^ swz_a(ra_)));
+  }
 #pragma unroll
   for (int t = 0; t < kLoadsPerWave; ++t) {
     const int p = (wid * kLoadsPerWave + t) * 64 + lane;
     const int ra_ = p >> 2, pca = p & 3;
-    aoff[t] = (uint32_t)(ra_ * K * 2 + 16 * (pca ^ swz_a(ra_)));
+    voff[t] = (uint32_t)(ra_ * K * 2 + 16 * (pca ^ swz_a(ra_)));
     const int rb = p >> 5, pcb = p & 31;
     const int cb = 2 * ((pcb >> 1) ^ swz_b(rb)) + (pcb & 1);  // logical chunk of that slot
     boff[t] = (uint32_t)((long long)rb * N * 2 + 16 * cb);
   }
 
-  // load q (0..3: A chunks, 4..7: W chunks) of K step ks into ring slot S;
-  // rb = the W descriptor of that step
+  // load q (0..LA-1: A chunks, LA..LA+3: W chunks) of K step ks into ring
+  // slot S; rb = the W descriptor of that step
   auto issue_one = [&](auto Sc, int ks, int q, const v4i& rb) {
     constexpr int S = decltype(Sc)::value;
     const int k0 = ks * BK;
-    if (q < kLoadsPerWave) {
-      dma16(ra, lds_addr(SA[S] + (wid * kLoadsPerWave + q) * 512), aoff[q], (uint32_t)k0 * 2u);
+    if (q < LA) {
+      dma16(ra, lds_addr(SA[S] + (wid * LA + q) * 512), aoff[q], (uint32_t)k0 * 2u);
     } else if (WL == kWDvDma) {
-      const int t = q - kLoadsPerWave;
+      const int t = q - LA;
       dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), boff[t], 0u);
     } else if (WL == kWVd) {
-      // rows n0 .. n0 + 255 of W[N][K]: the same tile shape and swizzle as A
-      const int t = q - kLoadsPerWave;
-      dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), aoff[t], (uint32_t)k0 * 2u);
-    } else if (q == kLoadsPerWave) {
+      // rows n0 .. n0 + 255 of W[N][K]: the same row layout and swizzle as A
+      const int t = q - LA;
+      dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), voff[t], (uint32_t)k0 * 2u);
+    } else if (q == LA) {
       // element loads of the whole W stage; columns past N read as zero
       const long long kbase = (long long)k0 * N;
 #pragma unroll
@@ -203,15 +205,15 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
     return rsrc_words(wtile + kbase, (uint32_t)min((wtotal - kbase) * 2, (long long)BK * N * 2));
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // A operand: row wm*128 + 32 i + (lane % 32), chunk kk/8 + lane/32; the
+  // A operand: row wm*32*MI + 32 i + (lane % 32), chunk kk/8 + lane/32; the
   // row's swizzle only depends on lane % 16
   const int arow = lane & 31, achk = lane >> 5, asw = swz_a(arow);
   // B operand (16-lane group g, lane jl in it): rows kk + 8 (g/2) + jl/4
@@ -226,15 +228,15 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
 
   // operand fragments: set 0 holds the k sub-step kk = 0 of a K step, set 1
   // the sub-step kk = 16
-  bf16x8 fa[2][4], fb[2][4];
-  // fragment pair idx of sub-step H: A rows wm*128 + 32 idx.., W columns
-  // wn*128 + 32 idx..
+  bf16x8 fa[2][MI], fb[2][4];
+  // fragment pair idx of sub-step H: A rows wm*32*MI + 32 idx.. (idx < MI),
+  // W columns wn*128 + 32 idx..
   auto read_pair = [&](auto Sc, auto Hc, int idx) {
     constexpr int S = decltype(Sc)::value, H = decltype(Hc)::value, kk = 16 * H;
     const uint16_t* As = SA[S];
     const uint16_t* Bs = SB[S];
     const int ac = ((kk >> 3) + achk) ^ asw;
-    fa[H][idx] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + idx * 32 + arow) * BK + ac * 8);
+    if (idx < MI) fa[H][idx] = *reinterpret_cast<const bf16x8*>(As + (wm * 32 * MI + idx * 32 + arow) * BK + ac * 8);
     if (WL == kWVd) {
       fb[H][idx] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 128 + idx * 32 + arow) * BK + ac * 8);
     } else {
@@ -261,7 +263,9 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
 
   // loads in flight per K step and wave (the element path waits for its own
   // W loads, leaving only the A loads)
-  constexpr int kGroup = WL == kWDvElem ? kLoadsPerWave : 2 * kLoadsPerWave;
+  constexpr int kGroup = WL == kWDvElem ? LA : LA + kLoadsPerWave;
+  constexpr int kMf = 4 * MI;                  // MFMAs per wave and K sub-step
+  constexpr int kPairs = MI == 4 ? 12 : 9;     // MFMA / LDS-read pairs of the first half
   const int nk = K / BK;
 
   // One K step in two halves.  First half: the kk = 0 MFMAs, while the
@@ -277,14 +281,14 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
     constexpr int S = decltype(Sc)::value;
     read_frags(Sc, H1{});
 #pragma unroll
-    for (int q = 0; q < 16; ++q) mfma(H0{}, q);
-    // interleave: one MFMA, one LDS read, twelve times; then four MFMAs
+    for (int q = 0; q < kMf; ++q) mfma(H0{}, q);
+    // interleave: one MFMA, one LDS read, kPairs times; then the other MFMAs
 #pragma unroll
-    for (int r = 0; r < 12; ++r) {
+    for (int r = 0; r < kPairs; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMf - kPairs, 0);
     __builtin_amdgcn_sched_barrier(0);
     // this wave's loads of step ks + 1 are done once at most the group of
     // step ks + 2 remains outstanding
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
     // steady stream (a load that finds its queue full stalls this wave's
     // MFMA issue behind it); the fragment reads fill the odd slots
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kMf; ++q) {
       mfma(H1{}, q);
       if ((q & 1) == 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -307,6 +311,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
         read_pair(std::integral_constant<int, (S + 1) % NS>{}, H0{}, q >> 1);
       }
     }
+    // loads left over when the step has fewer MFMA slots than loads (MI = 3)
+#pragma unroll
+    for (int e = kMf / 2; e < LA + kLoadsPerWave; ++e)
+      issue_one(std::integral_constant<int, (S + 3) % NS>{}, kl, e, rb);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -317,13 +325,13 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
     const int k1 = min(1, nk - 1), k2 = min(2, nk - 1);
     const v4i r0 = w_rsrc(0);
 #pragma unroll
-    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S0{}, 0, q, r0);
+    for (int q = 0; q < LA + kLoadsPerWave; ++q) issue_one(S0{}, 0, q, r0);
     const v4i r1 = w_rsrc(k1);
 #pragma unroll
-    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S1{}, k1, q, r1);
+    for (int q = 0; q < LA + kLoadsPerWave; ++q) issue_one(S1{}, k1, q, r1);
     const v4i r2 = w_rsrc(k2);
 #pragma unroll
-    for (int q = 0; q < 2 * kLoadsPerWave; ++q) issue_one(S2{}, k2, q, r2);
+    for (int q = 0; q < LA + kLoadsPerWave; ++q) issue_one(S2{}, k2, q, r2);
     wait_vm<2 * kGroup>();
     asm volatile("s_barrier" ::: "memory");
     read_frags(S0{}, H0{});
@@ -346,8 +354,8 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   const long long c0 = n0 + wn * 128;
   const bool vec = (N & 3) == 0 && c0 + 128 <= N;   // uniform per wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < MI; ++i) {
+    const int row = m0 + wm * 32 * MI + i * 32 + (lane & 31);
     if (row >= M) continue;
     float* const crow = P.C + (long long)row * N + c0 + 4 * (lane >> 5);
     if (vec) {
@@ -370,6 +378,28 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
         }
     }
   }
+}
+
+template <int WL>
+__global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int ntiles) {
+  // one LDS object per ring slot: the A stage, then the W stage
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BM * BK], s1[2 * BM * BK], s2[2 * BM * BK],
+      s3[2 * BM * BK];
+  uint16_t* const SA[NS] = {s0, s1, s2, s3};
+  uint16_t* const SB[NS] = {s0 + BM * BK, s1 + BM * BK, s2 + BM * BK, s3 + BM * BK};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware tile order: slot s on XCD x takes N tile (s / mtiles) * 8 + x
+  const int w = blockIdx.x;
+  const int xcd = w % kXcd, slot = w / kXcd;
+  const int mt = slot % mtiles;
+  const int nt = (slot / mtiles) * kXcd + xcd;
+  if (nt >= ntiles) return;
+  const int m0 = mt * BM;
+  const long long n0 = (long long)nt * BN;
+  if (P.M - m0 <= 192) lmhead_tile<WL, 3>(P, m0, n0, SA, SB, lane, wid);   // uniform
+  else lmhead_tile<WL, 4>(P, m0, n0, SA, SB, lane, wid);
 }
 
 }  // namespace

@@ -421,7 +421,10 @@ def test_lmhead_project_small_shapes_exact_on_integers(layout):
     # V tails, V % 8 != 0 (element-load path of the [d, V] layout), and K
     # with fewer steps than the load ring
     rng = np.random.default_rng(2)
-    for M, d, V in ((3, 64, 997), (130, 128, 1000), (1, 256, 8), (257, 64, 129), (300, 192, 513)):
+    # M tiles are 256 rows, the last one 192 when at most 192 rows remain:
+    # M = 192, 193, 448 and 450 sit on either side of those limits
+    for M, d, V in ((3, 64, 997), (130, 128, 1000), (1, 256, 8), (257, 64, 129), (300, 192, 513),
+                    (192, 64, 300), (193, 64, 260), (448, 64, 257), (450, 128, 264)):
         H = rng.integers(-4, 5, (M, d)).astype(np.float32)
         W = rng.integers(-4, 5, (d, V)).astype(np.float32)
         Wl = W if layout == "dv" else np.ascontiguousarray(W.T)
