@@ -10,7 +10,7 @@
 // lmhead_verify first gathers target and draft features into one block so
 // the head is streamed once for both), C fp32.  W comes in either layout:
 // [N, K] with the feature dimension innermost (a linear layer's weight as
-// checkpoints store it; the fast path), or [K, N] with the vocabulary
+// checkpoints store it), or [K, N] with the vocabulary
 // innermost.
 //
 // Workgroup tile 256 x 256, K step 32, four waves in a 2 x 2 grid of
