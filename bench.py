@@ -414,9 +414,12 @@ def main():
         fcat = torch.cat([ft, fd], 0)
         # the same head in the [V, d] layout a linear layer's weight is stored in
         Wvd = W.t().contiguous()
+        # the projection as lmhead_verify runs it: feature rows staged in a
+        # workspace first (lmhead_project_staged)
+        pws = torch.empty(L.lib.lmhead_project_workspace_bytes(M, ed), dtype=torch.uint8, device=dev)
         for name, layout, Wl in (("w_vd", L.W_VD, Wvd), ("w_dv", L.W_DV, W)):
             def pstep(i, Wl=Wl, layout=layout):
-                L.lmhead_project(fcat, Wl, out=proj_out, layout=layout)
+                L.lmhead_project(fcat, Wl, out=proj_out, layout=layout, ws=pws)
 
             def estep(i, Wl=Wl, layout=layout):
                 L.lmhead_verify(ft, fd, Wl, ex, eu, float(ew["temperature"]), ws=ews, out=eout, layout=layout)

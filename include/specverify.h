@@ -320,6 +320,24 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
                            spec_wlayout wl, int V, float* out_logits, hipStream_t s);
 
 /*
+ * lmhead_project_staged -- the same product as lmhead_project, bit for bit,
+ * with the feature rows first copied into the workspace as contiguous 16 KB
+ * blocks (256 rows x 32 features each), so that every GEMM load of them reads
+ * whole cache lines; faster than lmhead_project, most for [V, d] weights.
+ * Pages: as lmhead_project.
+ *
+ * Arguments as lmhead_project; ws is caller-owned device memory, 256-byte
+ * aligned, of at least lmhead_project_workspace_bytes(M, d) bytes
+ * (SPEC_EWORKSPACE otherwise), overwritten by the call.
+ */
+spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint16_t* W,
+                                  spec_wlayout wl, int V, float* out_logits, void* ws,
+                                  size_t ws_bytes, hipStream_t s);
+
+/* Workspace bytes lmhead_project_staged needs; 0 for an invalid (M, d). */
+size_t lmhead_project_workspace_bytes(int M, int d);
+
+/*
  * lmhead_verify -- EAGLE-style verification: the target features
  * (B*(gamma+1) rows, row b*(gamma+1)+i) and the draft features (B*gamma
  * rows, row b*gamma+i) go through the shared LM head into float32 logits

@@ -42,6 +42,8 @@ _SIGS = {
     "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
                                      _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
+    "lmhead_project_staged": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "lmhead_project_workspace_bytes": (_sz, [_i, _i]),
     "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
     "spec_tree_expand": (_i, [_vp, _i, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
@@ -236,15 +238,23 @@ def _head_dims(W, layout):
     raise ValueError("layout must be W_DV or W_VD")
 
 
-def lmhead_project(feat, W, out=None, layout=W_DV):
+def lmhead_project(feat, W, out=None, layout=W_DV, ws=None):
     """feat [M, d] bf16 bits, W bf16 bits ([d, V] for W_DV, [V, d] for W_VD)
-    -> fp32 logits [M, V]."""
+    -> fp32 logits [M, V].  With ws (a uint8 tensor of at least
+    lmhead_project_workspace_bytes(M, d) bytes, or True to allocate one) the
+    call goes through lmhead_project_staged: the same logits, faster."""
     M, d = feat.shape
     _, V = _head_dims(W, layout)
     if out is None:
         out = torch.empty((M, V), dtype=torch.float32, device=feat.device)
-    _check(lib.lmhead_project(_ptr(feat), M, d, _ptr(W), layout, V, _ptr(out), _stream(feat.device)),
-           "lmhead_project")
+    if ws is None:
+        _check(lib.lmhead_project(_ptr(feat), M, d, _ptr(W), layout, V, _ptr(out), _stream(feat.device)),
+               "lmhead_project")
+        return out
+    if ws is True:
+        ws = torch.empty(lib.lmhead_project_workspace_bytes(M, d), dtype=torch.uint8, device=feat.device)
+    _check(lib.lmhead_project_staged(_ptr(feat), M, d, _ptr(W), layout, V, _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(feat.device)), "lmhead_project_staged")
     return out
 
 

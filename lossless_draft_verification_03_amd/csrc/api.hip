@@ -106,7 +106,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
                                                             : (size_t)seqs * nseg2 * kDrawSub * 8;
   L->segsum = o; o = up(o + segsum_bytes);
   L->hcat = o;
-  if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)d * 2);
+  if (mode == SPEC_MODE_LMHEAD) o = up(o + lmhead_staged_bytes(rows, d));
   L->logits = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * (size_t)V * 4);
   L->total = o;
@@ -514,6 +514,39 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
   p.K = d;
   p.N = V;
   p.C = out_logits;
+  p.a_staged = 0;
+  return hip_status(launch_lmhead(p, s));
+}
+
+size_t lmhead_project_workspace_bytes(int M, int d) {
+  if (M < 1 || M > (1 << 22) || d < 64 || d % 64 != 0 || d > (1 << 20)) return 0;
+  return lmhead_staged_bytes(M, d);
+}
+
+spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint16_t* W, spec_wlayout wl, int V,
+                                  float* out_logits, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M < 1 || M > (1 << 22) || d < 64 || d % 64 != 0 || d > (1 << 20) || V < 1) return SPEC_EINVAL;
+  if (V >= (1 << 25) || (wl != SPEC_W_DV && wl != SPEC_W_VD)) return SPEC_EINVAL;
+  if (!feat || !W || !out_logits) return SPEC_EINVAL;
+  if (!aligned(feat, 16) || !aligned(W, 16) || !aligned(out_logits, 16)) return SPEC_EALIGN;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < lmhead_staged_bytes(M, d)) return SPEC_EWORKSPACE;
+  LmHeadStageParams sp;
+  sp.src0 = feat;
+  sp.rows0 = M;
+  sp.src1 = feat;
+  sp.M = M;
+  sp.K = d;
+  sp.dst = static_cast<uint16_t*>(ws);
+  if (launch_lmhead_stage(sp, s) != hipSuccess) return SPEC_EHIP;
+  LmHeadParams p;
+  p.A = sp.dst;
+  p.M = M;
+  p.W = W;
+  p.w_vd = wl == SPEC_W_VD;
+  p.K = d;
+  p.N = V;
+  p.C = out_logits;
+  p.a_staged = 1;
   return hip_status(launch_lmhead(p, s));
 }
 
@@ -538,18 +571,19 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   const spec_status w = check_ws(ws, ws_bytes, L);
   if (w != SPEC_OK) return w;
   float* Z = at<float>(ws, L.logits);
-  // the GEMM reads all B(2 gamma + 1) feature rows from one block
-  const size_t tbytes = (size_t)B * (gamma + 1) * (size_t)d * 2, dbytes = (size_t)B * gamma * (size_t)d * 2;
-  const uint16_t* H = target_feat;
-  if ((const char*)draft_feat != (const char*)target_feat + tbytes) {
-    uint16_t* hc = at<uint16_t>(ws, L.hcat);
-    if (hipMemcpyAsync(hc, target_feat, tbytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return SPEC_EHIP;
-    if (hipMemcpyAsync((char*)hc + tbytes, draft_feat, dbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return SPEC_EHIP;
-    H = hc;
-  }
+  // the GEMM reads all B(2 gamma + 1) feature rows, target rows first, from
+  // one staged block (so W streams once for both)
+  LmHeadStageParams sp;
+  sp.src0 = target_feat;
+  sp.rows0 = B * (gamma + 1);
+  sp.src1 = draft_feat;
+  sp.M = B * (2 * gamma + 1);
+  sp.K = d;
+  sp.dst = at<uint16_t>(ws, L.hcat);
+  if (launch_lmhead_stage(sp, s) != hipSuccess) return SPEC_EHIP;
   LmHeadParams p;
-  p.A = H;
+  p.A = sp.dst;
+  p.a_staged = 1;
   p.M = B * (2 * gamma + 1);
   p.W = W;
   p.w_vd = wl == SPEC_W_VD;

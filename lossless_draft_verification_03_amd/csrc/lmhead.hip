@@ -134,9 +134,15 @@ __device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long 
   const int M = P.M, K = P.K;
   const long long N = P.N;
 
-  // A rows past M read as zero through the descriptor bound
+  // A rows past M read as zero through the descriptor bound (row-major A),
+  // or as the zeros the staging wrote (staged A: the tile's blocks of 256
+  // rows x 64 bytes, one per K step)
+  const bool staged = P.a_staged != 0;
   const int arows = min(TM, M - m0);
-  const v4i ra = rsrc_words(P.A + (long long)m0 * K, (uint32_t)((long long)arows * K * 2));
+  const v4i ra = staged ? rsrc_words(P.A + (long long)(m0 / BM) * (K / BK) * (BM * BK), (uint32_t)((K / BK) * BM * BK * 2))
+                        : rsrc_words(P.A + (long long)m0 * K, (uint32_t)((long long)arows * K * 2));
+  const uint32_t arow_bytes = staged ? (uint32_t)(BK * 2) : (uint32_t)K * 2u;   // A row stride
+  const uint32_t astep_bytes = staged ? (uint32_t)(BM * BK * 2) : (uint32_t)(BK * 2);   // per K step
   const uint16_t* const wtile = P.W + n0;
   const long long wtotal = (long long)K * N - n0;  // elements of W from wtile on
 
@@ -149,7 +155,7 @@ __device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long 
   for (int t = 0; t < LA; ++t) {
     const int p = (wid * LA + t) * 64 + lane;
     const int ra_ = p >> 2, pca = p & 3;
-    aoff[t] = (uint32_t)(ra_ * K * 2 + 16 * (pca ^ swz_a(ra_)));
+    aoff[t] = (uint32_t)ra_ * arow_bytes + (uint32_t)(16 * (pca ^ swz_a(ra_)));
   }
 #pragma unroll
   for (int t = 0; t < kLoadsPerWave; ++t) {
@@ -167,7 +173,7 @@ __device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long 
     constexpr int S = decltype(Sc)::value;
     const int k0 = ks * BK;
     if (q < LA) {
-      dma16(ra, lds_addr(SA[S] + (wid * LA + q) * 512), aoff[q], (uint32_t)k0 * 2u);
+      dma16(ra, lds_addr(SA[S] + (wid * LA + q) * 512), aoff[q], (uint32_t)ks * astep_bytes);
     } else if (WL == kWDvDma) {
       const int t = q - LA;
       dma16(rb, lds_addr(SB[S] + (wid * kLoadsPerWave + t) * 512), boff[t], 0u);
@@ -402,7 +408,40 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   else lmhead_tile<WL, 4>(P, m0, n0, SA, SB, lane, wid);
 }
 
+// One 16-byte chunk per thread: chunk q of the staged buffer is chunk q % 4
+// of row (q / 4) % 256 of block q / 1024 (block = M tile * K/32 + K step).
+// The writes are contiguous; each row's four chunks are one 64-byte read.
+__global__ __launch_bounds__(256) void k_lmhead_stage(LmHeadStageParams P) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int nk = P.K / BK;
+  const long long blk = q >> 10;
+  if (blk >= (long long)((P.M + BM - 1) / BM) * nk) return;
+  const int c = (int)(q & 3), r = (int)((q >> 2) & (BM - 1));
+  const long long mt = blk / nk;
+  const int ks = (int)(blk - mt * nk);
+  const long long m = mt * BM + r;
+  v4i v = {0, 0, 0, 0};
+  if (m < P.M) {
+    const uint16_t* src = m < P.rows0 ? P.src0 + m * P.K : P.src1 + (m - P.rows0) * P.K;
+    v = *reinterpret_cast<const v4i*>(src + ks * BK + c * 8);
+  }
+  *reinterpret_cast<v4i*>(P.dst + q * 8) = v;
+}
+
 }  // namespace
+
+size_t lmhead_staged_bytes(long long M, long long K) {
+  return (size_t)((M + BM - 1) / BM) * (size_t)(K / BK) * BM * BK * 2;
+}
+
+hipError_t launch_lmhead_stage(const LmHeadStageParams& p, hipStream_t s) {
+  if (p.K % BK != 0 || p.K < BK || p.M < 1 || p.rows0 < 0 || p.rows0 > p.M) return hipErrorInvalidValue;
+  const long long chunks = (long long)lmhead_staged_bytes(p.M, p.K) / 16;
+  const long long blocks = (chunks + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_lmhead_stage, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s) {
   if (p.K % BK != 0 || p.K < BK || p.M < 1 || p.N < 1) return hipErrorInvalidValue;

@@ -128,14 +128,30 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 // ---------------------------------------------------------- LM head
 struct LmHeadParams {
-  const uint16_t* A;      // [M, K] bf16, rows 16-byte aligned
+  const uint16_t* A;      // [M, K] bf16 rows, 16-byte aligned (a_staged = 0), or the staged layout
   int M;
   const uint16_t* W;      // [K, N] bf16, N innermost (w_vd = 0) or [N, K], K innermost (w_vd = 1)
   int w_vd;
   int K, N;
   float* C;               // [M, N] fp32
+  int a_staged;
 };
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s);
+
+// Staged feature rows: for every 256-row M tile mt and K step ks (32
+// features) one contiguous 16 KB block, 256 rows x 64 bytes, at element
+// offset (mt * K / 32 + ks) * 8192; rows past M are zero.  The GEMM then
+// reads whole cache lines for its A operand.  Rows m < rows0 come from src0,
+// the others from src1 (row m - rows0).
+struct LmHeadStageParams {
+  const uint16_t* src0;
+  int rows0;
+  const uint16_t* src1;
+  int M, K;
+  uint16_t* dst;
+};
+size_t lmhead_staged_bytes(long long M, long long K);
+hipError_t launch_lmhead_stage(const LmHeadStageParams& p, hipStream_t s);
 
 // ---------------------------------------------------------- KV compaction
 struct KvParams {

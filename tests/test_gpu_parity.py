@@ -428,9 +428,13 @@ def test_lmhead_project_small_shapes_exact_on_integers(layout):
         H = rng.integers(-4, 5, (M, d)).astype(np.float32)
         W = rng.integers(-4, 5, (d, V)).astype(np.float32)
         Wl = W if layout == "dv" else np.ascontiguousarray(W.T)
-        Z = L.lmhead_project(to_dev(f32_to_bf16_bits(H)), to_dev(f32_to_bf16_bits(Wl)),
-                             layout=L.W_DV if layout == "dv" else L.W_VD).cpu().numpy()
+        lay = L.W_DV if layout == "dv" else L.W_VD
+        Hd, Wd = to_dev(f32_to_bf16_bits(H)), to_dev(f32_to_bf16_bits(Wl))
+        Z = L.lmhead_project(Hd, Wd, layout=lay).cpu().numpy()
         assert np.array_equal(Z, (H.astype(np.int64) @ W.astype(np.int64)).astype(np.float32)), (M, d, V)
+        # staged feature rows: the same logits
+        Zs = L.lmhead_project(Hd, Wd, layout=lay, ws=True).cpu().numpy()
+        assert np.array_equal(Zs, Z), (M, d, V)
 
 
 @pytest.fixture(scope="module")
@@ -453,6 +457,8 @@ def test_eagle_lmhead_logits_and_verify(c5):
     # MFMA operands hold the same values in the same k order
     Wvd = W.t().contiguous()
     assert torch.equal(L.lmhead_project(ft, Wvd, layout=L.W_VD), proj)
+    assert torch.equal(L.lmhead_project(ft, W, ws=True), proj)
+    assert torch.equal(L.lmhead_project(ft, Wvd, layout=L.W_VD, ws=True), proj)
     acc2, out2 = L.lmhead_verify(ft, fd, Wvd, x, u, float(w["temperature"]), ws=ws.clone(), layout=L.W_VD)
     assert torch.equal(acc2, acc) and torch.equal(out2, out)
     del Wvd
