@@ -345,8 +345,9 @@ size_t lmhead_project_workspace_bytes(int M, int d);
  * host round trip.  Same outputs and uniforms convention as
  * spec_verify_sample.  W and its layout wl as in lmhead_project.  d must be a
  * multiple of 64.
- * Features that are not already one contiguous block (draft rows right after
- * the target rows) are first copied into the workspace.
+ * The feature rows (target rows, then draft rows) are first staged in the
+ * workspace in the blocked layout of lmhead_project_staged, so one GEMM
+ * streams W once for both.
  * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
  * the call the logits are left in the last ceil256(B(2 gamma+1) V 4) bytes
  * of the workspace: B(gamma+1) target rows, then B gamma draft rows.
