@@ -77,6 +77,14 @@ def test_other_entry_points_reject_invalid_arguments():
     assert lib.lmhead_project(FAKE, 4, 100, FAKE, 0, 10, FAKE, None) == 1
     assert lib.lmhead_project(FAKE, 4, 128, FAKE + 2, 0, 10, FAKE, None) == 3
     assert lib.lmhead_project(FAKE, 4, 128, FAKE, 2, 10, FAKE, None) == 1   # unknown weight layout
+    # staged projection: its workspace size, then the same checks plus a missing or short workspace
+    need = lib.lmhead_project_workspace_bytes(704, 4096)
+    assert need == 3 * (4096 // 32) * 256 * 64 and lib.lmhead_project_workspace_bytes(4, 100) == 0
+    assert lib.lmhead_project_staged(FAKE, 4, 100, FAKE, 0, 10, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.lmhead_project_staged(FAKE, 4, 128, FAKE + 2, 0, 10, FAKE, FAKE, 1 << 30, None) == 3
+    assert lib.lmhead_project_staged(FAKE, 4, 128, FAKE, 0, 10, FAKE, None, 1 << 30, None) == 4
+    assert lib.lmhead_project_staged(FAKE, 704, 4096, FAKE, 1, 10, FAKE, FAKE, need - 1, None) == 4
+    assert lib.lmhead_project_staged(FAKE, 4, 128, FAKE, 0, 10, FAKE, FAKE + 16, 1 << 30, None) == 4
     assert lib.lmhead_verify(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 2, 3, 96, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
     assert lib.lmhead_verify(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 3, 128, 50, 0.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
     assert lib.lmhead_verify(FAKE, FAKE, FAKE, 7, FAKE, FAKE, 2, 3, 128, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
