@@ -14,6 +14,9 @@ function that uses it):
   with positive mass.  A zero residual after a rejection (impossible in
   exact arithmetic) falls back to p.
 * Argmax ties: lowest index.
+* Invalid drafts: a drafted token outside [0, V) at any position makes the
+  sequence's verification invalid: accept_len = -1 and no tokens (the
+  tree sampler applies the same rule to its nodes).
 * Tree: parent[0] = -1 and 0 <= parent[i] < i; node 0 is the already
   committed token and is not verified; a node's token is checked against
   the argmax of its parent's row; among equally deep matching nodes the
@@ -144,10 +147,17 @@ def verify_sample_seq(zt, zd, x, u, T):
     Returns (accept_len, tokens, info) with tokens = x_0..x_{j-1}, y.
     info["tests"] lists (i, u_i, r_i) for every accept test performed;
     info["draw"] is the inverse_cdf info of the final draw.
+
+    A drafted token outside [0, V) (anywhere in x, the pages give no rule:
+    reading stated in the module docstring) returns (-1, [], info) with no
+    tests and no draw.
     """
     zt = np.asarray(zt, np.float64)
     zd = np.asarray(zd, np.float64)
     g = zd.shape[0]
+    V = zt.shape[1]
+    if any(not 0 <= int(t) < V for t in np.asarray(x)[:g]):
+        return -1, [], dict(tests=[], draw=None, w=None)
     tests = []
     j = g
     for i in range(g):
@@ -303,8 +313,15 @@ def lmhead_logits(feat, W, col_block=8192):
 
 
 def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, T):
-    """Project target features (B*(g+1) rows) and draft features (B*g rows)
-    through the shared head, then run verify_sample on the float64 logits."""
+    """EAGLE-style verification: drafted features decoded through the
+    target's own head, then verified like any draft.
+
+    [R] "EAGLE: Predict Features, Not Tokens" (the draft reuses the target's
+    LM head); [M] "EAGLE's move".  feat_t [B*(g+1), d]: row b*(g+1)+i is the
+    target feature of position i of sequence b (i = g: the bonus row);
+    feat_d [B*g, d]: row b*g+i is the drafted feature of position i; W bf16
+    bits [d, V].  The logits of both go through verify_sample in float64.
+    Returns (accept_len, out, infos, zt [B, g+1, V], zd [B, g, V])."""
     B, g = draft_tokens.shape
     zt = lmhead_logits(feat_t, W).reshape(B, g + 1, -1)
     zd = lmhead_logits(feat_d, W).reshape(B, g, -1)

@@ -458,3 +458,77 @@ def test_batched_wrappers_agree_with_per_sequence():
     j, toks, _ = oracle.verify_sample_seq(w["target"][0].astype(np.float64), w["draft"][0].astype(np.float64),
                                           w["draft_tokens"][0], w["uniforms"][0], float(w["temperature"]))
     assert acc[0] == j and list(out[0, :j + 1]) == toks and np.all(out[0, j + 1:] == -1)
+
+
+def test_invalid_draft_token_makes_sequence_invalid():
+    """The reading for drafted tokens outside [0, V): the whole sequence is
+    flagged (accept_len -1, every output -1), whichever position holds it and
+    whether or not an earlier position would already have been rejected."""
+    rng = np.random.default_rng(4)
+    g, V = 4, 9
+    zt = rng.normal(0, 1, (g + 1, V))
+    zd = rng.normal(0, 1, (g, V))
+    u = np.full(g + 1, 0.5)
+    for pos in range(g):
+        for bad in (-1, V, V + 100):
+            x = rng.integers(0, V, g)
+            x[pos] = bad
+            j, toks, info = oracle.verify_sample_seq(zt, zd, x, u, 1.0)
+            assert j == -1 and toks == [] and info["tests"] == []
+    # batched: the flagged row is all -1, its neighbours are verified as usual
+    B = 3
+    T3 = np.stack([zt] * B).astype(np.float32)
+    D3 = np.stack([zd] * B).astype(np.float32)
+    X = rng.integers(0, V, (B, g)).astype(np.int32)
+    X[1, 3] = V
+    acc, out, _ = oracle.verify_sample(T3, D3, "f32", X, np.full((B, g + 1), 0.5, np.float32), 1.0)
+    assert acc[1] == -1 and np.all(out[1] == -1)
+    assert acc[0] >= 0 and acc[2] >= 0 and out[0, acc[0]] >= 0 and out[2, acc[2]] >= 0
+
+
+def test_lmhead_verify_planted_answers():
+    """oracle.lmhead_verify against outcomes fixed by construction (it pins
+    the feature-row layout: row b*(g+1)+i target, row b*g+i draft, row
+    b*(g+1)+g the bonus row).  W = identity (d = V = 64), so a feature row
+    is its own logit row.
+
+    * Target row (b, i) is 60 at a planted token a[b][i] and 0 elsewhere, the
+      draft rows are 0 (q uniform): p(a) rounds to 1 in float64, so x_i is
+      accepted iff x_i = a[b][i], the residual at a rejection is one-hot at
+      a[b][j], and the bonus is a[b][g]: the output is greedy verification
+      against the planted tokens (the review's "Does Using a Small Model's
+      Answer Reduce Quality?": a point-mass target turns the test into the
+      greedy rule).
+    * Draft features equal to the target features (q = p): every draft is
+      accepted and the bonus is a[b][g]."""
+    from gen.synth import f32_to_bf16_bits
+    rng = np.random.default_rng(12)
+    B, g, d = 5, 4, 64
+    V = d
+    W = f32_to_bf16_bits(np.eye(d, dtype=np.float32))
+    a = rng.integers(0, V, (B, g + 1))
+    Ht = np.zeros((B * (g + 1), d), np.float32)
+    for b in range(B):
+        for i in range(g + 1):
+            Ht[b * (g + 1) + i, a[b, i]] = 60.0
+    # drafts that match the planted tokens for the first m[b] positions
+    m = np.array([0, 2, 4, 1, 3])
+    x = rng.integers(0, V, (B, g)).astype(np.int32)
+    for b in range(B):
+        x[b, :m[b]] = a[b, :m[b]]
+        if m[b] < g:
+            x[b, m[b]] = (a[b, m[b]] + 1 + rng.integers(0, V - 1)) % V      # != a
+    u = rng.uniform(0.01, 0.99, (B, g + 1)).astype(np.float32)
+    Hd0 = np.zeros((B * g, d), np.float32)
+    acc, out, _, zt, zd = oracle.lmhead_verify(f32_to_bf16_bits(Ht), f32_to_bf16_bits(Hd0), W, x, u, 1.0)
+    assert zt.shape == (B, g + 1, V) and zd.shape == (B, g, V) and np.all(zd == 0)
+    for b in range(B):
+        assert acc[b] == m[b]
+        assert list(out[b, :m[b] + 1]) == list(a[b, :m[b]]) + [a[b, m[b]]]
+        assert np.all(out[b, m[b] + 1:] == -1)
+    # q = p: draft feature row b*g+i is target feature row b*(g+1)+i
+    Hd = np.stack([Ht[b * (g + 1) + i] for b in range(B) for i in range(g)])
+    acc, out, _, _, _ = oracle.lmhead_verify(f32_to_bf16_bits(Ht), f32_to_bf16_bits(Hd), W, x, u, 1.0)
+    assert np.all(acc == g)
+    for b in range(B):
+        assert list(out[b]) == list(x[b]) + [a[b, g]]
