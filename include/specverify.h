@@ -338,26 +338,58 @@ spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint
 size_t lmhead_project_workspace_bytes(int M, int d);
 
 /*
- * lmhead_verify -- EAGLE-style verification: the target features
- * (B*(gamma+1) rows, row b*(gamma+1)+i) and the draft features (B*gamma
- * rows, row b*gamma+i) go through the shared LM head into float32 logits
- * held in the workspace, then spec_verify_sample runs on them without a
- * host round trip.  Same outputs and uniforms convention as
- * spec_verify_sample.  W and its layout wl as in lmhead_project.  d must be a
- * multiple of 64.
+ * lmhead_verify -- EAGLE-style verification: draft features are decoded
+ * through the target's own, unchanged LM head, and the result is verified
+ * like any draft.
+ * Pages: "EAGLE-3 speculative decoding review", "EAGLE: Predict Features, Not
+ * Tokens" (the LM head turns the top-layer feature into vocabulary logits;
+ * the draft reuses the target's head); "EAGLE math", "EAGLE's move" and
+ * "Why feature drafting lands a higher acceptance rate"; verification as in
+ * spec_verify_sample.
+ *
+ * target_feat  [B*(gamma+1), d] bf16 bits: row b*(gamma+1)+i is the target's
+ *              feature for position i of sequence b (i = gamma: bonus row).
+ * draft_feat   [B*gamma, d] bf16 bits: row b*gamma+i is the drafted feature
+ *              of position i.
+ * W            [d, V] bf16 bits, vocabulary innermost (lmhead_verify_wvd
+ *              takes the [V, d] layout).  No bias: z = h W.
+ * draft_tokens, uniforms, temperature, accept_len, out_tokens: as in
+ *              spec_verify_sample (p from the target rows, q from the draft
+ *              rows, both float32 logits).
+ * d a multiple of 64 (<= 2^20); 1 <= V < 2^25; gamma and B as in
+ * spec_verify_sample.  Feature and weight pointers 16-byte aligned.
  * The feature rows (target rows, then draft rows) are first staged in the
  * workspace in the blocked layout of lmhead_project_staged, so one GEMM
- * streams W once for both.
+ * streams W once for both; the logits stay in the workspace (float32, no
+ * host round trip) for the verification kernels.
  * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
  * the call the logits are left in the last ceil256(B(2 gamma+1) V 4) bytes
  * of the workspace: B(gamma+1) target rows, then B gamma draft rows.
+ * Errors: as spec_verify_sample; an invalid d gives SPEC_EINVAL.
  */
 spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat,
-                          const uint16_t* W, spec_wlayout wl, const int32_t* draft_tokens,
+                          const uint16_t* W, const int32_t* draft_tokens,
                           const float* uniforms, int B, int gamma, int d, int V,
                           float temperature, int32_t* accept_len,
                           int32_t* out_tokens, void* ws, size_t ws_bytes,
                           hipStream_t s);
+
+/*
+ * lmhead_verify_wvd -- lmhead_verify with the LM-head weight stored [V, d]
+ * (feature dimension innermost, the way a linear layer's weight is usually
+ * kept).  Pages: as lmhead_verify.
+ *
+ * W_vd [V, d] bf16 bits, 16-byte aligned; every other argument, the
+ * workspace and the outputs as in lmhead_verify.  For the same weights the
+ * logits, and so the outputs, are bit-identical to lmhead_verify's with
+ * W = W_vd^T: the GEMM feeds the MFMAs the same values in the same order.
+ */
+spec_status lmhead_verify_wvd(const uint16_t* target_feat, const uint16_t* draft_feat,
+                              const uint16_t* W_vd, const int32_t* draft_tokens,
+                              const float* uniforms, int B, int gamma, int d, int V,
+                              float temperature, int32_t* accept_len,
+                              int32_t* out_tokens, void* ws, size_t ws_bytes,
+                              hipStream_t s);
 
 /*
  * spec_probe_probs -- test probe: the full distributions the sampling path

@@ -44,7 +44,8 @@ _SIGS = {
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_project_staged": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "lmhead_project_workspace_bytes": (_sz, [_i, _i]),
-    "lmhead_verify": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "lmhead_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "lmhead_verify_wvd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_kv_compact": (_i, [_vp, _i, _i, _i, _ll, _ll, _ll, _vp, _vp, _i, _vp, _vp, _vp]),
     "spec_tree_expand": (_i, [_vp, _i, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
                               _vp]),
@@ -259,6 +260,8 @@ def lmhead_project(feat, W, out=None, layout=W_DV, ws=None):
 
 
 def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=None, out=None, layout=W_DV):
+    """lmhead_verify (W [d, V], layout W_DV) or lmhead_verify_wvd (W [V, d],
+    layout W_VD) -> (accept_len [B], out_tokens [B, g+1])."""
     B, g = draft_tokens.shape
     d, V = _head_dims(W, layout)
     dev = W.device
@@ -266,10 +269,10 @@ def lmhead_verify(feat_t, feat_d, W, draft_tokens, uniforms, temperature, ws=Non
         out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
     acc, toks = out
     w = _workspace(MODE_LMHEAD, B, g, V, d, dev, ws)
-    _check(lib.lmhead_verify(_ptr(feat_t), _ptr(feat_d), _ptr(W), layout, _ptr(draft_tokens), _ptr(uniforms),
-                             B, g, d, V,
-                             float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)),
-           "lmhead_verify")
+    fn, name = (lib.lmhead_verify, "lmhead_verify") if layout == W_DV else (lib.lmhead_verify_wvd,
+                                                                           "lmhead_verify_wvd")
+    _check(fn(_ptr(feat_t), _ptr(feat_d), _ptr(W), _ptr(draft_tokens), _ptr(uniforms), B, g, d, V,
+              float(temperature), _ptr(acc), _ptr(toks), _ptr(w), w.numel(), _stream(dev)), name)
     return out
 
 
@@ -353,13 +356,16 @@ def lmhead_logits_view(ws, B, g, V, d):
     return z[: B * (g + 1)].view(B, g + 1, V), z[B * (g + 1):].view(B, g, V)
 
 
-def probe_probs(target, draft, temperature, ws=None):
+def probe_probs(target, draft, temperature, ws=None, out=None):
     """p, q and the normalised residual (float64 [rows, V]) as the draw sees them."""
     rows, V = target.shape
     dev = target.device
-    p = torch.empty((rows, V), dtype=torch.float64, device=dev)
-    q = torch.empty_like(p) if draft is not None else None
-    r = torch.empty_like(p) if draft is not None else None
+    if out is None:
+        p = torch.empty((rows, V), dtype=torch.float64, device=dev)
+        q = torch.empty_like(p) if draft is not None else None
+        r = torch.empty_like(p) if draft is not None else None
+    else:
+        p, q, r = out
     w = _workspace(MODE_ROWSTATS, 2 * rows, 0, V, 0, dev, ws)
     _check(lib.spec_probe_probs(_ptr(target), _ptr(draft), dtype_code(target), rows, V, float(temperature),
                                 _ptr(p), _ptr(q), _ptr(r), _ptr(w), w.numel(), _stream(dev)), "spec_probe_probs")

@@ -550,14 +550,20 @@ spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint
   return hip_status(launch_lmhead(p, s));
 }
 
-spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
-                          spec_wlayout wl, const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d,
-                          int V, float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
-                          size_t ws_bytes, hipStream_t s) {
+}  // extern "C"
+
+namespace {
+
+// lmhead_verify for either weight layout: stage the feature rows, one GEMM
+// into the workspace's float32 logits, then the sampling path on them.
+spec_status lmhead_verify_layout(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
+                                 int w_vd, const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
+                                 int d, int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
+                                 void* ws, size_t ws_bytes, hipStream_t s) {
   if (B < 1 || B > SPEC_MAX_BATCH || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB)
     return SPEC_EINVAL;
   if (d < 64 || d % 64 != 0 || d > (1 << 20)) return SPEC_EINVAL;
-  if (V >= (1 << 25) || (wl != SPEC_W_DV && wl != SPEC_W_VD)) return SPEC_EINVAL;
+  if (V >= (1 << 25)) return SPEC_EINVAL;
   if (!target_feat || !draft_feat || !W || !draft_tokens || !uniforms || !accept_len || !out_tokens)
     return SPEC_EINVAL;
   if (!aligned(target_feat, 16) || !aligned(draft_feat, 16) || !aligned(W, 16) ||
@@ -586,7 +592,7 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   p.a_staged = 1;
   p.M = B * (2 * gamma + 1);
   p.W = W;
-  p.w_vd = wl == SPEC_W_VD;
+  p.w_vd = w_vd;
   p.K = d;
   p.N = V;
   p.C = Z;
@@ -594,6 +600,26 @@ spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_fea
   const float* Zd = Z + (size_t)B * (gamma + 1) * (size_t)V;
   return sample_on(Z, Zd, DT_F32, draft_tokens, uniforms, B, gamma, V, tc, accept_len, out_tokens, ws,
                    L, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status lmhead_verify(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
+                          const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d, int V,
+                          float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                          size_t ws_bytes, hipStream_t s) {
+  return lmhead_verify_layout(target_feat, draft_feat, W, 0, draft_tokens, uniforms, B, gamma, d, V,
+                              temperature, accept_len, out_tokens, ws, ws_bytes, s);
+}
+
+spec_status lmhead_verify_wvd(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W_vd,
+                              const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int d, int V,
+                              float temperature, int32_t* accept_len, int32_t* out_tokens, void* ws,
+                              size_t ws_bytes, hipStream_t s) {
+  return lmhead_verify_layout(target_feat, draft_feat, W_vd, 1, draft_tokens, uniforms, B, gamma, d, V,
+                              temperature, accept_len, out_tokens, ws, ws_bytes, s);
 }
 
 spec_status spec_probe_probs(const void* target_logits, const void* draft_logits, spec_dtype dt, int rows,

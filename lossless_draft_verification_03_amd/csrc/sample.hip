@@ -57,6 +57,7 @@ __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
   R.Md = di.Md;
   R.rho_hi = (float)di.rho;
   R.rho_lo = (float)(di.rho - (double)R.rho_hi);
+  R.rho = di.rho;
   return R;
 }
 
@@ -200,7 +201,10 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   __shared__ int sh_first[4];
   __shared__ long long sh_y;
   __shared__ double sh_base, sh_thr;
-  __shared__ int sh_k, sh_fallback;
+  // sh_zero: the residual of row j has no mass (draw from p_j instead);
+  // sh_locfb: rounding left no crossing in the located sub-segment.  Two
+  // flags, because waves 1..3 read sh_zero while wave 0 locates.
+  __shared__ int sh_k, sh_zero, sh_locfb;
   // wid is wave-uniform; readfirstlane lets the compiler keep what derives
   // from it (buffer descriptors) in scalar registers
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -222,12 +226,12 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
     double total = wave_sum(m0);
     for (int c0 = kWave; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
     if (lane == 0) {
-      sh_fallback = total > 0.0 ? 0 : 1;
+      sh_zero = total > 0.0 ? 0 : 1;
       sh_thr = (double)u * total;
     }
   }
   __syncthreads();
-  if (sh_fallback) {
+  if (sh_zero) {
     // A zero residual cannot follow a rejection in exact arithmetic; if
     // rounding produces one, draw from p_j (this workgroup recomputes the
     // row's sub-segment masses alone, in place; the barrier makes them
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
     if (lane == 0) {
       sh_k = k;
       sh_base = base;
-      sh_fallback = fb;
+      sh_locfb = fb;
       sh_y = -1;
     }
   }
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   for (int v = 0; v < wid; ++v) wbase += sh_wtot[v];
   const double excl = sh_base + wbase + (incl - T);
   const double thr = sh_thr;
-  const bool cross = !sh_fallback && T > 0.0 && excl + T > thr;
+  const bool cross = !sh_locfb && T > 0.0 && excl + T > thr;
   const unsigned long long mc = __ballot(cross);
   const unsigned long long mp = __ballot(T > 0.0);
   if (lane == 0) sh_first[wid] = mc ? wid * kWave + (int)__ffsll((long long)mc) - 1 : INT_MAX;

@@ -230,6 +230,27 @@ __device__ __forceinline__ float exp_rel(float z, float M, const TempConst& tc) 
   }
 }
 
+// The same exponential as exp_rel, returned in fp64: the head 2^ah from the
+// hardware exp2 and the tail factor (1 + al ln 2) applied in fp64, so neither
+// the tail nor a later difference of two such values is rounded to fp32.
+template <int DT>
+__device__ __forceinline__ double exp_rel_f64(float z, float M, const TempConst& tc) {
+  float ah, al;
+  if constexpr (DT == DT_BF16) {
+    const float d = fmaxf(z - M, tc.d_min);
+    ah = d * tc.c_hi;
+    al = fmaf(d, tc.c_hi, -ah);
+    al = fmaf(d, tc.c_lo, al);
+  } else {
+    double a = ((double)z - (double)M) * tc.c64;
+    a = a > -200.0 ? a : -200.0;
+    ah = (float)a;
+    al = (float)(a - (double)ah);
+  }
+  const double e = (double)__builtin_amdgcn_exp2f(ah);
+  return fma(e, (double)al * kLn2, e);
+}
+
 // The row a final draw samples from: the target row alone (weights
 // e_t = 2^((z_t - M_t) c), proportional to p), or a residual row with weights
 // max(0, e_t - rho e_d) proportional to max(0, p - (rho S_d / S_t) q); rho is
@@ -239,6 +260,7 @@ struct DrawRow {
   const char* d;      // draft row base (resid only)
   float Mt, Md;
   float rho_hi, rho_lo;
+  double rho;         // rho_hi + rho_lo, unsplit (draw_weight_f64)
   bool resid;
 };
 
@@ -258,6 +280,16 @@ __device__ __forceinline__ float draw_weight_r(const DrawRow& R, float zt, float
 template <int DT>
 __device__ __forceinline__ float draw_weight(const DrawRow& R, float zt, float zd, const TempConst& tc) {
   return R.resid ? draw_weight_r<DT, true>(R, zt, zd, tc) : draw_weight_r<DT, false>(R, zt, zd, tc);
+}
+// The same weight formed in fp64 from exp_rel_f64 values and the unsplit
+// rho: max(0, e_t - rho e_d) with one fp64 rounding.  Its only error left is
+// that of the two hardware exp2 heads.
+template <int DT>
+__device__ __forceinline__ double draw_weight_f64(const DrawRow& R, float zt, float zd, const TempConst& tc) {
+  const double et = exp_rel_f64<DT>(zt, R.Mt, tc);
+  if (!R.resid) return et;
+  const double ed = exp_rel_f64<DT>(zd, R.Md, tc);
+  return fmax(fma(-R.rho, ed, et), 0.0);
 }
 
 // Wave-parallel location of the segment holding thr: lanes scan the segment

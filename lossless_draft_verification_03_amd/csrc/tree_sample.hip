@@ -100,8 +100,10 @@ struct WalkLds {
 
 // Wave wid's share of one segment's draw weights: the wid-th of kTW
 // contiguous sub-segments of [e0, e1), lane-interleaved 16-byte vectors, fp64
-// accumulation; returns this lane's partial.
-template <int DT, bool ALIGNED>
+// accumulation; returns this lane's partial.  F64W: each weight formed in
+// fp64 (draw_weight_f64; the W passes of the residual chain), else the final
+// draw's fp32 weight (draw_weight, which the pick rescans).
+template <int DT, bool ALIGNED, bool F64W>
 __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1, const TempConst& tc, int wid,
                                    int lane) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
@@ -130,13 +132,17 @@ __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1,
       unpack<DT>(vt[k], zt);
       if (R.resid) unpack<DT>(vd[k], zd);
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+      for (int i = 0; i < EPV; ++i) {
+        if constexpr (F64W) acc += draw_weight_f64<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+        else acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+      }
     }
   } else {
     for (long long e = s0 + lane; e < s1; e += kWave) {
       const float zt = load_elem<DT>(R.t, e);
       const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
-      acc += (double)draw_weight<DT>(R, zt, zd, tc);
+      if constexpr (F64W) acc += draw_weight_f64<DT>(R, zt, zd, tc);
+      else acc += (double)draw_weight<DT>(R, zt, zd, tc);
     }
   }
   return acc;
@@ -146,8 +152,8 @@ __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1,
 // fixed combination order throughout); if sub is not null, also every
 // segment's kTW sub-segment masses into sub[segment * kTW + sub-segment]
 // (global memory, read back by this workgroup after a barrier).  Every
-// thread of the block calls it.
-template <int DT, bool ALIGNED>
+// thread of the block calls it.  F64W as in walk_sub_partial.
+template <int DT, bool ALIGNED, bool F64W>
 __device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, WalkLds& L, int tid,
                             double* sub) {
   constexpr int SEG = walk_seg<DT>();
@@ -158,7 +164,7 @@ __device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, 
     for (int s = s0; s < s1; ++s) {
       const long long e0 = (long long)s * SEG;
       const long long e1 = e0 + SEG < V ? e0 + SEG : V;
-      const double a = wave_sum(walk_sub_partial<DT, ALIGNED>(R, e0, e1, tc, wid, lane));
+      const double a = wave_sum(walk_sub_partial<DT, ALIGNED, F64W>(R, e0, e1, tc, wid, lane));
       if (lane == 0) {
         L.red[(s - s0) * kTW + wid] = a;
         if (sub != nullptr) sub[s * kTW + wid] = a;
@@ -287,6 +293,7 @@ __device__ __forceinline__ void set_rho(DrawRow& R, double c, double St, double 
   const double rho = R.resid ? c * (St / Sd) : 0.0;
   R.rho_hi = (float)rho;
   R.rho_lo = (float)(rho - (double)R.rho_hi);
+  R.rho = rho;
 }
 
 // Rows of the first n_pre nodes of every sequence, swept up front across the
@@ -447,7 +454,9 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
         break;
       }
       set_rho(R, cn, St, Sd);
-      const double Wn = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, nullptr) / St;
+      // W of the next residual: fp64 weights, so a test's value
+      // max(0, p(x)/q(x) - c)/W carries no fp32 rounding of the residual
+      const double Wn = mass_pass<DT, ALIGNED, true>(R, V, P.tc, L, tid, nullptr) / St;
       if (Wn > 0.0) {
         cc = cn;
         W = Wn;
@@ -465,14 +474,14 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
 
   // final draw from R (fallback: the law before the last residual, then p)
   double* const sub = P.ws_sub + (long long)b * tree_walk_subsegments(P.V, DT);
-  double total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
+  double total = mass_pass<DT, ALIGNED, false>(R, V, P.tc, L, tid, sub);
   if (!(total > 0.0) && R.resid) {
     set_rho(R, c_fb, L.S[0], L.S[1]);
-    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
+    total = mass_pass<DT, ALIGNED, false>(R, V, P.tc, L, tid, sub);
   }
   if (!(total > 0.0) && R.resid) {
     set_rho(R, 0.0, L.S[0], L.S[1]);
-    total = mass_pass<DT, ALIGNED>(R, V, P.tc, L, tid, sub);
+    total = mass_pass<DT, ALIGNED, false>(R, V, P.tc, L, tid, sub);
   }
   const long long y = walk_pick<DT, ALIGNED>(R, V, (double)L.u[0] * total, P.tc, L, tid, sub);
   for (int c = tid; c < N; c += kTB) {

@@ -10,17 +10,13 @@
   runs of a test, must stay below MAX_RATE of the verified positions.
 """
 import numpy as np
-import torch
 
 MARGIN = 1e-6
 MAX_RATE = 1e-4
-# Tree sampling: a test after a rejected sibling compares u with
-# (p(x)/q(x) - c) / W, where W is a sum of float32 residual weights over the
-# whole vocabulary (error up to a few float32 ulps of 1 + c per unit W).
-MARGIN_RESID = 1e-5
 
 
 def to_dev(arr, device="cuda"):
+    import torch
     a = np.ascontiguousarray(arr)
     if a.dtype == np.uint16:
         a = a.view(np.int16)
@@ -79,12 +75,11 @@ def _draw_distance(info, y):
     return 0.0 if lo <= t < hi else min(abs(t - lo), abs(t - hi))
 
 
-def classify_tree_sample(gpu_acc, gpu_path, gpu_tok, ora_acc, ora_path, ora_tok, infos, parents,
-                         margin=MARGIN, margin_resid=MARGIN_RESID):
+def classify_tree_sample(gpu_acc, gpu_path, gpu_tok, ora_acc, ora_path, ora_tok, infos, parents, margin=MARGIN):
     """Tree sampling: equal outputs, or a first differing decision at an
-    oracle margin: an accept test (first child of its node: |u - r| < margin;
-    a later sibling: < margin_resid) or the final draw (as in
-    classify_sample).  parents [B][N]."""
+    oracle margin below `margin`: an accept test (|u - r|, for the first
+    child of a node and for a child tried after rejected siblings alike) or
+    the final draw (as in classify_sample).  parents [B][N]."""
     res = dict(exact=0, explained=0, unexplained=[], sequences=len(ora_acc), details=[])
     for b in range(len(ora_acc)):
         ja, jo = int(gpu_acc[b]), int(ora_acc[b])
@@ -95,16 +90,11 @@ def classify_tree_sample(gpu_acc, gpu_path, gpu_tok, ora_acc, ora_path, ora_tok,
         if ja < 0 or jo < 0:
             res["unexplained"].append((b, f"validity differs: gpu {ja} oracle {jo}"))
             continue
-        par = np.asarray(parents[b])
         gpu_set = set(int(c) for c in gp[:ja])
-        first_child = {}
-        for c in range(1, len(par)):
-            first_child.setdefault(int(par[c]), c)
         why = None
         for (c, u, r) in infos[b]["tests"]:
             if (u < r) != (c in gpu_set):
-                tol = margin if first_child[int(par[c])] == c else margin_resid
-                if abs(u - r) < tol:
+                if abs(u - r) < margin:
                     why = ("explained", (b, "accept", c, abs(u - r)))
                 else:
                     why = ("unexplained", (b, f"test of node {c}: |u-r|={abs(u - r):.3e}"))

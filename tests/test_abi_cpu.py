@@ -85,9 +85,19 @@ def test_other_entry_points_reject_invalid_arguments():
     assert lib.lmhead_project_staged(FAKE, 4, 128, FAKE, 0, 10, FAKE, None, 1 << 30, None) == 4
     assert lib.lmhead_project_staged(FAKE, 704, 4096, FAKE, 1, 10, FAKE, FAKE, need - 1, None) == 4
     assert lib.lmhead_project_staged(FAKE, 4, 128, FAKE, 0, 10, FAKE, FAKE + 16, 1 << 30, None) == 4
-    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 2, 3, 96, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
-    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 2, 3, 128, 50, 0.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
-    assert lib.lmhead_verify(FAKE, FAKE, FAKE, 7, FAKE, FAKE, 2, 3, 128, 50, 1.0, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    # EAGLE verification, both weight layouts: the argument order of the
+    # boundary (features, W, draft_tokens, uniforms, B, gamma, d, V, T, ...)
+    for fn in (lib.lmhead_verify, lib.lmhead_verify_wvd):
+        def lv(**kw):
+            a = dict(ft=FAKE, fd=FAKE, W=FAKE, x=FAKE, u=FAKE, B=2, g=3, d=128, V=50, T=1.0, acc=FAKE, out=FAKE,
+                     ws=FAKE, wsb=1 << 40)
+            a.update(kw)
+            return fn(a["ft"], a["fd"], a["W"], a["x"], a["u"], a["B"], a["g"], a["d"], a["V"], a["T"], a["acc"],
+                      a["out"], a["ws"], a["wsb"], None)
+        assert lv(d=96) == 1 and lv(d=0) == 1 and lv(T=0.0) == 1 and lv(g=64) == 1 and lv(V=1 << 25) == 1
+        assert lv(W=None) == 1 and lv(x=None) == 1 and lv(u=None) == 1
+        assert lv(W=FAKE + 8) == 3 and lv(x=FAKE + 2) == 3 and lv(u=FAKE + 1) == 3 and lv(fd=FAKE + 4) == 3
+        assert lv(ws=None) == 4 and lv(wsb=1024) == 4
     # row stats: want out of range, missing sum output
     assert lib.spec_row_stats(FAKE, 1, 4, 10, 1.0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert lib.spec_row_stats(FAKE, 1, 4, 10, 1.0, 1, FAKE, None, None, FAKE, 1 << 30, None) == 1

@@ -10,10 +10,13 @@ import numpy as np
 import pytest
 import torch
 
-import lossless_draft_verification_03_amd as L
+import lossless_draft_verification_03_amd as _binding
 import oracle
 from gen import make_workload
 from parity import classify_sample, to_dev
+import sentinel
+
+L = sentinel.wrap(_binding)   # every output buffer sentinel-filled before each call
 
 pytestmark = pytest.mark.gpu
 

@@ -45,6 +45,7 @@ class _Calls:
             "tree": (torch.empty(4, **i32), torch.empty((4, 15), **i32), torch.empty((4, 15), **i32)),
             "tsample": (torch.empty(4, **i32), torch.empty((4, 15), **i32), torch.empty((4, 15), **i32)),
         }
+        self.clear()                             # no output starts from recycled memory
 
     def run(self):
         a, t = self.lin, self.tree

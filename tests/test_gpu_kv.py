@@ -6,12 +6,15 @@ import numpy as np
 import pytest
 import torch
 
-import lossless_draft_verification_03_amd as L
+import lossless_draft_verification_03_amd as _binding
 import oracle
 from gen import make_workload
 from gen.synth import tree_parents
 from oracle.kv import kv_compact as oracle_kv
 from parity import to_dev
+import sentinel
+
+L = sentinel.wrap(_binding)   # every output buffer sentinel-filled before each call
 
 pytestmark = pytest.mark.gpu
 

@@ -14,11 +14,12 @@ import torch
 import oracle
 from gen import make_workload
 from gen.synth import f32_to_bf16_bits, tree_parents
+import sentinel
 from parity import MAX_RATE, classify_sample, to_dev
 
 pytestmark = pytest.mark.gpu
 
-L = pytest.importorskip("lossless_draft_verification_03_amd")
+L = sentinel.wrap(pytest.importorskip("lossless_draft_verification_03_amd"))
 
 
 def _need_gpu():
@@ -105,11 +106,61 @@ def test_flip_rate_zipf32k():
     assert t["explained"] <= MAX_RATE * t["positions"]
 
 
+# The batch the forked oracle workers of the flip-rate test read: set before
+# the fork, so every worker inherits it without a copy.
+_FLIP = {}
+
+
+def _flip_worker(span):
+    b0, b1 = span
+    f = _FLIP
+    acc, out, infos = oracle.verify_sample(f["target"][b0:b1], f["draft"][b0:b1], "bf16", f["tokens"][b0:b1],
+                                           f["uniforms"][b0:b1], f["T"])
+    res = classify_sample(f["gacc"][b0:b1], f["gout"][b0:b1], acc, out, infos)
+    return (res["exact"], res["explained"], [(b0 + d[0],) + tuple(d[1:]) for d in res["details"]],
+            [(b0 + b, why) for b, why in res["unexplained"]])
+
+
+@pytest.mark.timeout(1200)
 def test_flip_rate_b64g7v128k():
-    """The same budget on the B=64, gamma=7, V=128256 bf16 workload over 24
-    seeded batches (10752 positions)."""
-    t = _flip_rate("b64g7v128k", range(100, 124))
-    assert t["explained"] <= MAX_RATE * t["positions"]
+    """The flip budget at the large workload's shape and distributions (bf16,
+    gamma = 7, V = 128256, target ~ N(0, 2), draft noise N(0, 0.8), T = 0.7)
+    over 28 batches of 512 sequences: 100352 verified positions, so the
+    0.01% budget allows 10 explained disagreements and a rate of that order
+    is resolved.  The batches come from the seeded device generator
+    (gen.device); the oracle runs in forked worker processes, each on a slice
+    of the batch."""
+    import multiprocessing
+    import os
+    from gen.device import make_linear_device
+    nb, B, g, V = 28, 512, 7, 128256
+    nw = max(1, min(8, len(os.sched_getaffinity(0)) - 1))
+    spans = [(b0, min(B, b0 + (B + nw - 1) // nw)) for b0 in range(0, B, (B + nw - 1) // nw)]
+    ctx = multiprocessing.get_context("fork")
+    tally = dict(explained=0, positions=0, exact=0)
+    details = []
+    for s in range(nb):
+        w = make_linear_device(B, g, V, seed=1000 + s)
+        acc, out = L.verify_sample(w["target"], w["draft"], w["draft_tokens"], w["uniforms"], w["temperature"])
+        torch.cuda.synchronize()
+        _FLIP.update(target=w["target"].view(torch.int16).cpu().numpy().view(np.uint16),
+                     draft=w["draft"].view(torch.int16).cpu().numpy().view(np.uint16),
+                     tokens=w["draft_tokens"].cpu().numpy(), uniforms=w["uniforms"].cpu().numpy(),
+                     T=float(np.float32(w["temperature"])), gacc=acc.cpu().numpy(), gout=out.cpu().numpy())
+        del w, acc, out
+        with ctx.Pool(nw) as pool:
+            parts = pool.map(_flip_worker, spans)
+        _FLIP.clear()
+        unexplained = [u for p in parts for u in p[3]]
+        assert not unexplained, (s, unexplained[:5])
+        tally["exact"] += sum(p[0] for p in parts)
+        tally["explained"] += sum(p[1] for p in parts)
+        tally["positions"] += B * g
+        details += [(s,) + d for p in parts for d in p[2]]
+        print(f"[flip b64g7v128k] batch {s + 1}/{nb}: {tally}", flush=True)
+    print("explained disagreements:", details)
+    assert tally["positions"] >= 100000
+    assert tally["explained"] <= MAX_RATE * tally["positions"]
 
 
 def test_b64g7v128k_greedy(c3):
@@ -278,13 +329,22 @@ def test_zero_residual_falls_back_to_p(dt, V, B, g):
     assert res["explained"] == 0
 
 
-def test_invalid_draft_tokens_flag_sequence():
-    w = make_workload("tiny", B=4, gamma=3, V=50, seed=1)
-    w["draft_tokens"][1, 2] = 50
+@pytest.mark.parametrize("dt,V", [("f32", 50), ("bf16", 9000)])
+def test_invalid_draft_tokens_flag_sequence(dt, V):
+    """A drafted token outside [0, V) flags its sequence (accept_len -1, all
+    outputs -1) wherever it sits, as the oracle's rule says; the other
+    sequences of the batch are verified as usual."""
+    w = make_workload("tiny", B=6, gamma=3, V=V, dtype=dt, seed=1)
+    w["draft_tokens"][1, 2] = V
     w["draft_tokens"][3, 0] = -1
+    w["draft_tokens"][4, 1] = -7
+    w["draft_tokens"][5, 2] = V + 12345
     acc, out = _run_sample(w)
-    assert acc[1] == -1 and np.all(out[1] == -1) and acc[3] == -1 and np.all(out[3] == -1)
-    assert acc[0] >= 0 and acc[2] >= 0
+    oacc, oout, infos = _oracle_sample(w)
+    assert list(oacc[[1, 3, 4, 5]]) == [-1] * 4 and oacc[0] >= 0 and oacc[2] >= 0
+    res = classify_sample(acc, out, oacc, oout, infos)
+    assert not res["unexplained"] and res["explained"] == 0, res
+    assert np.array_equal(acc, oacc) and np.array_equal(out, oout)
 
 
 def test_tree_edges():
@@ -443,48 +503,85 @@ def c5():
 
 
 def test_eagle_lmhead_logits_and_verify(c5):
+    """The EAGLE workload (B = 64, gamma = 5, d = 4096, V = 128256) through
+    lmhead_verify, all 64 sequences:
+
+    * the logits it leaves in its workspace equal the standalone projection
+      of the target and of the draft feature rows, bit for bit, and the [V, d]
+      entry point gives the same logits and outputs;
+    * every logit of every row lies within the float32 accumulation bound
+      |dz| <= d 2^-24 sum_k |h_k||w_k| of the oracle's float64 logits;
+    * the oracle run on the GPU's own float32 logits reproduces the outputs
+      under the standard rules: disagreements only at an oracle margin below
+      1e-6, and no more than 0.01% of the 320 verified positions;
+    * the oracle run on its float64 logits (end to end) is reported with the
+      margins of any disagreement, which the logit error must explain."""
     w = c5
     B, g, d, V = w["B"], w["gamma"], w["d"], w["V"]
+    T = float(w["temperature"])
     ft, fd, W = to_dev(w["feat_t"]), to_dev(w["feat_d"]), to_dev(w["W"])
     x, u = to_dev(w["draft_tokens"]), to_dev(w["uniforms"])
     ws = L.new_workspace(L.MODE_LMHEAD, B, g, V, d)
-    acc, out = L.lmhead_verify(ft, fd, W, x, u, float(w["temperature"]), ws=ws)
+    ws.fill_(0xA5)
+    acc, out = L.lmhead_verify(ft, fd, W, x, u, T, ws=ws)
     zt_gpu, zd_gpu = L.lmhead_logits_view(ws, B, g, V, d)
-    # the projection inside lmhead_verify is the standalone projection
+    # the projections inside lmhead_verify are the standalone projections
     proj = L.lmhead_project(ft, W)
     assert torch.equal(proj.view(B, g + 1, V), zt_gpu)
+    assert torch.equal(L.lmhead_project(fd, W).view(B, g, V), zd_gpu)
     # the [V, d] weight layout gives bit-identical logits and verdicts: the
     # MFMA operands hold the same values in the same k order
     Wvd = W.t().contiguous()
     assert torch.equal(L.lmhead_project(ft, Wvd, layout=L.W_VD), proj)
     assert torch.equal(L.lmhead_project(ft, W, ws=True), proj)
     assert torch.equal(L.lmhead_project(ft, Wvd, layout=L.W_VD, ws=True), proj)
-    acc2, out2 = L.lmhead_verify(ft, fd, Wvd, x, u, float(w["temperature"]), ws=ws.clone(), layout=L.W_VD)
+    acc2, out2 = L.lmhead_verify(ft, fd, Wvd, x, u, T, ws=ws.clone(), layout=L.W_VD)
     assert torch.equal(acc2, acc) and torch.equal(out2, out)
-    del Wvd
-    seqs = list(range(0, B, 4))
-    rows_t = np.array([b * (g + 1) + i for b in seqs for i in range(g + 1)])
-    rows_d = np.array([b * g + i for b in seqs for i in range(g)])
-    zt_o = oracle.lmhead_logits(w["feat_t"][rows_t], w["W"])
-    zd_o = oracle.lmhead_logits(w["feat_d"][rows_d], w["W"])
-    zt_g = zt_gpu.reshape(-1, V)[torch.from_numpy(rows_t).cuda()].cpu().numpy().astype(np.float64)
-    zd_g = zd_gpu.reshape(-1, V)[torch.from_numpy(rows_d).cuda()].cpu().numpy().astype(np.float64)
-    # fp32 accumulation over d terms: |dz| <= d * 2^-24 * sum|h||w| (Higham);
-    # the observed error must also sit far below it
-    Ht = oracle.decode(w["feat_t"][rows_t], "bf16")
-    Wa = np.abs(oracle.decode(w["W"][:, :4096], "bf16"))
-    bound = d * 2.0 ** -24 * (np.abs(Ht) @ Wa)
-    assert np.all(np.abs(zt_g[:, :4096] - zt_o[:, :4096]) <= bound)
-    err = max(np.abs(zt_g - zt_o).max(), np.abs(zd_g - zd_o).max())
-    print("max |dz|", err)
-    assert err < 1e-4
-    # verification on the GPU's logits reproduces the oracle run on the
-    # oracle's float64 logits up to the propagated logit error
-    zt_ob = zt_o.reshape(len(seqs), g + 1, V)
-    zd_ob = zd_o.reshape(len(seqs), g, V)
-    oacc, oout, infos = oracle.verify_sample(zt_ob, zd_ob, "f64", w["draft_tokens"][seqs], w["uniforms"][seqs],
-                                             float(w["temperature"]))
-    margin = 1e-6 + 4 * err / float(w["temperature"])
-    res = classify_sample(acc.cpu().numpy()[seqs], out.cpu().numpy()[seqs], oacc, oout, infos, margin=margin)
-    print(res["exact"], res["explained"], res["details"])
+    del Wvd, proj
+    acc, out = acc.cpu().numpy(), out.cpu().numpy()
+    zt_g = zt_gpu.cpu().numpy()
+    zd_g = zd_gpu.cpu().numpy()
+    del ws, zt_gpu, zd_gpu
+    torch.cuda.empty_cache()
+    # oracle logits for every row (float64, exact products) and the float32
+    # accumulation bound, column block by column block
+    H = np.concatenate([w["feat_t"], w["feat_d"]], 0)
+    Ha = np.abs(oracle.decode(H, "bf16")).astype(np.float32)
+    rows_t = B * (g + 1)
+    z_o = np.empty((H.shape[0], V), np.float64)
+    worst = dict(err=0.0, ratio=0.0)
+    zg = np.concatenate([zt_g.reshape(rows_t, V), zd_g.reshape(B * g, V)], 0).astype(np.float64)
+
+    def block(c0):
+        c1 = min(V, c0 + 8192)
+        z_o[:, c0:c1] = oracle.lmhead_logits(H, w["W"][:, c0:c1])
+        # |h||w| summed in float32 (non-negative terms: relative error below
+        # d 2^-24), widened by 1e-3 to stay an upper bound
+        bound = d * 2.0 ** -24 * (Ha @ np.abs(oracle.decode(w["W"][:, c0:c1], "bf16")).astype(np.float32))
+        bound = bound.astype(np.float64) * (1 + 1e-3)
+        err = np.abs(zg[:, c0:c1] - z_o[:, c0:c1])
+        assert np.all(err <= bound), (c0, float(err.max()))
+        return float(err.max()), float((err / bound).max())
+
+    for c0 in range(0, V, 8192):               # the BLAS calls use every core
+        e, r = block(c0)
+        worst["err"] = max(worst["err"], e)
+        worst["ratio"] = max(worst["ratio"], r)
+    print("max |dz|", worst["err"], "max |dz| / bound", worst["ratio"])
+    del zg
+    # verification of the GPU's own logits: the standard rules
+    oacc, oout, infos = oracle.verify_sample(zt_g, zd_g, "f32", w["draft_tokens"], w["uniforms"], T)
+    res = classify_sample(acc, out, oacc, oout, infos)
+    print("on the GPU logits: exact", res["exact"], "explained", res["explained"], res["details"])
     assert not res["unexplained"], res["unexplained"]
+    assert res["explained"] <= MAX_RATE * B * g
+    # end to end: the oracle on its float64 logits; reported, and every
+    # disagreement must sit within the margin the logit error can move
+    zt_o = z_o[:rows_t].reshape(B, g + 1, V)
+    zd_o = z_o[rows_t:].reshape(B, g, V)
+    eacc, eout, einfos = oracle.verify_sample(zt_o, zd_o, "f64", w["draft_tokens"], w["uniforms"], T)
+    prop = 1e-6 + 4 * worst["err"] / T
+    e2e = classify_sample(acc, out, eacc, eout, einfos, margin=prop)
+    print(f"end to end (float64 logits): exact {e2e['exact']} of {B}, disagreements "
+          f"{e2e['explained'] + len(e2e['unexplained'])} with margins {e2e['details']}")
+    assert not e2e["unexplained"], e2e["unexplained"]

@@ -10,11 +10,14 @@ import numpy as np
 import pytest
 import torch
 
-import lossless_draft_verification_03_amd as L
+import lossless_draft_verification_03_amd as _binding
 import oracle
 from gen.synth import f32_to_bf16_bits
 from oracle.tree_build import build_tree, expand_step, new_table
 from parity import to_dev
+import sentinel
+
+L = sentinel.wrap(_binding)   # every output buffer sentinel-filled before each call
 
 pytestmark = pytest.mark.gpu
 
