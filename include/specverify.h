@@ -182,6 +182,33 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
                                hipStream_t s);
 
 /*
+ * spec_verify_sample_noalloc -- spec_verify_sample for callers that cannot
+ * allocate device memory or hand over a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, outputs and results as spec_verify_sample (bit-identical: the
+ * same kernels run on the same layout), without ws / ws_bytes.  The
+ * workspace is a static device array of SPEC_NOALLOC_SCRATCH_BYTES bytes in
+ * the library, one per GPU, held until the process ends; its address is
+ * looked up on the first call on each device.  The call allocates nothing.
+ * Sizes whose workspace (spec_workspace_bytes(SPEC_MODE_SAMPLE, B, gamma, V,
+ * 0)) exceeds SPEC_NOALLOC_SCRATCH_BYTES are rejected with SPEC_EWORKSPACE
+ * before anything is launched (B = 64, gamma = 7, V = 128256 needs about
+ * 0.42 MB; the limit holds about 2500 such sequences).  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind; the array needs no
+ * clearing (each call writes every byte it reads), but calls that overlap in
+ * time on the same GPU (several streams, several host threads) race on it
+ * and give undefined results: serialise them, or use spec_verify_sample with
+ * distinct workspaces.  A failed device lookup reports SPEC_EHIP.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+spec_status spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                       spec_dtype dt, const int32_t* draft_tokens,
+                                       const float* uniforms, int B, int gamma, int V,
+                                       float temperature, int32_t* accept_len,
+                                       int32_t* out_tokens, hipStream_t s);
+
+/*
  * spec_verify_sample_early_exit -- spec_verify_sample with the rows swept in
  * position order: target and draft row i of a sequence are read only if its
  * positions before the block holding i were all accepted.

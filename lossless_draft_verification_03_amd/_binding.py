@@ -23,6 +23,7 @@ lib = ctypes.CDLL(LIB_PATH)
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_EHIP = range(6)
 SPEC_F32, SPEC_BF16 = 0, 1
 MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS, MODE_TREE_EXPAND, MODE_TREE_SAMPLE = range(7)
+SPEC_NOALLOC_SCRATCH_BYTES = 16 << 20  # the static workspace of spec_verify_sample_noalloc
 W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (feature innermost)
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
@@ -36,6 +37,7 @@ _SIGS = {
     "spec_row_segments": (_i, [_i, _i]),
     "spec_row_partials": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _vp, _vp, _vp]),
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),

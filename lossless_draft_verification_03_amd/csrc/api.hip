@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sv_kernels.hpp"
 
 using namespace sv;
@@ -250,6 +252,32 @@ spec_status check_sample_args(const void* target_logits, const void* draft_logit
   return check_ws(ws, ws_bytes, *L);
 }
 
+// ------------------------------------------------- allocation-free calls
+// The workspace of spec_verify_sample_noalloc: one static device array per
+// GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, so kernels get the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)SPEC_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or null on a HIP
+// error (no device, symbol not found).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -358,6 +386,24 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
   if (st != SPEC_OK) return st;
   return sample_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc,
                    accept_len, out_tokens, ws, L, s);
+}
+
+spec_status spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits, spec_dtype dt,
+                                       const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                                       float temperature, int32_t* accept_len, int32_t* out_tokens,
+                                       hipStream_t s) {
+  // the same checks as spec_verify_sample, with the layout checked against
+  // the scratch array's size instead of a caller's workspace
+  TempConst tc;
+  Layout L;
+  const spec_status st = check_sample_args(target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V,
+                                           temperature, accept_len, out_tokens, reinterpret_cast<void*>(kAlign),
+                                           kScratchBytes, &tc, &L);
+  if (st != SPEC_OK) return st;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return SPEC_EHIP;
+  return sample_on(target_logits, draft_logits, (int)dt, draft_tokens, uniforms, B, gamma, V, tc, accept_len,
+                   out_tokens, ws, L, s);
 }
 
 spec_status spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits, spec_dtype dt,

@@ -210,3 +210,25 @@ def test_tree_sample_rejects_invalid_arguments():
     assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, 0) <= sz
     assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 63, 128256, 64) == 0
     assert L.workspace_bytes(L.MODE_TREE_SAMPLE, 32, 4097, 1000) == 0
+
+
+def test_noalloc_sample_checks_before_any_device_call():
+    """spec_verify_sample_noalloc validates like spec_verify_sample and turns
+    a workspace past its static scratch array into SPEC_EWORKSPACE, all
+    before it looks up the device array (no GPU needed); the binding's
+    copy of the limit is the header's."""
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SPEC_NOALLOC_SCRATCH_BYTES
+    fn = L.lib.spec_verify_sample_noalloc
+
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, dt=L.SPEC_BF16, x=FAKE, u=FAKE, B=2, g=3, V=100, T=1.0, acc=FAKE, out=FAKE)
+        a.update(kw)
+        return fn(a["t"], a["d"], a["dt"], a["x"], a["u"], a["B"], a["g"], a["V"], a["T"], a["acc"], a["out"], None)
+    assert call(dt=9) == 2 and call(B=0) == 1 and call(g=64) == 1 and call(T=0.0) == 1 and call(u=None) == 1
+    assert call(t=FAKE + 4) == 3
+    big = 4096
+    assert L.workspace_bytes(L.MODE_SAMPLE, big, 7, 128256) > L.SPEC_NOALLOC_SCRATCH_BYTES
+    assert call(B=big, g=7, V=128256) == 4
+    assert L.workspace_bytes(L.MODE_SAMPLE, 64, 7, 128256) <= L.SPEC_NOALLOC_SCRATCH_BYTES
