@@ -6,6 +6,14 @@ the residual / bonus draw.  Inputs sit in HBM before timing starts; the step
 rotates over R >= 4 input replicas (>= 1 GB) so the 256 MB Infinity Cache
 cannot serve them.  Prints ONE JSON line.
 
+Besides the headline: the per-step time distribution (median, p10, p90 from
+events around every step), the row sweep alone (the roofline line) and a
+plain stream read of the same bytes (the HBM rate reachable on this device),
+the outputs' parity counts against the CPU oracle, the same workload under
+the Zipf recipe (reading B), and the oracle itself on the host's cores as the
+CPU baseline (the sampling workload, and the EAGLE-style LM head plus
+verification with BLAS on every core).
+
 Secondary legs (same JSON line, "modes"): greedy verification of the same
 tensors; early-exit sampling; greedy and stochastic tree verification (B=32,
 63-node binary tree); KV-cache compaction to the accepted paths; one EAGLE-2
@@ -35,7 +43,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip the greedy / tree / LM-head legs")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of the oracle baseline")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle parity counts")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of each oracle baseline leg")
     return ap.parse_args()
 
 
@@ -78,6 +87,94 @@ def time_events(fn, n, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n          # ms per call
+
+
+def step_distribution(fn, n, stream):
+    """Per-call times (ms) from an event pair around every call, in a pass
+    of its own (the headline's timed region has no events inside it)."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    ev[-1][1].synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5), "calls": n}
+
+
+# ------------------------------------------------------ oracle worker pool
+# The oracle runs in forked worker processes: each inherits the batch below
+# (set before the fork, never copied) and takes a slice of its sequences.
+_BATCH = {}
+
+
+def _cpu_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _spans(B, n):
+    step = (B + n - 1) // n
+    return [(b0, min(B, b0 + step)) for b0 in range(0, B, step)]
+
+
+def _oracle_slice(span):
+    import oracle
+    b0, b1 = span
+    f = _BATCH
+    return oracle.verify_sample(f["target"][b0:b1], f["draft"][b0:b1], f["dtype"], f["tokens"][b0:b1],
+                                f["uniforms"][b0:b1], f["T"])
+
+
+def _classify_slice(span):
+    from parity import classify_sample
+    acc, out, infos = _oracle_slice(span)
+    b0, b1 = span
+    res = classify_sample(_BATCH["gacc"][b0:b1], _BATCH["gout"][b0:b1], acc, out, infos)
+    return res["exact"], res["explained"], len(res["unexplained"]), [d[3] for d in res["details"]]
+
+
+def _time_slice(span):
+    _oracle_slice(span)
+    return span[1] - span[0]
+
+
+def _with_batch(batch, fn, spans, repeat_until=None):
+    """Run fn over the spans in a fork pool with `batch` visible to the
+    workers; with repeat_until (seconds), repeat whole passes until at least
+    that much wall time has gone.  Returns (results of the last pass,
+    passes, seconds)."""
+    import multiprocessing
+    _BATCH.clear()
+    _BATCH.update(batch)
+    try:
+        with multiprocessing.get_context("fork").Pool(len(spans)) as pool:
+            t0 = time.perf_counter()
+            passes = 0
+            while True:
+                res = pool.map(fn, spans)
+                passes += 1
+                el = time.perf_counter() - t0
+                if repeat_until is None or el >= repeat_until:
+                    return res, passes, el
+    finally:
+        _BATCH.clear()
+
+
+def parity_counts(w, gacc, gout):
+    """Sequences whose GPU outputs equal the oracle's, disagreements that an
+    oracle margin below 1e-6 explains (with those margins), and unexplained
+    ones, over the whole batch."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    B = len(gacc)
+    batch = dict(target=w["target"], draft=w["draft"], dtype=w["dtype"], tokens=w["draft_tokens"],
+                 uniforms=w["uniforms"], T=float(w["temperature"]), gacc=gacc, gout=gout)
+    res, _, _ = _with_batch(batch, _classify_slice, _spans(B, _cpu_workers()))
+    return {"sequences": B, "exact": sum(r[0] for r in res), "explained": sum(r[1] for r in res),
+            "unexplained": sum(r[2] for r in res), "explained_margins": [m for r in res for m in r[3]],
+            "rule": "outputs equal, or the first differing decision at an oracle margin below 1e-6"}
 
 
 def main():
@@ -170,6 +267,65 @@ def main():
                      "avg_launch_us": round(k1_ms * 1e3, 2)},
         "wall_s_timed_region": round(wall, 4),
     }
+    result["step_distribution"] = step_distribution(step, args.steps, stream)
+
+    # the HBM read rate reachable here: a plain read of the same 246 MB
+    # replicas with the sweep's load pattern and no arithmetic
+    sink = torch.empty(max(1, L.lib.spec_stream_read_sink_words(k1_bytes)), dtype=torch.int32, device=dev)
+
+    def sread(i):
+        L.stream_read(reps[i % R][0], sink=sink)
+
+    for i in range(args.warmup):
+        sread(i)
+    sr_ms = time_events(sread, args.steps, stream)
+    sr_gbs = k1_bytes / (sr_ms * 1e-3) / 1e9
+    result["stream_read"] = {"GBs": round(sr_gbs, 1), "frac_of_peak": round(sr_gbs / HBM_PEAK_GBS, 4),
+                             "bytes": k1_bytes, "avg_launch_us": round(sr_ms * 1e3, 2),
+                             "sweep_frac_of_stream_read": round(k1_gbs / sr_gbs, 4),
+                             "step_frac_of_stream_read": round(step_gbs / sr_gbs, 4)}
+
+    # parity of this run's outputs with the oracle (one fresh call, outputs
+    # filled with -7 first so nothing stale can pass), and of greedy mode
+    if not args.no_parity:
+        pout = (torch.full((B,), -7, dtype=torch.int32, device=dev),
+                torch.full((B, g + 1), -7, dtype=torch.int32, device=dev))
+        L.verify_sample(reps[0][1], reps[0][2], x, u, T, ws=ws, out=pout)
+        result["parity"] = parity_counts(w, pout[0].cpu().numpy(), pout[1].cpu().numpy())
+        import oracle
+        gout_ = (torch.full((B,), -7, dtype=torch.int32, device=dev),
+                 torch.full((B, g + 1), -7, dtype=torch.int32, device=dev))
+        L.verify_greedy(reps[0][1], x, out=gout_)
+        oacc, oout = oracle.verify_greedy(w["target"], "bf16", w["draft_tokens"])
+        result["parity"]["greedy_bit_exact_sequences"] = int(np.sum(
+            (gout_[0].cpu().numpy() == oacc) & np.all(gout_[1].cpu().numpy() == oout, axis=1)))
+
+    # the same shapes under the Zipf recipe (target N(0, 3) - 1.1 ln pi(v)
+    # over one seeded permutation, draft noise N(0, 0.8))
+    wb = make_workload("b64g7v128k", logits="zipf", target_std=3.0, zipf_slope=1.1, cache=True)
+    base_b = torch.cat([d(wb["target"]).view(rows_t, V), d(wb["draft"]).view(rows_d, V)], 0)
+    reps_b = []
+    for _ in range(4):
+        buf = base_b.clone()
+        reps_b.append((buf[:rows_t].view(B, g + 1, V), buf[rows_t:].view(B, g, V)))
+    del base_b
+    xb, ub = d(wb["draft_tokens"]), d(wb["uniforms"])
+    bout = (torch.full((B,), -7, dtype=torch.int32, device=dev), torch.full((B, g + 1), -7, dtype=torch.int32,
+                                                                           device=dev))
+
+    def bstep_(i):
+        L.verify_sample(reps_b[i % 4][0], reps_b[i % 4][1], xb, ub, T, ws=ws, out=bout)
+
+    for i in range(args.warmup):
+        bstep_(i)
+    bms = time_events(bstep_, args.steps, stream)
+    result["reading_b_zipf"] = {"ms": round(bms, 5), "positions_per_s": round(B * g / (bms * 1e-3), 1),
+                                "hbm_frac_step": round(k1_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "mean_accept_len": round(bout[0].float().mean().item(), 3)}
+    if not args.no_parity:
+        result["reading_b_zipf"]["parity"] = parity_counts(wb, bout[0].cpu().numpy(), bout[1].cpu().numpy())
+    del reps_b
+    torch.cuda.empty_cache()
 
     # ------------------------------------------------------- other modes
     if not args.no_modes:
@@ -441,19 +597,45 @@ def main():
 
     # --------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
-        import oracle
-        # whole-batch passes of the oracle until about args.cpu_seconds of work
-        passes, t0 = 0, time.perf_counter()
-        while True:
-            oracle.verify_sample(w["target"], w["draft"], "bf16", w["draft_tokens"], w["uniforms"], T)
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+        # the oracle as it stands, float64 NumPy, on the headline batch: the
+        # 64 sequences split over one forked worker process per core, whole
+        # passes repeated for about args.cpu_seconds
+        nw = _cpu_workers()
+        batch = dict(target=w["target"], draft=w["draft"], dtype="bf16", tokens=w["draft_tokens"],
+                     uniforms=w["uniforms"], T=T)
+        _, passes, el = _with_batch(batch, _time_slice, _spans(B, nw), repeat_until=args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(passes * B * g / el, 2), "unit": "verified positions/s",
-                                  "cores": 1, "kind": "oracle",
-                                  "sample": f"{passes} passes over the same {B}-sequence batch, float64 NumPy "
-                                            f"on one thread, {el:.1f} s"}
+                                  "cores": nw, "kind": "oracle",
+                                  "sample": f"{passes} passes over the same {B}-sequence batch (B=64 gamma=7 "
+                                            f"V=128256 bf16), sequences split over {nw} forked worker "
+                                            f"processes (float64 NumPy, one thread each), {el:.1f} s",
+                                  "gpu_over_cpu": round(value / (passes * B * g / el), 1)}
+        if not args.no_modes:
+            # the EAGLE-style path: float64 LM head (BLAS on every core) and
+            # verification of the resulting logits, 16 sequences per pass
+            import oracle
+            from threadpoolctl import threadpool_limits
+            ew = make_workload("eagle_lmhead", cache=True)
+            eB, eg = ew["B"], ew["gamma"]
+            nseq = 16
+            rt = np.concatenate([np.arange(b * (eg + 1), (b + 1) * (eg + 1)) for b in range(nseq)])
+            rd = np.concatenate([np.arange(b * eg, (b + 1) * eg) for b in range(nseq)])
+            with threadpool_limits(limits=nw):
+                t0, passes = time.perf_counter(), 0
+                while True:
+                    oracle.lmhead_verify(ew["feat_t"][rt], ew["feat_d"][rd], ew["W"], ew["draft_tokens"][:nseq],
+                                         ew["uniforms"][:nseq], float(ew["temperature"]))
+                    passes += 1
+                    el = time.perf_counter() - t0
+                    if el >= args.cpu_seconds:
+                        break
+            cv = passes * nseq * eg / el
+            e_gpu = result.get("modes", {}).get("eagle_lmhead_b64g5d4096_w_dv", {}).get("positions_per_s")
+            result["cpu_baseline"]["eagle_lmhead_b64g5d4096"] = {
+                "value": round(cv, 2), "unit": "verified positions/s", "cores": nw, "kind": "oracle",
+                "sample": f"{passes} passes over {nseq} of the 64 sequences ({nseq * (2 * eg + 1)} feature rows, "
+                          f"float64 GEMM with BLAS on {nw} threads, then verification), {el:.1f} s",
+                "gpu_over_cpu": round(e_gpu / cv, 1) if e_gpu else None}
     print(json.dumps(result), flush=True)
 
 

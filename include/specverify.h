@@ -114,6 +114,20 @@ spec_status spec_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
 const char* spec_status_str(spec_status st);
 
 /*
+ * spec_stream_read -- bandwidth probe (not a verification step): reads
+ * [src, src + bytes) once with the row sweep's load pattern (32 KB per
+ * workgroup, eight non-temporal 16-byte loads per lane in flight) and no
+ * arithmetic, so its rate is the HBM read rate the verification kernels can
+ * reach on this device.  sink [>= spec_stream_read_sink_words(bytes)] uint32
+ * receives one XOR word per workgroup (meaningless; it keeps the loads live).
+ * bytes a positive multiple of 16 (<= 2^40); src 16-byte aligned, sink
+ * 4-byte aligned.
+ */
+long long spec_stream_read_sink_words(long long bytes);
+spec_status spec_stream_read(const void* src, long long bytes, uint32_t* sink,
+                             long long sink_words, hipStream_t s);
+
+/*
  * spec_row_stats -- one pass over each logit row.
  * Pages: "EAGLE-3 speculative decoding review", "EAGLE: Predict Features, Not
  * Tokens" (logits z -> softmax -> next-token distribution) and "Does Using a

@@ -33,6 +33,8 @@ _SIGS = {
     "spec_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "spec_workspace_init": (_i, [_vp, _sz, _vp]),
     "spec_status_str": (ctypes.c_char_p, [_i]),
+    "spec_stream_read_sink_words": (_ll, [_ll]),
+    "spec_stream_read": (_i, [_vp, _ll, _vp, _ll, _vp]),
     "spec_row_stats": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_row_segments": (_i, [_i, _i]),
     "spec_row_partials": (_i, [_vp, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
@@ -345,6 +347,16 @@ def tree_build(table, n_nodes, M, out=None):
                                _ptr(opar), _ptr(otok), _ptr(odep), _ptr(oidx), _ptr(omask), _stream(dev)),
            "spec_tree_build")
     return out
+
+
+def stream_read(buf, sink=None):
+    """Bandwidth probe: read the whole of `buf` (a contiguous device tensor
+    whose byte size is a multiple of 16) once; returns the sink tensor."""
+    n = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(max(1, lib.spec_stream_read_sink_words(n)), dtype=torch.int32, device=buf.device)
+    _check(lib.spec_stream_read(_ptr(buf), n, _ptr(sink), sink.numel(), _stream(buf.device)), "spec_stream_read")
+    return sink
 
 
 def lmhead_logits_view(ws, B, g, V, d):

@@ -299,6 +299,19 @@ spec_status spec_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
   return hip_status(launch_fill_zero(ws, ws_bytes, s));
 }
 
+long long spec_stream_read_sink_words(long long bytes) {
+  if (bytes < 16 || bytes % 16 != 0) return 0;
+  return stream_read_workgroups(bytes);
+}
+
+spec_status spec_stream_read(const void* src, long long bytes, uint32_t* sink, long long sink_words,
+                             hipStream_t s) {
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || bytes > (1LL << 40)) return SPEC_EINVAL;
+  if (sink_words < stream_read_workgroups(bytes)) return SPEC_EINVAL;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return SPEC_EALIGN;
+  return hip_status(launch_stream_read(src, bytes, sink, s));
+}
+
 const char* spec_status_str(spec_status st) {
   switch (st) {
     case SPEC_OK: return "SPEC_OK";

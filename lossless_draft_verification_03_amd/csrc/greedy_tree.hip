@@ -188,7 +188,51 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
   if (i < ntail) tail[i] = 0;
 }
 
+// Stream read: workgroup c reads 16-byte vectors [c V, (c + 1) V) of the
+// buffer, V = kBlock * kStreamVPT, each lane issuing its kStreamVPT
+// non-temporal loads before it uses any (the row sweep's access pattern
+// without its arithmetic), and XORs them into one word per workgroup so the
+// loads stay live.  A bandwidth probe, not part of any verification call.
+constexpr int kStreamVPT = 8;
+
+__global__ __launch_bounds__(kBlock) void k_stream_read(const char* src, long long nvec, uint32_t* sink) {
+  __shared__ uint32_t sh[kBlock / kWave];
+  const int tid = threadIdx.x;
+  const long long v0 = (long long)blockIdx.x * kBlock * kStreamVPT;
+  const long long nv = nvec - v0 < (long long)kBlock * kStreamVPT ? nvec - v0 : (long long)kBlock * kStreamVPT;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src + v0 * 16, (uint32_t)nv * 16u);
+  v4i x[kStreamVPT];
+#pragma unroll
+  for (int k = 0; k < kStreamVPT; ++k) x[k] = load16(r, (uint32_t)(k * kBlock + tid) * 16u);   // past nv: 0
+  uint32_t acc = 0;
+#pragma unroll
+  for (int k = 0; k < kStreamVPT; ++k) acc ^= (uint32_t)(x[k][0] ^ x[k][1] ^ x[k][2] ^ x[k][3]);
+  acc ^= (uint32_t)dpp_i<kDppXor1>((int)acc);
+  acc ^= (uint32_t)dpp_i<kDppXor2>((int)acc);
+  acc ^= (uint32_t)dpp_i<kDppHalfMirror>((int)acc);
+  acc ^= (uint32_t)dpp_i<kDppMirror>((int)acc);
+  acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, 0) ^ (uint32_t)__builtin_amdgcn_readlane((int)acc, 16) ^
+        (uint32_t)__builtin_amdgcn_readlane((int)acc, 32) ^ (uint32_t)__builtin_amdgcn_readlane((int)acc, 48);
+  if ((tid & (kWave - 1)) == 0) sh[tid / kWave] = acc;
+  __syncthreads();
+  if (tid == 0) sink[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
+}
+
 }  // namespace
+
+long long stream_read_workgroups(long long bytes) {
+  const long long per = (long long)kBlock * kStreamVPT * 16;
+  return (bytes + per - 1) / per;
+}
+
+hipError_t launch_stream_read(const void* src, long long bytes, uint32_t* sink, hipStream_t s) {
+  const long long grid = stream_read_workgroups(bytes);
+  if (grid < 1) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(kBlock), 0, s, static_cast<const char*>(src),
+                     bytes / 16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_greedy_finish(const GreedyParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.B), block(kBlock);

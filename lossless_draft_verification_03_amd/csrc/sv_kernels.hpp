@@ -125,6 +125,10 @@ hipError_t launch_probe(const ProbeParams& p, int dt, hipStream_t s);
 
 // ---------------------------------------------------------- utilities
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+// Bandwidth probe: read [src, src + bytes) (bytes a multiple of 16) with the
+// row sweep's load pattern, one XOR word per workgroup into sink.
+long long stream_read_workgroups(long long bytes);
+hipError_t launch_stream_read(const void* src, long long bytes, uint32_t* sink, hipStream_t s);
 
 // ---------------------------------------------------------- LM head
 struct LmHeadParams {
