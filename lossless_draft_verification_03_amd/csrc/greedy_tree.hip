@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void k_tree_finish(TreeParams P) {
 }
 
 // p, q and the normalised residual of row pairs, through the same element
-// function as the sampling draw.  Test probe; one workgroup per row.
+// function as the linear sampling draw (exp_koff).  Test probe; one workgroup
+// per row.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_probe(ProbeParams P) {
   __shared__ double sh4[4];
@@ -149,23 +150,29 @@ __global__ __launch_bounds__(kBlock) void k_probe(ProbeParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   const char* t = static_cast<const char*>(P.tgt) + r * V * ES;
   const char* d = P.drf ? static_cast<const char*>(P.drf) + r * V * ES : nullptr;
+  // the linear draw's weights: 2^(z c - K) with K = fl(M c_hi), and the
+  // fp64 factors 2^(K - M c) back to 2^((z - M) c)
   const float Mt = P.row_max[r];
   const double St = P.row_sum[r];
-  float Md = 0.f;
-  double Sd = 1.0, rho = 0.0;
+  const float Kt = koff_of(Mt, P.tc);
+  const double ft = exp2_f64((double)Kt - (double)Mt * P.tc.c64);
+  float Md = 0.f, Kd = 0.f;
+  double Sd = 1.0, fd = 1.0, rho = 0.0;
   if (d) {
     Md = P.row_max[P.rows + r];
     Sd = P.row_sum[P.rows + r];
-    rho = St / Sd;
+    Kd = koff_of(Md, P.tc);
+    fd = exp2_f64((double)Kd - (double)Md * P.tc.c64);
+    rho = St / Sd * (fd / ft);
   }
   const float rho_hi = (float)rho, rho_lo = (float)(rho - (double)rho_hi);
   double part = 0.0;
   for (long long e = tid; e < V; e += kBlock) {
-    const float et = exp_rel<DT>(load_elem<DT>(t, e), Mt, P.tc);
-    P.out_p[r * V + e] = (double)et / St;
+    const float et = exp_koff(load_elem<DT>(t, e), Kt, P.tc);
+    P.out_p[r * V + e] = (double)et * ft / St;
     if (d) {
-      const float ed = exp_rel<DT>(load_elem<DT>(d, e), Md, P.tc);
-      if (P.out_q) P.out_q[r * V + e] = (double)ed / Sd;
+      const float ed = exp_koff(load_elem<DT>(d, e), Kd, P.tc);
+      if (P.out_q) P.out_q[r * V + e] = (double)ed * fd / Sd;
       float w = fmaf(-ed, rho_hi, et);
       w = fmaxf(fmaf(-ed, rho_lo, w), 0.f);
       part += (double)w;

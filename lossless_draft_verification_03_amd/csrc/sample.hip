@@ -20,16 +20,19 @@
 //               them reach the same j; workgroup (b, 0) records it.  Then the
 //               draw weights of one segment of row j are summed in fp64, each
 //               wave over its own contiguous quarter (a sub-segment):
-//                 j <  gamma : w = max(0, p_j - q_j)  (as S_t w = max(0, e_t - rho e_d))
-//                 j == gamma : w = p_gamma            (as S_t w = e_t)
+//                 j <  gamma : w = max(0, p_j - q_j)  (as max(0, e_t - rho e_d))
+//                 j == gamma : w = p_gamma            (as e_t)
+//               with e = 2^(z c - K) per element in the row sweep's K-offset
+//               form (exp_koff), K = fl(M c_hi) per row and rho absorbing
+//               both rows' normalisers and offsets.
 //  k_draw_pick  one workgroup per sequence: wave 0 locates the sub-segment
 //               holding u[b][gamma] * total among the B x 4 nseg masses, the
 //               block rescans those 2048 elements with one contiguous run per
 //               lane (weights kept in registers), block-scans the lane sums
 //               in fp64 and the crossing lane walks its run.
-// The weights cost about 26 VALU slots per element (two double-float
-// exponents), so the mass pass is VALU-bound chip-wide and the pick's rescan
-// VALU-bound on its one CU; the sub-segments cut the rescan to a quarter.
+// A residual weight costs two exp2 and about seven other VALU instructions
+// per element pair; the pick's rescan is VALU-bound on its one CU, and the
+// sub-segments cut it to a quarter of a segment.
 #include "sv_kernels.hpp"
 
 #include <limits.h>
@@ -53,8 +56,10 @@ __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
   R.resid = di.j < g;
   R.t = static_cast<const char*>(P.tgt) + ((long long)b * (g + 1) + di.j) * V * ES;
   R.d = R.resid ? static_cast<const char*>(P.drf) + ((long long)b * g + di.j) * V * ES : R.t;
-  R.Mt = di.Mt;
-  R.Md = di.Md;
+  R.Mt = 0.f;
+  R.Md = 0.f;
+  R.Kt = di.Kt;
+  R.Kd = di.Kd;
   R.rho_hi = (float)di.rho;
   R.rho_lo = (float)(di.rho - (double)R.rho_hi);
   R.rho = di.rho;
@@ -91,14 +96,14 @@ __device__ double sub_partial(const DrawRow& R, long long s0, long long s1, cons
         unpack<DT>(vt[k], zt);
         if constexpr (RESID) unpack<DT>(vd[k], zd);
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) acc += (double)draw_weight_r<DT, RESID>(R, zt[i], RESID ? zd[i] : 0.f, tc);
+        for (int i = 0; i < EPV; ++i) acc += (double)draw_weight_k<RESID>(R, zt[i], RESID ? zd[i] : 0.f, tc);
       }
     }
   } else {
     for (long long e = s0 + lane; e < s1; e += kWave) {
       const float zt = load_elem<DT>(R.t, e);
       const float zd = RESID ? load_elem<DT>(R.d, e) : 0.f;
-      acc += (double)draw_weight_r<DT, RESID>(R, zt, zd, tc);
+      acc += (double)draw_weight_k<RESID>(R, zt, zd, tc);
     }
   }
   return wave_sum(acc);
@@ -166,12 +171,18 @@ __global__ __launch_bounds__(kBlock) void k_draw_mass(SampleParams P) {
     const unsigned long long mr = __ballot(rej);
     if (tid == 0) {
       const int j = mb ? -1 : (mr ? (int)__ffsll((long long)mr) - 1 : g);
+      // the draw's weights are 2^(z c - K) with K = fl(M c_hi) per row; rho
+      // absorbs the two rows' offsets from the exact 2^((z - M) c)
       DrawInfo di;
       di.j = j;
-      di.Mt = j >= 0 ? sh_M[j] : 0.f;
-      di.Md = (j >= 0 && j < g) ? sh_M[g + 1 + j] : 0.f;
+      const float Mt = j >= 0 ? sh_M[j] : 0.f, Md = (j >= 0 && j < g) ? sh_M[g + 1 + j] : 0.f;
+      di.Kt = koff_of(Mt, P.tc);
+      di.Kd = koff_of(Md, P.tc);
       di.pad_ = 0.f;
-      di.rho = (j >= 0 && j < g) ? sh_S[j] / sh_S[g + 1 + j] : 0.0;
+      di.rho = (j >= 0 && j < g)
+                   ? sh_S[j] / sh_S[g + 1 + j] *
+                         exp2_f64(((double)di.Kd - (double)Md * P.tc.c64) - ((double)di.Kt - (double)Mt * P.tc.c64))
+                   : 0.0;
       sh_di = di;
       if (s == 0) {
         P.info[b] = di;
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
         if (R.resid) unpack<DT>(vd[k], zd);
 #pragma unroll
         for (int i = 0; i < EPV; ++i)
-          w[k * EPV + i] = k < nvec ? draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, P.tc) : 0.f;
+          w[k * EPV + i] = k < nvec ? draw_weight_k(R, zt[i], R.resid ? zd[i] : 0.f, P.tc) : 0.f;
       }
     } else {
 #pragma unroll
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
       if (ee < re) {
         const float zt = load_elem<DT>(R.t, ee);
         const float zd = R.resid ? load_elem<DT>(R.d, ee) : 0.f;
-        v = draw_weight<DT>(R, zt, zd, P.tc);
+        v = draw_weight_k(R, zt, zd, P.tc);
       }
       w[e] = v;
     }

@@ -241,9 +241,10 @@ def test_probe_probs_within_tolerance():
             ro = wo / wo.sum()
             assert np.all(np.abs(p[i] - po) <= 1e-5 * po + 1e-300)
             assert np.all(np.abs(q[i] - qo) <= 1e-5 * qo + 1e-300)
-            # residual: relative 1e-5, plus the cancellation floor of p - q
-            # (each carries ~1e-7 relative error, so |d(p - q)| <= 1e-6 (p + q))
-            bound = 1e-5 * ro + 1e-6 * (po + qo) / wo.sum()
+            # residual: relative 1e-5, plus the cancellation floor of p - q:
+            # the rule allows p and q 1e-5 relative error each, so their
+            # difference may carry 1e-5 (p + q) where p and q nearly cancel
+            bound = 1e-5 * ro + 1e-5 * (po + qo) / wo.sum()
             assert np.all(np.abs(r[i] - ro) <= bound)
 
 
