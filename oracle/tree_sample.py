@@ -25,6 +25,17 @@ bonus token is drawn from p.  Uniforms: u[n] (n >= 1) is node n's test; u[0],
 the root's slot (the root is never tested), is the final draw.  As for a
 chain of drafts, a token outside [0, V) on any node but the root makes the
 sequence invalid (accept_len = -1).
+
+Second reading, for children drawn WITHOUT replacement (EAGLE-2 keeps k
+distinct candidates per node, [M] "EAGLE-2: dynamic draft trees"; a sampling
+drafter that wants k distinct children draws them one after another from q
+with the earlier ones removed, as the Gumbel-top-k trick does in one go):
+child k's proposal is q_k = q restricted to the tokens not yet drafted at the
+node, renormalised, and every test and residual uses q_k in place of q:
+accept iff u[c] < p_k(x) / q_k(x), then p_{k+1} = norm(max(0, p_k - q_k)).
+Each test is again one rejection-sampling step of p_k with the proposal the
+child was actually drawn from, so the committed token has law p.  A proposal
+with no mass left gives q_k(x) = 0 (the ratio rule's +inf or 0).
 """
 import numpy as np
 
@@ -38,9 +49,12 @@ def children_of(parent):
     return kids
 
 
-def verify_tree_sample_seq(zt, zd, node_tokens, parent, u, T):
+def verify_tree_sample_seq(zt, zd, node_tokens, parent, u, T, siblings="iid"):
     """One sequence.  zt, zd [N, V]: target and draft rows of every node (row
     n of zd is the draft distribution n's children were drawn from).
+    siblings: "iid" (children drawn independently from q) or
+    "without_replacement" (drawn one after another from q without
+    replacement; see the module docstring).
     Returns (accept_len, path, tokens, info): accept_len = depth of the last
     accepted node (-1 for an invalid tree), path = accepted nodes from the
     root down (root excluded), tokens = their tokens then the final token.
@@ -62,18 +76,27 @@ def verify_tree_sample_seq(zt, zd, node_tokens, parent, u, T):
             break
         q = softmax(zd[n], T)
         cur = p
+        prop = q                                    # the law the next child was drawn from
         nxt = None
         for c in kids[n]:
             x = int(node_tokens[c])
-            r = accept_ratio(cur[x], q[x])
+            r = accept_ratio(cur[x], prop[x])
             tests.append((c, float(u[c]), r))
             if float(u[c]) < r:
                 nxt = c
                 break
-            res = residual(cur, q)
+            res = residual(cur, prop)
             total = np.sum(res)
             if total > 0.0:                         # > 0 in exact arithmetic after a rejection
                 cur = res / total
+            if siblings == "without_replacement":   # the next child cannot be x again
+                prop = prop.copy()
+                prop[x] = 0.0
+                left = np.sum(prop)
+                if left > 0.0:
+                    prop = prop / left
+            elif siblings != "iid":
+                raise ValueError(siblings)
         if nxt is None:
             w = cur                                 # every child rejected
             break
@@ -84,7 +107,7 @@ def verify_tree_sample_seq(zt, zd, node_tokens, parent, u, T):
     return len(path), path, tokens, dict(tests=tests, draw=draw, w=w)
 
 
-def verify_tree_sample(target, draft, dtype, node_tokens, parent, uniforms, T):
+def verify_tree_sample(target, draft, dtype, node_tokens, parent, uniforms, T, siblings="iid"):
     """Batched: target, draft [B, N, V]; parent [N] or [B, N]; uniforms [B, N].
     Returns (accept_len [B], path [B, N] -1 padded, tokens [B, N] -1 padded,
     infos)."""
@@ -98,7 +121,7 @@ def verify_tree_sample(target, draft, dtype, node_tokens, parent, uniforms, T):
     for b in range(B):
         pb = par if par.ndim == 1 else par[b]
         d, path, tk, info = verify_tree_sample_seq(decode(target[b], dtype), decode(draft[b], dtype),
-                                                   node_tokens[b], pb, uniforms[b], T)
+                                                   node_tokens[b], pb, uniforms[b], T, siblings)
         acc[b] = d
         paths[b, :len(path)] = path
         toks[b, :len(tk)] = tk

@@ -16,7 +16,7 @@ import oracle
 from oracle.tree_sample import children_of, verify_tree_sample_seq
 
 
-def _law_over_uniforms(zt, zd, tok, parent, T, N):
+def _law_over_uniforms(zt, zd, tok, parent, T, N, siblings="iid"):
     """Exact distribution of the committed tokens over the uniforms, found by
     exploring the oracle's accept tests depth first: each test splits the
     uniform's range at min(1, r); the final draw contributes its normalised
@@ -29,7 +29,7 @@ def _law_over_uniforms(zt, zd, tok, parent, T, N):
         u = np.full(N, 0.5)
         for c, v in fixed.items():
             u[c] = v
-        d, path, tokens, info = verify_tree_sample_seq(zt, zd, tok, parent, u, T)
+        d, path, tokens, info = verify_tree_sample_seq(zt, zd, tok, parent, u, T, siblings)
         undecided = [(c, r) for (c, _, r) in info["tests"] if c not in fixed]
         if not undecided:
             w = np.asarray(info["w"], np.float64)
@@ -108,6 +108,120 @@ def test_tree_sampling_preserves_the_target_distribution():
                 got = second[a] / second[a].sum()
                 want = oracle.softmax(model([a])[0], T)
                 assert np.max(np.abs(got - want)) < 1e-12, (si, a)
+
+
+def _committed_law(shapes_and_models, V, T, siblings, distinct):
+    """For each (parent, model): the exact law of the first committed token
+    and of the second given the first, over the draft tokens (i.i.d. from q
+    per node, or drawn without replacement: ordered distinct tuples, child k
+    of a node weighted q(x_k) / (1 - sum of q over the earlier siblings))
+    and over the uniforms."""
+    out = []
+    for parent, model in shapes_and_models:
+        N = len(parent)
+        kids = children_of(parent)
+        first = np.zeros(V)
+        second = np.zeros((V, V))
+        for assign in itertools.product(range(V), repeat=N - 1):
+            tok = np.array([0] + list(assign))
+            if distinct and any(len({int(tok[c]) for c in kids[n]}) < len(kids[n]) for n in range(N)):
+                continue
+            paths = [[]] * N
+            for n in range(1, N):
+                paths[n] = paths[parent[n]] + [int(tok[n])]
+            weight = 1.0
+            for n in range(N):
+                q = oracle.softmax(model(paths[n])[1], T)
+                left = 1.0
+                for c in kids[n]:
+                    weight *= q[tok[c]] / left
+                    if distinct:
+                        left -= q[tok[c]]
+            zt = np.stack([model(paths[n])[0] for n in range(N)])
+            zd = np.stack([model(paths[n])[1] for n in range(N)])
+            for prob, prefix, law in _law_over_uniforms(zt, zd, tok, parent, T, N, siblings):
+                pw = weight * prob
+                if prefix:
+                    first[prefix[0]] += pw
+                    if len(prefix) >= 2:
+                        second[prefix[0], prefix[1]] += pw
+                    else:
+                        second[prefix[0]] += pw * law
+                else:
+                    first += pw * law
+        out.append((first, second))
+    return out
+
+
+def _worst_error(laws, shapes_and_models, T):
+    """Largest deviation of the committed laws from the target's."""
+    err = 0.0
+    for (first, second), (_, model) in zip(laws, shapes_and_models):
+        err = max(err, np.max(np.abs(first - oracle.softmax(model([])[0], T))))
+        for a in range(len(first)):
+            if second[a].sum() > 1e-9:
+                got = second[a] / second[a].sum()
+                err = max(err, np.max(np.abs(got - oracle.softmax(model([a])[0], T))))
+    return err
+
+
+def test_without_replacement_siblings_preserve_the_target_distribution():
+    # children drawn one after another without replacement (EAGLE-2's k
+    # distinct candidates per node, sampled): exact enumeration over ordered
+    # distinct sibling tuples.  V = 3 with three siblings makes the last
+    # sibling's proposal a point mass on the one token left.
+    cases = [
+        ([-1, 0, 0], 4),
+        ([-1, 0, 0, 0], 4),
+        ([-1, 0, 0, 0], 3),
+        ([-1, 0, 0, 1, 2], 4),
+        ([-1, 0, 1, 0, 1, 1], 3),
+    ]
+    T = 0.8
+    bias = []
+    for ci, (parent, V) in enumerate(cases):
+        sm = [(parent, _path_model(V, 70 + ci))]
+        laws = _committed_law(sm, V, T, "without_replacement", distinct=True)
+        assert _worst_error(laws, sm, T) < 1e-12, ci
+        bias.append(_worst_error(_committed_law(sm, V, T, "iid", distinct=True), sm, T))
+    # the i.i.d. rule applied to such children is biased (a residual that has
+    # collapsed onto one token hides it, so not in every case): the pin tells
+    # the two readings apart
+    assert max(bias) > 1e-2, bias
+
+
+def test_without_replacement_equals_iid_without_siblings():
+    rng = np.random.default_rng(11)
+    parent = np.array([-1, 0, 1, 2, 3])
+    for trial in range(20):
+        V = int(rng.integers(2, 30))
+        zt = rng.normal(0, 2, (5, V))
+        zd = zt + rng.normal(0, 1, (5, V))
+        tok = rng.integers(0, V, 5)
+        u = rng.random(5)
+        a = verify_tree_sample_seq(zt, zd, tok, parent, u, 1.0, "iid")
+        b = verify_tree_sample_seq(zt, zd, tok, parent, u, 1.0, "without_replacement")
+        assert a[:3] == b[:3], trial
+
+
+def test_without_replacement_rejects_a_repeated_sibling():
+    # a token drafted twice at one node has no proposal mass the second time
+    # and no residual target mass left after its first rejection
+    rng = np.random.default_rng(5)
+    parent = np.array([-1, 0, 0, 0])
+    for trial in range(50):
+        V = int(rng.integers(3, 12))
+        zt = rng.normal(0, 2, (4, V))
+        zd = rng.normal(0, 2, (4, V))
+        x = int(rng.integers(0, V))
+        y = (x + 1) % V
+        tok = np.array([0, x, x, y])
+        u = rng.random(4)
+        u[1] = 0.999999                                  # the first x is rejected
+        _, _, _, info = verify_tree_sample_seq(zt, zd, tok, parent, u, 1.0, "without_replacement")
+        tests = {c: r for (c, _, r) in info["tests"]}
+        if tests[1] < u[1]:
+            assert tests[2] == 0.0, trial
 
 
 def test_chain_tree_equals_linear_speculative_sampling():
