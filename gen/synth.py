@@ -173,7 +173,11 @@ def make_tree_sample(cfg):
     (row n belongs to node n), node tokens [B,N], parent [N] (or [B,N] for
     tree="random_per_seq"), uniforms [B,N].  The children of a node are
     independent Gumbel-max draws from q = softmax(draft row / T) of the
-    parent, the way a sampling drafter grows the tree."""
+    parent, the way a sampling drafter grows the tree; with
+    siblings="without_replacement", the m children of a node (in index order)
+    are the m largest of one Gumbel-perturbed copy of the parent's draft row,
+    best first: m draws from q one after another without replacement (the
+    Gumbel-top-k trick), so a node needs m <= V."""
     B, N, V, dt, T = cfg["B"], cfg["N"], cfg["V"], cfg["dtype"], float(cfg["temperature"])
     ss = np.random.SeedSequence(cfg["seed"]).spawn(6)
     shape = cfg.get("tree", "binary")
@@ -188,6 +192,13 @@ def make_tree_sample(cfg):
     target = np.empty((B, N, V), odt)
     draft = np.empty((B, N, V), odt)
     node_tokens = np.zeros((B, N), np.int32)
+    siblings = cfg.get("siblings", "iid")
+    if siblings not in ("iid", "without_replacement"):
+        raise ValueError(siblings)
+    if siblings != "iid":
+        for par in (parent if parent.ndim == 2 else parent[None]):
+            if N > 1 and np.bincount(par[1:], minlength=N).max() > V:
+                raise ValueError("a node has more children than there are tokens to draw without replacement")
 
     def seq(b):
         par = parent if parent.ndim == 1 else parent[b]
@@ -196,11 +207,22 @@ def make_tree_sample(cfg):
         draft[b] = _round(zd, dt)
         if N > 1:
             zd = _as_f64(draft[b], dt)
-            node_tokens[b, 1:] = _gumbel_max(_rng(kid_x[b]), zd[par[1:]], T)
+            if siblings == "iid":
+                node_tokens[b, 1:] = _gumbel_max(_rng(kid_x[b]), zd[par[1:]], T)
+                return
+            rng = _rng(kid_x[b])
+            for n in range(N):
+                kids = np.nonzero(par == n)[0]
+                kids = kids[kids > 0]
+                if len(kids) == 0:
+                    continue
+                g = zd[n] / T + rng.gumbel(size=V)
+                top = np.argsort(-g, kind="stable")[:len(kids)]
+                node_tokens[b, kids] = top
 
     _parallel(B, seq)
     uniforms = _rng(ss[3]).random((B, N), dtype=np.float32)
-    return dict(kind="tree_sample", dtype=dt, B=B, N=N, V=V, temperature=np.float32(T),
+    return dict(kind="tree_sample", dtype=dt, B=B, N=N, V=V, temperature=np.float32(T), siblings=siblings,
                 target=target, draft=draft, node_tokens=node_tokens, parent=parent, uniforms=uniforms)
 
 
@@ -247,7 +269,7 @@ def make_workload(name, cache=False, **overrides):
     if os.path.exists(path):
         with np.load(path, allow_pickle=False) as f:
             out = {k: f[k] for k in f.files}
-        for k in ("kind", "dtype"):
+        for k in ("kind", "dtype", "siblings"):
             if k in out:
                 out[k] = str(out[k])
         for k in ("B", "gamma", "V", "N", "d"):

@@ -79,6 +79,14 @@ typedef enum {
                      a linear layer's weight is usually stored (faster path)  */
 } spec_wlayout;
 
+/* How the children of one draft-tree node were drawn (sampling trees). */
+typedef enum {
+  SPEC_SIBLINGS_IID = 0,      /* independently from the node's draft law q  */
+  SPEC_SIBLINGS_DISTINCT = 1  /* one after another from q without
+                                 replacement (k distinct candidates, e.g. by
+                                 the Gumbel-top-k trick)                   */
+} spec_siblings;
+
 typedef enum {
   SPEC_MODE_SAMPLE = 0,   /* spec_verify_sample: gamma_or_N = gamma        */
   SPEC_MODE_GREEDY = 1,   /* spec_verify_greedy: gamma_or_N = gamma        */
@@ -304,15 +312,18 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * Reduce Quality?" (A(x) = min(1, p(x)/q(x)); resample from
  * norm(max(0, p - q))).
  *
- * p = softmax(target row / T), q = softmax(draft row / T).  The children of
- * a node are taken to be independent draws from that node's q.  From the
- * root: the children of the current node are tested in increasing index;
- * child c (token x) is accepted iff uniforms[b][c] < p_k(x) / q(x), with
- * p_1 = p and p_{k+1} = norm(max(0, p_k - q)) after each rejection; an
- * accepted child becomes the current node.  If every child is rejected one
- * token is drawn from the last residual; at a node without children the
- * bonus token is drawn from p.  The final draw takes uniforms[b][0]
- * (inverse CDF in vocabulary order, as in spec_verify_sample).
+ * p = softmax(target row / T), q = softmax(draft row / T).  From the root:
+ * the children of the current node are tested in increasing index; child c,
+ * the k-th (token x), is accepted iff uniforms[b][c] < p_k(x) / q_k(x), with
+ * p_1 = p and p_{k+1} = norm(max(0, p_k - q_k)) after each rejection; an
+ * accepted child becomes the current node.  q_k is the law child k was drawn
+ * from: q itself for SPEC_SIBLINGS_IID; for SPEC_SIBLINGS_DISTINCT, q with
+ * the tokens of children 1 .. k-1 removed and renormalised (a token repeated
+ * among siblings then has q_k(x) = 0 and no residual mass: it is rejected).
+ * If every child is rejected one token is drawn from the last residual; at a
+ * node without children the bonus token is drawn from p.  The final draw
+ * takes uniforms[b][0] (inverse CDF in vocabulary order, as in
+ * spec_verify_sample).
  *
  * target_logits, draft_logits [B, N, V] (dt): row n of each belongs to node
  *               n; draft row n is the law n's children were drawn from.
@@ -323,6 +334,7 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * parent        [N] (parent_batch_stride = 0) or [B, N] (= N): parent[0] = -1
  *               and 0 <= parent[n] < n.
  * uniforms      [B, N] float32 in [0, 1).
+ * siblings      SPEC_SIBLINGS_IID or SPEC_SIBLINGS_DISTINCT (else EINVAL).
  * n_sweep       nodes 0 .. n_sweep-1 of every sequence have both rows swept
  *               across the whole GPU before the walk; deeper visited nodes
  *               are reduced on demand by their sequence's workgroup.  -1
@@ -341,7 +353,8 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
                                     spec_dtype dt, const int32_t* node_tokens,
                                     const int32_t* parent, int parent_batch_stride,
                                     const float* uniforms, int B, int N, int V,
-                                    float temperature, int n_sweep, int32_t* accept_len,
+                                    float temperature, spec_siblings siblings, int n_sweep,
+                                    int32_t* accept_len,
                                     int32_t* out_path, int32_t* out_tokens, void* ws,
                                     size_t ws_bytes, hipStream_t s);
 

@@ -25,6 +25,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 MODE_SAMPLE, MODE_GREEDY, MODE_TREE, MODE_LMHEAD, MODE_ROWSTATS, MODE_TREE_EXPAND, MODE_TREE_SAMPLE = range(7)
 SPEC_NOALLOC_SCRATCH_BYTES = 16 << 20  # the static workspace of spec_verify_sample_noalloc
 W_DV, W_VD = 0, 1  # LM-head weight [d, V] (vocabulary innermost) or [V, d] (feature innermost)
+SIBLINGS = {"iid": 0, "without_replacement": 1}  # how a tree node's children were drawn
 MAX_GAMMA = 63
 MAX_TREE_NODES = 4096
 
@@ -43,8 +44,8 @@ _SIGS = {
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
-                                     _sz, _vp]),
+    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp,
+                                     _vp, _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_project_staged": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "lmhead_project_workspace_bytes": (_sz, [_i, _i]),
@@ -211,12 +212,16 @@ def verify_tree(target, node_tokens, parent, ws=None, out=None):
     return out
 
 
-def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None, n_sweep=-1):
+def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None, n_sweep=-1,
+                       siblings="iid"):
     """target, draft [B, N, V]; node_tokens [B, N]; parent [N] or [B, N];
-    uniforms [B, N] -> (accept_len, out_path, out_tokens).  n_sweep: nodes
-    whose rows are swept before the walk (-1: automatic); a workspace passed
-    in must be sized with the same n_sweep (new_workspace(MODE_TREE_SAMPLE,
-    B, N, V, n_sweep))."""
+    uniforms [B, N] -> (accept_len, out_path, out_tokens).  siblings: "iid"
+    (children drawn independently from q) or "without_replacement" (drawn one
+    after another without replacement).  n_sweep: nodes whose rows are swept
+    before the walk (-1: automatic); a workspace passed in must be sized with
+    the same n_sweep (new_workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep))."""
+    if siblings not in SIBLINGS:
+        raise ValueError("siblings must be one of %s" % sorted(SIBLINGS))
     B, N, V = target.shape
     if tuple(draft.shape) != (B, N, V) or dtype_code(draft) != dtype_code(target):
         raise ValueError("draft must match target in shape and dtype")
@@ -229,7 +234,7 @@ def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature
     w = _workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep, dev, ws)
     _check(lib.spec_verify_tree_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(node_tokens),
                                        _ptr(parent), stride, _ptr(uniforms), B, N, V, float(temperature),
-                                       int(n_sweep), _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
+                                       SIBLINGS[siblings], int(n_sweep), _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
                                        _stream(dev)),
            "spec_verify_tree_sample")
     return out

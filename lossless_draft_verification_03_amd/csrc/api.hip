@@ -513,10 +513,11 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
 
 spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
                                     const int32_t* node_tokens, const int32_t* parent, int parent_batch_stride,
-                                    const float* uniforms, int B, int N, int V, float temperature, int n_sweep,
-                                    int32_t* accept_len, int32_t* out_path, int32_t* out_tokens, void* ws,
-                                    size_t ws_bytes, hipStream_t s) {
+                                    const float* uniforms, int B, int N, int V, float temperature,
+                                    spec_siblings siblings, int n_sweep, int32_t* accept_len, int32_t* out_path,
+                                    int32_t* out_tokens, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!dtype_ok(dt)) return SPEC_EDTYPE;
+  if (siblings != SPEC_SIBLINGS_IID && siblings != SPEC_SIBLINGS_DISTINCT) return SPEC_EINVAL;
   if (B < 1 || B > SPEC_MAX_BATCH || N < 1 || N > SPEC_MAX_TREE_NODES || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
       !row_bytes_ok(V, dt))
     return SPEC_EINVAL;
@@ -547,6 +548,7 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   p.N = N;
   p.V = V;
   p.tc = tc;
+  p.distinct = siblings == SPEC_SIBLINGS_DISTINCT;
   p.nseg = sh.nseg;
   p.seg_vecs = sh.seg_vecs;
   p.n_pre = (int)tree_presweep_nodes(B, N, V, (int)dt, n_sweep);

@@ -242,6 +242,7 @@ struct TreeSampleParams {
   const float* unif;       // [B, N]: u[b][n] tests node n, u[b][0] is the final draw
   int B, N, V;
   TempConst tc;
+  int distinct;            // 1: siblings drawn without replacement (q_k excludes earlier siblings)
   int nseg;                // row sweep segments per row (row_sweep_shape)
   int seg_vecs;
   int n_pre;               // nodes 0 .. n_pre-1 have their rows swept before the walk

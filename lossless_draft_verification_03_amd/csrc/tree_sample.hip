@@ -8,23 +8,41 @@
 // Decoding", 3. Accept or Reject.
 //
 // Reading of the sibling rule (the pages name it for trees without spelling
-// out siblings): the children of a node were drawn independently from the
-// node's draft row q and are tried in increasing node index; the first child
-// is tested against p_1 = p, and after each rejection the law moves on to
-// p_{k+1} = norm(max(0, p_k - q)).  An accepted child becomes the current
-// node; when every child is rejected one token is drawn from the last
-// residual; at a node without children the bonus token is drawn from p.
-// Uniforms: u[n] (n >= 1) is node n's test, u[0] the final draw.
+// out siblings): the children of a node are tried in increasing node index;
+// child k (token x) is tested against p_k(x) / q_k(x), where p_1 = p, q_k is
+// the law child k was drawn from, and after each rejection the law moves on
+// to p_{k+1} = norm(max(0, p_k - q_k)).  Two drafting laws: children drawn
+// independently from the node's draft row q (q_k = q), or one after another
+// without replacement (q_k = q with the earlier siblings' tokens removed,
+// renormalised: EAGLE-2's k distinct candidates per node, sampled).  An
+// accepted child becomes the current node; when every child is rejected one
+// token is drawn from the last residual; at a node without children the
+// bonus token is drawn from p.  Uniforms: u[n] (n >= 1) is node n's test,
+// u[0] the final draw.
 //
-// Closed form used for the residual chain.  With c_1 = 0, W_1 = 1,
-//   p_k = max(0, p - c_k q) / W_k,  c_{k+1} = c_k + W_k,
+// Closed form used for the residual chain.  Let R_k = 1 - sum_{i<k} q(x_i)
+// over distinct earlier siblings (R_k = 1 for independent draws), so
+// q_k = q / R_k off the removed tokens.  With c_1 = 0, W_1 = 1,
+//   p_k = max(0, p - c_k q) / W_k,  c_{k+1} = c_k + W_k / R_k,
 //   W_{k+1} = sum_v max(0, p(v) - c_{k+1} q(v)).
-// (Induction: where p > c_k q, max(0, p_k - q) = max(0, p - (c_k + W_k) q)
-// / W_k; elsewhere both sides are 0.)  So child k passes iff
-//   u < max(0, p(x)/q(x) - c_k) / W_k,
+// (Induction: where p > c_k q and v is not removed, max(0, p_k - q_k) =
+// max(0, p - (c_k + W_k / R_k) q) / W_k; elsewhere both sides are 0.  A
+// removed token x_i was rejected, so p_i(x_i) < q_i(x_i), which is
+// p(x_i) < c_{i+1} q(x_i): the formula already gives it no mass later.)  So
+// child k passes iff
+//   u < R_k max(0, p(x)/q(x) - c_k) / W_k,
 // the ratio p(x)/q(x) formed in fp64 exactly as in the chain sampler, and a
 // residual is a draw row with rho = c S_t / S_d.  A zero W (impossible in
-// exact arithmetic after a rejection) leaves (c, W) unchanged.
+// exact arithmetic after a rejection) leaves (c, W) unchanged.  Without
+// replacement, a token repeated among siblings is rejected (q_k(x) = 0 and
+// p_k(x) = 0) and R_k = 0 (no proposal mass left) gives the ratio rule's
+// q = 0 case and leaves (c, W) unchanged.  R_k is the ratio of two sums that
+// the W pass after the previous rejection forms from the same fp64 draft
+// weights e: over the tokens not removed, and over the whole row.  Nothing
+// cancels, so R_k keeps its relative precision however small it is (a
+// peaked draft whose first sibling holds all but 1e-12 of q is the usual
+// case for k distinct children), and it is exactly 0 when every token with
+// weight has been removed.  (1 - sum q(x_i) would lose R_k to cancellation.)
 //
 // k_tree_presweep (optional): the rows of the first n_pre nodes of every
 // sequence, one row segment per workgroup across the whole chip.
@@ -82,6 +100,7 @@ struct WalkLds {
   float gt[kTreeMaxNodes];   // target logit of node c's token in its parent's row
   float gd[kTreeMaxNodes];   // draft logit of the same
   int kids[kTreeMaxNodes];   // children of the current node, index order
+  int xt[kTreeMaxNodes];     // without replacement: tokens of the siblings tried so far
   double seg[kTMaxSeg];      // segment masses of the last pass
   Partial part[2 * kTLdsPart];
   float qm[kTQuarters][kBlock / kWave];
@@ -94,6 +113,8 @@ struct WalkLds {
   float M[2];
   double S[2];
   double total, base, thr;
+  double wrem[kTW];
+  double sd_all, sd_rem;     // SD passes: draft weight sums over the row, over the tokens kept
   long long y;
   int nk, k, fallback;
 };
@@ -102,16 +123,35 @@ struct WalkLds {
 // contiguous sub-segments of [e0, e1), lane-interleaved 16-byte vectors, fp64
 // accumulation; returns this lane's partial.  F64W: each weight formed in
 // fp64 (draw_weight_f64; the W passes of the residual chain), else the final
-// draw's fp32 weight (draw_weight, which the pick rescans).
-template <int DT, bool ALIGNED, bool F64W>
+// draw's fp32 weight (draw_weight, which the pick rescans).  SD (with F64W on
+// a residual row): also add this lane's fp64 draft weights e_d to sd[0], and
+// those of tokens other than xt[0 .. nx) to sd[1].
+template <int DT, bool ALIGNED, bool F64W, bool SD>
 __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1, const TempConst& tc, int wid,
-                                   int lane) {
+                                   int lane, double* sd, const int* xt, int nx) {
+  static_assert(!SD || F64W, "draft sums come with the fp64 weights");
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int SUB = walk_seg<DT>() / kTW;
+  static_assert(SUB / kWave <= 32, "one bit per element of a lane's share");
   const long long s0 = min(e0 + (long long)wid * SUB, e1);
   const long long s1 = min(s0 + SUB, e1);
   double acc = 0.0;
+  // SD: bit j set when the lane's j-th element of this sub-segment is a
+  // removed token (element order of the loops below)
+  uint32_t xm = 0;
+  if constexpr (SD) {
+    for (int j = 0; j < nx; ++j) {
+      const long long off = (long long)xt[j] - s0;
+      if (off < 0 || off >= s1 - s0) continue;
+      const int o = (int)off;
+      if constexpr (ALIGNED) {
+        if (((o / EPV) & (kWave - 1)) == lane) xm |= 1u << ((o / EPV / kWave) * EPV + o % EPV);
+      } else {
+        if ((o & (kWave - 1)) == lane) xm |= 1u << (o / kWave);
+      }
+    }
+  }
   if constexpr (ALIGNED) {
     constexpr int KV = SUB / EPV / kWave;
     const int nvec = (int)((s1 - s0) / EPV);
@@ -133,16 +173,33 @@ __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1,
       if (R.resid) unpack<DT>(vd[k], zd);
 #pragma unroll
       for (int i = 0; i < EPV; ++i) {
-        if constexpr (F64W) acc += draw_weight_f64<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
-        else acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+        if constexpr (SD) {
+          const double ed = exp_rel_f64<DT>(zd[i], R.Md, tc);
+          acc += fmax(fma(-R.rho, ed, exp_rel_f64<DT>(zt[i], R.Mt, tc)), 0.0);
+          sd[0] += ed;
+          if (!((xm >> (k * EPV + i)) & 1u)) sd[1] += ed;
+        } else if constexpr (F64W) {
+          acc += draw_weight_f64<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+        } else {
+          acc += (double)draw_weight<DT>(R, zt[i], R.resid ? zd[i] : 0.f, tc);
+        }
       }
     }
   } else {
-    for (long long e = s0 + lane; e < s1; e += kWave) {
+    int j = 0;
+    for (long long e = s0 + lane; e < s1; e += kWave, ++j) {
       const float zt = load_elem<DT>(R.t, e);
       const float zd = R.resid ? load_elem<DT>(R.d, e) : 0.f;
-      if constexpr (F64W) acc += draw_weight_f64<DT>(R, zt, zd, tc);
-      else acc += (double)draw_weight<DT>(R, zt, zd, tc);
+      if constexpr (SD) {
+        const double ed = exp_rel_f64<DT>(zd, R.Md, tc);
+        acc += fmax(fma(-R.rho, ed, exp_rel_f64<DT>(zt, R.Mt, tc)), 0.0);
+        sd[0] += ed;
+        if (!((xm >> j) & 1u)) sd[1] += ed;
+      } else if constexpr (F64W) {
+        acc += draw_weight_f64<DT>(R, zt, zd, tc);
+      } else {
+        acc += (double)draw_weight<DT>(R, zt, zd, tc);
+      }
     }
   }
   return acc;
@@ -152,19 +209,22 @@ __device__ double walk_sub_partial(const DrawRow& R, long long e0, long long e1,
 // fixed combination order throughout); if sub is not null, also every
 // segment's kTW sub-segment masses into sub[segment * kTW + sub-segment]
 // (global memory, read back by this workgroup after a barrier).  Every
-// thread of the block calls it.  F64W as in walk_sub_partial.
-template <int DT, bool ALIGNED, bool F64W>
+// thread of the block calls it.  F64W and SD as in walk_sub_partial; SD
+// leaves the draft row's fp64 weight sums (lanes, then waves, in a fixed
+// order) in L.sd_all (every token) and L.sd_rem (every token but xt[0 .. nx)).
+template <int DT, bool ALIGNED, bool F64W, bool SD = false>
 __device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, WalkLds& L, int tid,
-                            double* sub) {
+                            double* sub, const int* xt = nullptr, int nx = 0) {
   constexpr int SEG = walk_seg<DT>();
   const int lane = tid & (kWave - 1), wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nseg = (int)((V + SEG - 1) / SEG);
+  double sd[2] = {0.0, 0.0};
   for (int s0 = 0; s0 < nseg; s0 += kTChunk) {
     const int s1 = min(s0 + kTChunk, nseg);
     for (int s = s0; s < s1; ++s) {
       const long long e0 = (long long)s * SEG;
       const long long e1 = e0 + SEG < V ? e0 + SEG : V;
-      const double a = wave_sum(walk_sub_partial<DT, ALIGNED, F64W>(R, e0, e1, tc, wid, lane));
+      const double a = wave_sum(walk_sub_partial<DT, ALIGNED, F64W, SD>(R, e0, e1, tc, wid, lane, sd, xt, nx));
       if (lane == 0) {
         L.red[(s - s0) * kTW + wid] = a;
         if (sub != nullptr) sub[s * kTW + wid] = a;
@@ -178,10 +238,29 @@ __device__ double mass_pass(const DrawRow& R, long long V, const TempConst& tc, 
     }
     __syncthreads();
   }
+  if constexpr (SD) {
+    const double all = wave_sum(sd[0]), rem = wave_sum(sd[1]);
+    if (lane == 0) {
+      L.wtot[wid] = all;
+      L.wrem[wid] = rem;
+    }
+    __syncthreads();
+  }
   if (wid == 0) {
     double tot = 0.0;
     for (int c0 = 0; c0 < nseg; c0 += kWave) tot += wave_sum(c0 + lane < nseg ? L.seg[c0 + lane] : 0.0);
     if (lane == 0) L.total = tot;
+    if constexpr (SD) {
+      if (lane == 0) {
+        double ta = 0.0, tr = 0.0;
+        for (int w = 0; w < kTW; ++w) {
+          ta += L.wtot[w];
+          tr += L.wrem[w];
+        }
+        L.sd_all = ta;
+        L.sd_rem = tr;
+      }
+    }
   }
   __syncthreads();
   return L.total;
@@ -439,24 +518,41 @@ __global__ __launch_bounds__(kTB) void k_tree_walk(TreeSampleParams P) {
     // every thread evaluates the same tests on the same LDS values, so the
     // decisions (and the passes between them) are block-uniform
     double cc = 0.0, W = 1.0;
+    double Rk = 1.0;                          // without replacement: R_k of the child being tested
     int chosen = -1;
     for (int i = 0; i < nk; ++i) {
       const int ci = L.kids[i];
-      const double r = child_ratio(L.gt[ci], L.gd[ci], Mt, St, Md, Sd, cc, W, P.tc);
+      double r = child_ratio(L.gt[ci], L.gd[ci], Mt, St, Md, Sd, cc, W, P.tc);
+      if (P.distinct && i > 0) {
+        int hit = 0;
+        for (int j = tid; j < i; j += kTB) hit |= L.tok[L.kids[j]] == L.tok[ci];
+        const bool dup = __syncthreads_or(hit) != 0;
+        r = dup ? 0.0 : (Rk > 0.0 ? Rk * r : (r > 0.0 ? __builtin_huge_val() : 0.0));
+      }
       if ((double)L.u[ci] < r) {
         chosen = ci;
         break;
       }
-      const double cn = cc + W;
+      const double cn = Rk > 0.0 ? cc + W / Rk : cc;
       if (i + 1 == nk) {                      // every child rejected
         set_rho(R, cn, St, Sd);
         c_fb = cc;
         break;
       }
       set_rho(R, cn, St, Sd);
+      if (!(Rk > 0.0)) continue;              // the residual is the current law: (c, W) stay
       // W of the next residual: fp64 weights, so a test's value
-      // max(0, p(x)/q(x) - c)/W carries no fp32 rounding of the residual
-      const double Wn = mass_pass<DT, ALIGNED, true>(R, V, P.tc, L, tid, nullptr) / St;
+      // max(0, p(x)/q(x) - c)/W carries no fp32 rounding of the residual;
+      // without replacement the same pass sums the draft row's weights
+      double Wn;
+      if (P.distinct) {
+        for (int j = tid; j <= i; j += kTB) L.xt[j] = L.tok[L.kids[j]];
+        __syncthreads();
+        Wn = mass_pass<DT, ALIGNED, true, true>(R, V, P.tc, L, tid, nullptr, L.xt, i + 1) / St;
+        Rk = L.sd_all > 0.0 ? L.sd_rem / L.sd_all : 0.0;
+      } else {
+        Wn = mass_pass<DT, ALIGNED, true>(R, V, P.tc, L, tid, nullptr) / St;
+      }
       if (Wn > 0.0) {
         cc = cn;
         W = Wn;

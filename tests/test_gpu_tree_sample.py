@@ -25,14 +25,15 @@ def _run(w, T=None, n_sweep=-1):
     T = float(w["temperature"]) if T is None else T
     acc, path, toks = L.verify_tree_sample(to_dev(w["target"]), to_dev(w["draft"]), to_dev(w["node_tokens"]),
                                            to_dev(np.ascontiguousarray(w["parent"]).astype(np.int32)),
-                                           to_dev(w["uniforms"]), T, n_sweep=n_sweep)
+                                           to_dev(w["uniforms"]), T, n_sweep=n_sweep,
+                                           siblings=w.get("siblings", "iid"))
     return acc.cpu().numpy(), path.cpu().numpy(), toks.cpu().numpy()
 
 
 def _oracle(w, T=None):
     T = float(w["temperature"]) if T is None else T
     return oracle.verify_tree_sample(w["target"], w["draft"], w["dtype"], w["node_tokens"], w["parent"],
-                                     w["uniforms"], T)
+                                     w["uniforms"], T, w.get("siblings", "iid"))
 
 
 def _parents(w):
@@ -197,3 +198,97 @@ def test_committed_tokens_follow_the_target_law():
         r = res / res.sum()
     rate = float(np.mean(acc >= 1))
     assert abs(rate - (1.0 - left)) < 4 * np.sqrt(left * (1 - left) / B) + 1e-9, (rate, 1 - left)
+
+
+# ------------------------------------------------ children without replacement
+@pytest.mark.parametrize("dtype,V,N,tree,noise,T", [
+    ("f32", 1000, 15, "binary", 0.8, 1.0),
+    ("bf16", 777, 31, "random_per_seq", 1.5, 0.7),     # ragged V, per-sequence parents
+    ("bf16", 512, 12, "star", 3.0, 1.0),               # 11 distinct siblings
+    ("f32", 300, 21, "wide", 1.0, 0.6),
+    ("f32", 40, 40, "random", 2.0, 1.3),               # tiny V, many siblings
+    ("bf16", 70001, 7, "star", 2.5, 1.0),              # several draw segments, unaligned
+    ("bf16", 131080, 5, "wide", 2.0, 0.9),             # several draw segments, aligned
+])
+def test_without_replacement_matches_oracle(dtype, V, N, tree, noise, T):
+    w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
+                      temperature=T, siblings="without_replacement", seed=V + N + 1)
+    g, _ = _check(w)
+    for ns in (0, N):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
+
+
+def test_without_replacement_full_size_and_differs_from_iid():
+    # the benchmark's shapes with two distinct children per node
+    w = make_workload("tree_sample63", siblings="without_replacement", seed=3, cache=True)
+    g, _ = _check(w)
+    # the other rule on the same inputs: its own oracle, and different
+    # decisions somewhere (the first sibling's test is the same, later ones not)
+    wi = dict(w, siblings="iid")
+    gi, _ = _check(wi)
+    assert any(not np.array_equal(x, y) for x, y in zip(g, gi))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_without_replacement_peaked_draft(dtype):
+    # the first sibling holds nearly all of q (logit gaps 9, 20, 35 over the
+    # rest of the row): the later siblings' proposals q / R_k have R_k from
+    # ~1e-3 down to ~1e-12, where 1 - q(x_1) would be lost to cancellation
+    w = make_workload("tree_sample63", B=60, N=9, V=5000, dtype="f32", tree="star", draft_noise=1.0,
+                      temperature=1.0, siblings="without_replacement", seed=8)
+    dr = w["draft"].astype(np.float64)
+    for b in range(w["B"]):
+        dr[b, 0, int(w["node_tokens"][b, 1])] = dr[b, 0].max() + (9.0, 20.0, 35.0)[b % 3] + 0.05 * b
+    if dtype == "bf16":
+        from gen.synth import f32_to_bf16_bits
+        w["target"] = f32_to_bf16_bits(w["target"])
+        w["draft"] = f32_to_bf16_bits(dr.astype(np.float32))
+        w["dtype"] = "bf16"
+    else:
+        w["draft"] = dr.astype(np.float32)
+    (acc, _, _), _ = _check(w)
+    assert np.any(acc == 0)
+    # R_2 = 1 - q(x_1) in fp64 from the oracle's own law: down to ~1e-12
+    zd = oracle.decode(w["draft"][:, 0], w["dtype"])
+    r2 = [1.0 - oracle.softmax(zd[b], 1.0)[int(w["node_tokens"][b, 1])] for b in range(w["B"])]
+    assert min(r2) < 1e-10
+
+
+def test_without_replacement_repeated_and_exhausted_siblings():
+    # tokens repeated among siblings (rejected), and V = 3 with all three
+    # tokens as children (the last proposal a point mass; then nothing left)
+    rng = np.random.default_rng(31)
+    w = make_workload("tree_sample63", B=40, N=6, V=3, dtype="f32", tree="star", draft_noise=2.0,
+                      temperature=1.0, siblings="iid", seed=31)
+    w["siblings"] = "without_replacement"
+    tok = w["node_tokens"]
+    for b in range(20, 40):
+        tok[b, 1:4] = rng.permutation(3)
+    w["uniforms"][:, 1:] = np.maximum(w["uniforms"][:, 1:], np.float32(0.6))   # more rejections
+    _check(w, max_explained=1)
+
+
+def test_without_replacement_committed_tokens_follow_the_target_law():
+    # 3 distinct siblings under the root (V = 4), drawn without replacement
+    # from q: the first committed token must follow p; chi-square with 3
+    # degrees of freedom against the 0.999 quantile (fixed seed)
+    rng = np.random.default_rng(22)
+    B, V, N, T = 120000, 4, 4, 1.0
+    zt = np.array([1.0, 0.2, -0.5, 0.7])
+    zd = np.array([-0.3, 1.1, 0.4, 0.0])
+    p = np.exp(zt / T) / np.exp(zt / T).sum()
+    target = np.broadcast_to(zt.astype(np.float32), (B, N, V)).copy()
+    draft = np.broadcast_to(zd.astype(np.float32), (B, N, V)).copy()
+    tokens = np.zeros((B, N), np.int32)
+    tokens[:, 1:] = np.argsort(-(zd / T + rng.gumbel(size=(B, V))), axis=1, kind="stable")[:, :3]
+    w = dict(dtype="f32", B=B, N=N, V=V, temperature=np.float32(T), target=target, draft=draft,
+             node_tokens=tokens, parent=np.array([-1, 0, 0, 0], np.int32),
+             uniforms=rng.random((B, N), dtype=np.float32), siblings="without_replacement")
+    acc, path, toks = _run(w)
+    counts = np.bincount(toks[:, 0], minlength=V)
+    chi2 = float(np.sum((counts - B * p) ** 2 / (B * p)))
+    assert chi2 < 16.27, (counts / B, p, chi2)
+    # the same children verified with the i.i.d. rule are biased
+    acc_i, _, toks_i = _run(dict(w, siblings="iid"))
+    counts_i = np.bincount(toks_i[:, 0], minlength=V)
+    assert float(np.sum((counts_i - B * p) ** 2 / (B * p))) > 100.0
