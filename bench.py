@@ -487,7 +487,24 @@ def main():
             "full_sweep_equiv_GBs": round(sbytes / (sms * 1e-3) / 1e9, 1),
             "mean_accept_len": round(sout[0].float().mean().item(), 3),
             "max_accept_len": int(sout[0].max().item())}
-        del st_, sd_, sws
+        del st_, sd_
+        # the same shapes with each node's two children drawn from q without
+        # replacement (distinct tokens, the top-k style of tree)
+        rw = make_workload("tree_sample63", siblings="without_replacement", seed=3, cache=True)
+        rt_, rd_ = d(rw["target"]), d(rw["draft"])
+        rn, rp, ru = d(rw["node_tokens"]), d(rw["parent"]), d(rw["uniforms"])
+
+        def rstep(i):
+            L.verify_tree_sample(rt_, rd_, rn, rp, ru, sT, ws=sws, out=sout, siblings="without_replacement")
+
+        for i in range(args.warmup):
+            rstep(i)
+        rms = time_events(rstep, args.steps, stream)
+        modes["tree_sample_distinct_b32n63v128k"] = {
+            "ms": round(rms, 5), "sequences_per_s": round(rw["B"] / (rms * 1e-3), 1),
+            "mean_accept_len": round(sout[0].float().mean().item(), 3),
+            "max_accept_len": int(sout[0].max().item())}
+        del rt_, rd_, sws
         torch.cuda.empty_cache()
         # KV compaction to the paths the tree verifier accepted: a cache of
         # 32 layers x (K, V) planes of 8 heads x 128 bf16 per entry

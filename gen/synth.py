@@ -217,8 +217,9 @@ def make_tree_sample(cfg):
                 if len(kids) == 0:
                     continue
                 g = zd[n] / T + rng.gumbel(size=V)
-                top = np.argsort(-g, kind="stable")[:len(kids)]
-                node_tokens[b, kids] = top
+                m = len(kids)
+                top = np.argpartition(-g, m - 1)[:m] if m < V else np.arange(V)
+                node_tokens[b, kids] = top[np.argsort(-g[top], kind="stable")]
 
     _parallel(B, seq)
     uniforms = _rng(ss[3]).random((B, N), dtype=np.float32)
