@@ -101,6 +101,7 @@ typedef enum {
 /* Limits checked by every entry point. */
 #define SPEC_MAX_GAMMA 63       /* one 64-wide wavefront lane per position   */
 #define SPEC_MAX_TREE_NODES 4096
+#define SPEC_MAX_TREE_ROUNDS 64   /* n_rounds limit of spec_verify_tree_sample */
 #define SPEC_MAX_BATCH (1 << 20)
 #define SPEC_MAX_SAMPLE_VOCAB (1 << 25)   /* V limit of the sampling calls */
 #define SPEC_MAX_TOPK 16          /* children per expanded draft-tree node    */
@@ -337,9 +338,16 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt,
  * siblings      SPEC_SIBLINGS_IID or SPEC_SIBLINGS_DISTINCT (else EINVAL).
  * n_sweep       nodes 0 .. n_sweep-1 of every sequence have both rows swept
  *               across the whole GPU before the walk; deeper visited nodes
- *               are reduced on demand by their sequence's workgroup.  -1
- *               picks the prefix from B, N and V.  Outputs do not depend on
- *               it (both reductions give the same bits); -1 <= n_sweep <= N.
+ *               are reduced when the walk reaches them.  -1 picks the prefix
+ *               from B, N and V.  -1 <= n_sweep <= N.
+ * n_rounds      the walk's passes over a node's rows (its row statistics on
+ *               arrival, the residual mass W after a rejected sibling) run
+ *               across the whole GPU in up to n_rounds rounds, two launches
+ *               each; passes a walk still needs after them run on its
+ *               sequence's own workgroup.  -1 picks a number from N;
+ *               -1 <= n_rounds <= SPEC_MAX_TREE_ROUNDS.  Outputs depend on
+ *               neither n_sweep nor n_rounds: every placement of a pass
+ *               gives the same bits.
  * accept_len [B] out: number of accepted nodes; -1 when the tree is invalid
  *            or a token of a node n >= 1 lies outside [0, V) (outputs -1).
  * out_path   [B, N] out: accepted nodes (root excluded) in root-to-leaf
@@ -354,7 +362,7 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
                                     const int32_t* parent, int parent_batch_stride,
                                     const float* uniforms, int B, int N, int V,
                                     float temperature, spec_siblings siblings, int n_sweep,
-                                    int32_t* accept_len,
+                                    int n_rounds, int32_t* accept_len,
                                     int32_t* out_path, int32_t* out_tokens, void* ws,
                                     size_t ws_bytes, hipStream_t s);
 

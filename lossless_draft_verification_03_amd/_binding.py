@@ -44,8 +44,8 @@ _SIGS = {
     "spec_verify_sample_early_exit": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_tree": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp,
-                                     _vp, _sz, _vp]),
+    "spec_verify_tree_sample": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _f, _i, _i, _i, _vp, _vp,
+                                     _vp, _vp, _sz, _vp]),
     "lmhead_project": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp]),
     "lmhead_project_staged": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "lmhead_project_workspace_bytes": (_sz, [_i, _i]),
@@ -213,13 +213,14 @@ def verify_tree(target, node_tokens, parent, ws=None, out=None):
 
 
 def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature, ws=None, out=None, n_sweep=-1,
-                       siblings="iid"):
+                       siblings="iid", n_rounds=-1):
     """target, draft [B, N, V]; node_tokens [B, N]; parent [N] or [B, N];
     uniforms [B, N] -> (accept_len, out_path, out_tokens).  siblings: "iid"
     (children drawn independently from q) or "without_replacement" (drawn one
     after another without replacement).  n_sweep: nodes whose rows are swept
     before the walk (-1: automatic); a workspace passed in must be sized with
-    the same n_sweep (new_workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep))."""
+    the same n_sweep (new_workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep)).
+    n_rounds: chip-wide pass rounds of the walk (-1: automatic)."""
     if siblings not in SIBLINGS:
         raise ValueError("siblings must be one of %s" % sorted(SIBLINGS))
     B, N, V = target.shape
@@ -234,7 +235,7 @@ def verify_tree_sample(target, draft, node_tokens, parent, uniforms, temperature
     w = _workspace(MODE_TREE_SAMPLE, B, N, V, n_sweep, dev, ws)
     _check(lib.spec_verify_tree_sample(_ptr(target), _ptr(draft), dtype_code(target), _ptr(node_tokens),
                                        _ptr(parent), stride, _ptr(uniforms), B, N, V, float(temperature),
-                                       SIBLINGS[siblings], int(n_sweep), _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
+                                       SIBLINGS[siblings], int(n_sweep), int(n_rounds), _ptr(acc), _ptr(path), _ptr(toks), _ptr(w), w.numel(),
                                        _stream(dev)),
            "spec_verify_tree_sample")
     return out

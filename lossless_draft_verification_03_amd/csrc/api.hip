@@ -15,6 +15,7 @@ using namespace sv;
 
 static_assert(SPEC_MAX_TREE_NODES == kTreeMaxNodes, "tree size limit of the walk kernel");
 static_assert((long long)SPEC_MAX_SAMPLE_VOCAB == kMaxSampleVocab, "vocabulary limit of the draw kernels");
+static_assert(SPEC_MAX_TREE_ROUNDS == kTreeMaxRounds, "round limit of the tree sampler");
 
 namespace {
 
@@ -29,16 +30,28 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // no initialisation and can be shared by calls of any layout (one at a time).
 struct Layout {
   size_t info, part, rmax, rsum, rarg, gath, segsum, hcat, logits, total;
+  size_t tstate, tglog, twpart;        // tree sampler: walk states, token logits, W sums
   long long rows;
   int nseg, nseg2;
 };
 
 // Nodes whose rows the tree sampler sweeps before its walk.  n_sweep >= 0
 // is the caller's choice (at most N); -1 picks as many leading nodes as fit
-// about kTreePresweepBytes of target and draft rows, the point where sweeping
-// a prefix node for every sequence costs about what one on-demand visit of a
-// node costs a walk (a single CU reduces one node's two rows).
-constexpr long long kTreePresweepBytes = 160LL << 20;
+// about kTreePresweepBytes of target and draft rows.  A walk reaches a node
+// beyond the prefix one round later, and a round costs about what sweeping
+// this many bytes does (measured on 32 trees of 63 nodes at V = 128256, bf16:
+// 4 nodes, against 0 to 10).
+constexpr long long kTreePresweepBytes = 64LL << 20;
+
+// Chip-wide rounds of a tree-sampling call when the caller leaves it open:
+// a round costs about 2.5 us when no walk needs it, while a pass left to the
+// finishing kernel costs one CU about 20 us, so enough rounds for the walks
+// of the usual tree shapes (a visit beyond the prefix and a W pass per
+// level), at most one per node beyond the root.
+int tree_auto_rounds(int N) {
+  const int r = 8;
+  return N - 1 < r ? (N - 1 > 0 ? N - 1 : 0) : r;
+}
 
 long long tree_presweep_nodes(long long B, long long N, long long V, int dt, long long n_sweep) {
   if (n_sweep >= 0) return n_sweep < N ? n_sweep : N;
@@ -69,9 +82,10 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
       rows = B * gN;
       break;
     case SPEC_MODE_TREE_SAMPLE: {
-      // the walk's per-sequence partials of one target and one draft row,
-      // then those of the swept prefix (d carries the call's n_sweep); sized
-      // for whichever element type needs more
+      // the walk's per-sequence partials of one target and one draft row
+      // (two buffers, alternating between rounds), then those of the swept
+      // prefix (d carries the call's n_sweep); sized for whichever element
+      // type needs more
       if (gN < 1 || gN > SPEC_MAX_TREE_NODES || d < -1 || d > gN) return false;
       long long pre = 0;
       for (int t = 0; t < 2; ++t) {
@@ -79,7 +93,7 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
             2 * B * tree_presweep_nodes(B, gN, V, t, d) * row_sweep_shape((int)V, t).nseg;
         if (need > pre) pre = need;
       }
-      rows = 2 * B + (pre + row_sweep_shape((int)V, DT_F32).nseg - 1) / row_sweep_shape((int)V, DT_F32).nseg;
+      rows = 4 * B + (pre + row_sweep_shape((int)V, DT_F32).nseg - 1) / row_sweep_shape((int)V, DT_F32).nseg;
       break;
     }
     case SPEC_MODE_ROWSTATS:
@@ -104,9 +118,14 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
   L->rarg = o;   o = up(o + (size_t)rows * 4);
   L->gath = o;   o = up(o + (size_t)rows * 4);
   // the linear draw's sub-segment masses; the tree walk's in the tree sampler
-  const size_t segsum_bytes = mode == SPEC_MODE_TREE_SAMPLE ? (size_t)B * tree_walk_subsegments(V, DT_F32) * 8
+  const size_t segsum_bytes = mode == SPEC_MODE_TREE_SAMPLE ? (size_t)B * tree_segments(V) * kDrawSub * 8
                                                             : (size_t)seqs * nseg2 * kDrawSub * 8;
   L->segsum = o; o = up(o + segsum_bytes);
+  if (mode == SPEC_MODE_TREE_SAMPLE) {
+    L->tstate = o; o = up(o + (size_t)2 * B * sizeof(TreeWalkState));
+    L->tglog = o;  o = up(o + (size_t)B * gN * 2 * 4);
+    L->twpart = o; o = up(o + (size_t)2 * B * tree_segments(V) * 3 * 8);
+  }
   L->hcat = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + lmhead_staged_bytes(rows, d));
   L->logits = o;
@@ -514,10 +533,12 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
 spec_status spec_verify_tree_sample(const void* target_logits, const void* draft_logits, spec_dtype dt,
                                     const int32_t* node_tokens, const int32_t* parent, int parent_batch_stride,
                                     const float* uniforms, int B, int N, int V, float temperature,
-                                    spec_siblings siblings, int n_sweep, int32_t* accept_len, int32_t* out_path,
-                                    int32_t* out_tokens, void* ws, size_t ws_bytes, hipStream_t s) {
+                                    spec_siblings siblings, int n_sweep, int n_rounds, int32_t* accept_len,
+                                    int32_t* out_path, int32_t* out_tokens, void* ws, size_t ws_bytes,
+                                    hipStream_t s) {
   if (!dtype_ok(dt)) return SPEC_EDTYPE;
   if (siblings != SPEC_SIBLINGS_IID && siblings != SPEC_SIBLINGS_DISTINCT) return SPEC_EINVAL;
+  if (n_rounds < -1 || n_rounds > SPEC_MAX_TREE_ROUNDS) return SPEC_EINVAL;
   if (B < 1 || B > SPEC_MAX_BATCH || N < 1 || N > SPEC_MAX_TREE_NODES || V < 1 || V > SPEC_MAX_SAMPLE_VOCAB ||
       !row_bytes_ok(V, dt))
     return SPEC_EINVAL;
@@ -552,9 +573,13 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   p.nseg = sh.nseg;
   p.seg_vecs = sh.seg_vecs;
   p.n_pre = (int)tree_presweep_nodes(B, N, V, (int)dt, n_sweep);
+  p.rounds = n_rounds >= 0 ? n_rounds : tree_auto_rounds(N);
   p.ws_part = at<Partial>(ws, L.part);
-  p.pre_part = p.ws_part + 2LL * B * sh.nseg;
+  p.pre_part = p.ws_part + 4LL * B * sh.nseg;
   p.ws_sub = at<double>(ws, L.segsum);
+  p.state = at<TreeWalkState>(ws, L.tstate);
+  p.glog = at<float>(ws, L.tglog);
+  p.wpart = at<double>(ws, L.twpart);
   p.accept_len = accept_len;
   p.out_path = out_path;
   p.out_tokens = out_tokens;

@@ -221,17 +221,26 @@ hipError_t launch_tree_build(const TreeBuildParams& p, hipStream_t s);
 
 // ---------------------------------------------------------- tree sampling
 constexpr int kTreeMaxNodes = 4096;           // nodes per tree (verification calls)
+constexpr int kTreeMaxRounds = 64;            // chip-wide pass rounds of one tree-sampling call
 constexpr long long kMaxSampleVocab = 1LL << 25;
 
-// One workgroup per sequence walks its tree, computing the row statistics of
-// the nodes it visits on the way (the rows of other nodes are never read).
-// The tree walk's draw segments (1024 threads x 32 bf16 or 16 fp32 elements)
-// and the kTreeWalkSub sub-segments of each whose masses its final draw keeps.
-constexpr int kTreeWalkSub = 16;
-__host__ __device__ constexpr long long tree_walk_seg(int dt) { return dt == DT_BF16 ? 32768 : 16384; }
-__host__ __device__ inline long long tree_walk_subsegments(long long V, int dt) {
-  return (V + tree_walk_seg(dt) - 1) / tree_walk_seg(dt) * kTreeWalkSub;
-}
+// The walk keeps each sequence's state in the workspace between its kernels.
+// Passes over a node's rows after the row sweep (W passes, the final draw)
+// work in segments of kTreeSeg elements, one 256-thread workgroup each, one
+// 2048-element sub-segment per wave.
+constexpr int kTreeSeg = 8192;
+__host__ __device__ inline long long tree_segments(long long V) { return (V + kTreeSeg - 1) / kTreeSeg; }
+
+struct TreeWalkState {
+  int n, d, i, phase;      // current node, accepted depth, next child to test (index order), pending work
+  int nk, mready;          // children of n (set with a pending row sweep); draw masses in place
+  float Mt, Md;            // row statistics of n
+  double St, Sd;
+  double cc, W, Rk;        // the residual chain at n: p_i = max(0, p - cc q) / W, and R_i
+  double cn, cfb;          // c of the pending W pass or draw, and of the law before it
+  double pad2_;
+};
+static_assert(sizeof(TreeWalkState) == 96, "state layout");
 
 struct TreeSampleParams {
   const void* tgt;         // [B, N, V] target rows of the nodes
@@ -246,9 +255,13 @@ struct TreeSampleParams {
   int nseg;                // row sweep segments per row (row_sweep_shape)
   int seg_vecs;
   int n_pre;               // nodes 0 .. n_pre-1 have their rows swept before the walk
+  int rounds;              // chip-wide rounds before the walks finish on their own CUs
   Partial* pre_part;       // [2 B n_pre][nseg]: target rows (b, n), then draft rows (b, n)
-  Partial* ws_part;        // [B][2 nseg] partials of the walk, used when nseg exceeds the LDS slots
-  double* ws_sub;          // [B][tree_walk_subsegments(V, dt)] sub-segment masses of the final draw
+  Partial* ws_part;        // [2][B][2 nseg]: partials of a node swept during the walk (two buffers)
+  TreeWalkState* state;    // [2][B] (two buffers)
+  float* glog;             // [B][N][2]: node c's token logit in its parent's target and draft rows
+  double* wpart;           // [2][B][tree_segments(V)][3]: W-pass segment sums (two buffers)
+  double* ws_sub;          // [B][tree_segments(V) * kDrawSub] sub-segment masses of the final draw
   int32_t* accept_len;     // [B]
   int32_t* out_path;       // [B, N]
   int32_t* out_tokens;     // [B, N]

@@ -189,12 +189,13 @@ def test_tree_sample_rejects_invalid_arguments():
 
     def call(**kw):
         a = dict(t=FAKE, d=FAKE, dt=1, tok=FAKE, par=FAKE, ps=0, u=FAKE, B=2, N=15, V=1000, T=0.7, sib=0,
-                 ns=-1, acc=FAKE, path=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
+                 ns=-1, nr=-1, acc=FAKE, path=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
         a.update(kw)
         return fn(a["t"], a["d"], a["dt"], a["tok"], a["par"], a["ps"], a["u"], a["B"], a["N"], a["V"], a["T"],
-                  a["sib"], a["ns"], a["acc"], a["path"], a["out"], a["ws"], a["wsb"], None)
+                  a["sib"], a["ns"], a["nr"], a["acc"], a["path"], a["out"], a["ws"], a["wsb"], None)
     assert call(dt=3) == 2
     assert call(sib=2) == 1 and call(sib=-1) == 1                    # SPEC_SIBLINGS_IID or _DISTINCT
+    assert call(nr=-2) == 1 and call(nr=65) == 1                     # -1 <= n_rounds <= 64
     assert call(B=0) == 1 and call(N=0) == 1 and call(N=4097) == 1 and call(V=0) == 1
     assert call(V=(1 << 25) + 1) == 1
     assert call(ps=7) == 1                                           # parent stride must be 0 or N

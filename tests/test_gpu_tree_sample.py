@@ -21,12 +21,12 @@ L = sentinel.wrap(_binding)   # every output buffer sentinel-filled before each 
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, T=None, n_sweep=-1):
+def _run(w, T=None, n_sweep=-1, n_rounds=-1):
     T = float(w["temperature"]) if T is None else T
     acc, path, toks = L.verify_tree_sample(to_dev(w["target"]), to_dev(w["draft"]), to_dev(w["node_tokens"]),
                                            to_dev(np.ascontiguousarray(w["parent"]).astype(np.int32)),
                                            to_dev(w["uniforms"]), T, n_sweep=n_sweep,
-                                           siblings=w.get("siblings", "iid"))
+                                           siblings=w.get("siblings", "iid"), n_rounds=n_rounds)
     return acc.cpu().numpy(), path.cpu().numpy(), toks.cpu().numpy()
 
 
@@ -65,9 +65,10 @@ def test_matches_oracle(dtype, V, N, tree, noise, T):
     w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
                       temperature=T, seed=V + N)
     g, _ = _check(w)
-    # the swept prefix changes where the statistics are reduced, not their bits
-    for ns in (0, N // 2, N):
-        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
+    # the swept prefix and the number of chip-wide rounds change where the
+    # statistics and the W sums are reduced, not their bits
+    for ns, nr in ((0, -1), (N // 2, -1), (N, -1), (-1, 0), (-1, 1), (0, 2), (N, 3), (0, 64)):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns, n_rounds=nr), g)), (ns, nr)
 
 
 def test_large_vocabulary_uses_workspace_partials():
@@ -85,7 +86,9 @@ def test_largest_tree():
     for tree, noise in (("star", 3.0), ("chain", 0.3)):
         w = make_workload("tree_sample63", B=2, N=L.MAX_TREE_NODES, V=97, dtype="f32", tree=tree,
                           draft_noise=noise, temperature=1.0, seed=13)
-        _check(w)
+        g, _ = _check(w)
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_rounds=64), g))
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_rounds=0), g))
 
 
 def test_matches_oracle_many_rejections():
@@ -99,8 +102,8 @@ def test_full_size():
     # the benchmark's shapes: 32 sequences, 63-node binary tree, 128256 bf16
     w = make_workload("tree_sample63", cache=True)
     g, _ = _check(w)
-    for ns in (0, 63):
-        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
+    for ns, nr in ((0, -1), (63, -1), (-1, 0), (-1, 2), (0, 64)):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns, n_rounds=nr), g)), (ns, nr)
 
 
 def test_chain_tree_equals_chain_sampler():
@@ -214,8 +217,8 @@ def test_without_replacement_matches_oracle(dtype, V, N, tree, noise, T):
     w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
                       temperature=T, siblings="without_replacement", seed=V + N + 1)
     g, _ = _check(w)
-    for ns in (0, N):
-        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns), g)), ns
+    for ns, nr in ((0, -1), (N, -1), (-1, 0), (0, 1), (N, 2), (-1, 64)):
+        assert all(np.array_equal(x, y) for x, y in zip(_run(w, n_sweep=ns, n_rounds=nr), g)), (ns, nr)
 
 
 def test_without_replacement_full_size_and_differs_from_iid():
