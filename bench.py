@@ -347,11 +347,12 @@ def main():
         # early-exit verification on the same replicas, then on a batch with
         # low acceptance (draft noise 3.0) against the full sweep
         def ee_blocks(K):
-            # the library's blocks: K positions each, or 1, 2, 4, ... for K = 0
+            # the library's blocks: K positions each; K = 0: position 0, then
+            # the rest; K = -1: 1, 2, 4, ... positions
             out, i0, n = [], 0, (K if K > 0 else 1)
             while i0 <= g:
                 out.append((i0, min(i0 + n, g + 1)))
-                i0, n = min(i0 + n, g + 1), (K if K > 0 else 2 * n)
+                i0, n = min(i0 + n, g + 1), (K if K > 0 else (g if K == 0 else 2 * n))
             return out
 
         def ee_bytes(acc_h, K):
@@ -371,19 +372,18 @@ def main():
             _, t, dr = reps[i % R]
             L.verify_sample(t, dr, x, u, T, ws=ws, out=eout, early_exit=True, positions_per_launch=K)
 
-        K_half = (g + 2) // 2                  # two launches
         for i in range(args.warmup):
             estep(i)
             estep(i, 1)
-            estep(i, K_half)
+            estep(i, -1)
         ems1 = time_events(lambda i: estep(i, 1), args.steps, stream)
-        emsh = time_events(lambda i: estep(i, K_half), args.steps, stream)
+        emsd = time_events(lambda i: estep(i, -1), args.steps, stream)
         ems = time_events(estep, args.steps, stream)
         ee = {"ms": round(ems, 5), "blocks": ee_blocks(K_auto),
               "positions_per_s": round(B * g / (ems * 1e-3), 1),
               "rows_bytes_read": ee_bytes(eout[0].cpu().numpy(), K_auto), "full_sweep_ms": round(ms, 5),
               "ms_one_position_per_launch": round(ems1, 5),
-              f"ms_{K_half}_positions_per_launch": round(emsh, 5)}
+              "ms_doubling_blocks": round(emsd, 5)}
         del reps
         torch.cuda.empty_cache()
         wl = make_workload("b64g7v128k", draft_noise=3.0, seed=5)
@@ -403,12 +403,15 @@ def main():
             lstep(i, False)
             lstep(i, True)
             lstep(i, True, 1)
+            lstep(i, True, -1)
         lfull = time_events(lambda i: lstep(i, False), args.steps, stream)
         lee1 = time_events(lambda i: lstep(i, True, 1), args.steps, stream)
+        leed = time_events(lambda i: lstep(i, True, -1), args.steps, stream)
         lee = time_events(lambda i: lstep(i, True), args.steps, stream)
         ee["low_acceptance"] = {"draft_noise": 3.0, "mean_accept_len": round(eout[0].float().mean().item(), 3),
                                 "full_sweep_ms": round(lfull, 5), "early_exit_ms": round(lee, 5),
                                 "early_exit_ms_one_position_per_launch": round(lee1, 5),
+                                "early_exit_ms_doubling_blocks": round(leed, 5),
                                 "rows_bytes_read": ee_bytes(eout[0].cpu().numpy(), K_auto)}
         del lo
         torch.cuda.empty_cache()
@@ -430,10 +433,12 @@ def main():
             l4(i, False)
             l4(i, True)
             l4(i, True, 1)
+            l4(i, True, -1)
         ee["low_acceptance_b256"] = {
             "full_sweep_ms": round(time_events(lambda i: l4(i, False), 10, stream), 5),
             "early_exit_ms": round(time_events(lambda i: l4(i, True), 10, stream), 5),
-            "early_exit_ms_one_position_per_launch": round(time_events(lambda i: l4(i, True, 1), 10, stream), 5)}
+            "early_exit_ms_one_position_per_launch": round(time_events(lambda i: l4(i, True, 1), 10, stream), 5),
+            "early_exit_ms_doubling_blocks": round(time_events(lambda i: l4(i, True, -1), 10, stream), 5)}
         modes["early_exit_b64g7v128k"] = ee
         del lo4, ws4
         torch.cuda.empty_cache()

@@ -246,9 +246,11 @@ spec_status spec_verify_sample_noalloc(const void* target_logits, const void* dr
  *   launch per block; a sequence's next block is read only if every position
  *   of its earlier blocks was accepted.  K = gamma + 1 is one full sweep.
  *   Smaller K reads fewer rows and pays one launch latency (about 5 us) per
- *   block.  0 picks blocks of 1, 2, 4, ... positions: within twice the rows of
- *   K = 1 whatever the acceptance, in ceil(log2(gamma + 2)) launches.
- *   0 <= K <= gamma + 1.
+ *   block.  0 picks two blocks, position 0 then positions 1..gamma: a
+ *   sequence whose first draft is rejected reads one position's rows, and
+ *   the others read all of theirs in one more launch.  -1 picks blocks of
+ *   1, 2, 4, ... positions: within twice the rows of K = 1 whatever the
+ *   acceptance, in ceil(log2(gamma + 2)) launches.  -1 <= K <= gamma + 1.
  */
 spec_status spec_verify_sample_early_exit(const void* target_logits, const void* draft_logits,
                                           spec_dtype dt, const int32_t* draft_tokens,

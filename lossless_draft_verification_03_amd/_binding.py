@@ -159,8 +159,8 @@ def verify_sample(target, draft, draft_tokens, uniforms, temperature, ws=None, o
                   positions_per_launch=0):
     """target [B, g+1, V], draft [B, g, V] -> (accept_len [B], out_tokens [B, g+1]).
     early_exit: sweep the rows in blocks of positions_per_launch positions (0:
-    automatic) and skip a sequence's later blocks after a rejection (same
-    results)."""
+    position 0, then the rest; -1: blocks of 1, 2, 4, ...) and skip a
+    sequence's later blocks after a rejection (same results)."""
     B, g1, V = target.shape
     g = g1 - 1
     dev = target.device

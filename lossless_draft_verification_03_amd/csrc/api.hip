@@ -447,14 +447,15 @@ spec_status spec_verify_sample_early_exit(const void* target_logits, const void*
   const spec_status st = check_sample_args(target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V,
                                            temperature, accept_len, out_tokens, ws, ws_bytes, &tc, &L);
   if (st != SPEC_OK) return st;
-  if (positions_per_launch < 0 || positions_per_launch > gamma + 1) return SPEC_EINVAL;
+  if (positions_per_launch < -1 || positions_per_launch > gamma + 1) return SPEC_EINVAL;
   const int K = positions_per_launch;
   RowStatsParams r = sample_sweep_params(target_logits, draft_logits, draft_tokens, B, gamma, V, (int)dt, tc, ws, L);
   r.step_B = B;
   r.step_unif = uniforms;
   r.step_alive = at<int>(ws, L.rarg);  // [B, gamma+1]; the sampler leaves this region unused
-  // blocks of K positions, or of 1, 2, 4, ... positions for K = 0
-  for (int i0 = 0, prev = -1, len = K > 0 ? K : 1; i0 <= gamma; len = K > 0 ? K : 2 * len) {
+  // blocks of K positions; for K = 0 position 0, then the rest; for K = -1
+  // blocks of 1, 2, 4, ... positions
+  for (int i0 = 0, prev = -1, len = K > 0 ? K : 1; i0 <= gamma; len = K > 0 ? K : (K == 0 ? gamma : 2 * len)) {
     r.step = i0;
     r.step_end = i0 + len < gamma + 1 ? i0 + len : gamma + 1;
     r.step_prev = prev;

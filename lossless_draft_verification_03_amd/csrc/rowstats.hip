@@ -47,7 +47,6 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   __shared__ float sh_m[kBlock / kWave];
   __shared__ double sh_s[kBlock / kWave];
   __shared__ int sh_a[kBlock / kWave];
-  __shared__ int sh_alive;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const long long unit = blockIdx.x;
@@ -69,43 +68,15 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
     const int i = i0 + k / 2, kind = k & 1;
     const long long ab = b * (g + 1);
     r = kind == 0 ? ab + i : P.rows0 + b * g + i;
-    // The block is needed only if positions 0 .. i0-1 were all accepted: the
-    // previous block recorded whether 0 .. ip-1 were, and positions
-    // ip .. i0-1 are tested here from their rows' partials and gathered
-    // logits, one position per group of STEPNP lanes, each group merging as
-    // the draw kernel does.
-    if (wid == 0) {
-      int al = 1;
-      if (ip >= 0) {
-        al = P.step_alive[ab + ip];
-        if (al) {
-          constexpr int G = kWave / STEPNP;
-          const int gq = lane / STEPNP, gl = lane & (STEPNP - 1);
-          for (int c0 = ip; c0 < i0; c0 += G) {
-            const int ii = c0 + gq;
-            const bool live = ii < i0;        // uniform per lane group
-            bool rej = false;
-            if (live) {
-              const int x = P.gather_tokens[b * g + ii];
-              float Mt, Md;
-              double St, Sd;
-              int a;
-              merge_partials<1, STEPNP>(P.part + (ab + ii) * P.nseg, P.nseg, P.tc, gl, &Mt, &St, &a);
-              merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + ii) * P.nseg, P.nseg, P.tc, gl, &Md, &Sd, &a);
-              rej = x < 0 || x >= P.V ||
-                    sample_rejects(P.gather_out[ab + ii], P.gather_out[P.rows0 + b * g + ii], Mt, St, Md, Sd,
-                                   P.step_unif[ab + ii], P.tc);
-            }
-            if (__ballot(rej)) al = 0;
-          }
-        }
-      }
-      if (lane == 0) sh_alive = al;
+    // The block is needed only if positions 0 .. i0-1 were all accepted, as
+    // k_step_alive recorded before this launch (the first block is always
+    // needed; it records that for the next test).
+    (void)ip;
+    if (ip < 0) {
+      if (k == 0 && s == 0 && tid == 0) P.step_alive[ab + i0] = 1;
+    } else if (!P.step_alive[ab + i0]) {
+      return;                                 // uniform
     }
-    __syncthreads();
-    const int alive = sh_alive;
-    if (k == 0 && s == 0 && tid == 0) P.step_alive[ab + i0] = alive;
-    if (!alive) return;
   }
   const bool second = r >= P.rows0;
   const char* base = static_cast<const char*>(second ? P.src1 : P.src0);
@@ -143,6 +114,44 @@ __global__ __launch_bounds__(kBlock) void k_row_merge(RowStatsParams P) {
   }
 }
 
+// Early exit: whether each sequence needs the block starting at position
+// i0 = step.  alive[b][i0] = alive[b][ip] and every position ip .. i0-1
+// (ip = step_prev, the previous block's first position) accepted, tested
+// from the rows' partials and gathered logits, one position per group of
+// STEPNP lanes, each group merging as the draw kernel does, so the decision
+// is the draw's bit for bit.  One wave per sequence.
+template <int STEPNP>
+__global__ __launch_bounds__(kBlock) void k_step_alive(RowStatsParams P) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const long long b = (long long)blockIdx.x * (kBlock / kWave) + tid / kWave;
+  if (b >= P.step_B) return;                  // whole waves; no barriers here
+  const int i0 = P.step, ip = P.step_prev, g = P.gather_g;
+  const long long ab = b * (g + 1);
+  int al = P.step_alive[ab + ip];
+  if (al) {
+    constexpr int G = kWave / STEPNP;
+    const int gq = lane / STEPNP, gl = lane & (STEPNP - 1);
+    for (int c0 = ip; c0 < i0; c0 += G) {
+      const int ii = c0 + gq;
+      const bool live = ii < i0;              // uniform per lane group
+      bool rej = false;
+      if (live) {
+        const int x = P.gather_tokens[b * g + ii];
+        float Mt, Md;
+        double St, Sd;
+        int a;
+        merge_partials<1, STEPNP>(P.part + (ab + ii) * P.nseg, P.nseg, P.tc, gl, &Mt, &St, &a);
+        merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + ii) * P.nseg, P.nseg, P.tc, gl, &Md, &Sd, &a);
+        rej = x < 0 || x >= P.V ||
+              sample_rejects(P.gather_out[ab + ii], P.gather_out[P.rows0 + b * g + ii], Mt, St, Md, Sd,
+                             P.step_unif[ab + ii], P.tc);
+      }
+      if (__ballot(rej)) al = 0;
+    }
+  }
+  if (lane == 0) P.step_alive[ab + i0] = al;
+}
+
 template <int DT, int WANT>
 hipError_t launch_sweep_t(const RowStatsParams& p, hipStream_t s) {
   const long long grid = (p.rows0 + p.rows1) * (long long)p.nseg;
@@ -159,6 +168,10 @@ hipError_t launch_step_np(const RowStatsParams& p, hipStream_t s) {
   const long long grid = (long long)p.step_B * per * p.nseg;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (p.step_prev >= 0) {
+    const long long wpb = kBlock / kWave;
+    hipLaunchKernelGGL((k_step_alive<NP>), dim3((unsigned)((p.step_B + wpb - 1) / wpb)), dim3(kBlock), 0, s, p);
+  }
   hipLaunchKernelGGL((k_row_sweep<DT, 1, NP>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }

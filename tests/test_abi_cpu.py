@@ -64,6 +64,21 @@ def test_sample_rejects_invalid_arguments(kw, code):
     assert _sample(**kw) == code
 
 
+def test_early_exit_block_size_checked_before_any_launch():
+    # -1 <= positions_per_launch <= gamma + 1 (0: two blocks, -1: doubling
+    # blocks); the sampling checks come first, with the same codes
+    fn = L.lib.spec_verify_sample_early_exit
+
+    def call(K, **kw):
+        a = dict(t=FAKE, d=FAKE, dt=L.SPEC_BF16, x=FAKE, u=FAKE, B=2, g=3, V=100, T=1.0, acc=FAKE, out=FAKE,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return fn(a["t"], a["d"], a["dt"], a["x"], a["u"], a["B"], a["g"], a["V"], a["T"], K, a["acc"], a["out"],
+                  a["ws"], a["wsb"], None)
+    assert call(-2) == 1 and call(5) == 1 and call(-5) == 1
+    assert call(0, g=0) == 1 and call(0, t=FAKE + 4) == 3 and call(0, ws=None) == 4
+
+
 def test_other_entry_points_reject_invalid_arguments():
     lib = L.lib
     assert lib.spec_verify_greedy(None, 1, FAKE, 1, 1, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1

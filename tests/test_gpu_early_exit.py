@@ -21,7 +21,7 @@ L = sentinel.wrap(_binding)   # every output buffer sentinel-filled before each 
 pytestmark = pytest.mark.gpu
 
 
-def _both(w, T=None, ks=(0, 1, 2, 3)):
+def _both(w, T=None, ks=(0, -1, 1, 2, 3)):
     """The full sweep and early exit with each block size in ks (0 =
     automatic); asserts the early-exit outputs agree across block sizes."""
     t, d = to_dev(w["target"]), to_dev(w["draft"])
@@ -68,14 +68,14 @@ def test_early_exit_matches_oracle_on_zipf():
 @pytest.mark.parametrize("B,g,V", [(1, 1, 1), (3, 2, 3), (2, 3, 5), (5, 1, 4097), (2, 63, 300), (4, 5, 16385)])
 def test_early_exit_edge_shapes(dt, B, g, V):
     w = make_workload("tiny", B=B, gamma=g, V=V, dtype=dt, seed=B * 100 + g)
-    (a1, o1), (a2, o2) = _both(w, ks=(0, 1, 2, 5, g, g + 1))
+    (a1, o1), (a2, o2) = _both(w, ks=(0, -1, 1, 2, 5, g, g + 1))
     assert np.array_equal(a1, a2) and np.array_equal(o1, o2)
 
 
 def test_early_exit_block_size_checked():
     w = make_workload("tiny", B=2, gamma=4, V=100, seed=1)
     args = (to_dev(w["target"]), to_dev(w["draft"]), to_dev(w["draft_tokens"]), to_dev(w["uniforms"]), 1.0)
-    for k in (-1, 6):
+    for k in (-2, 6):
         with pytest.raises(L.SpecError):
             L.verify_sample(*args, early_exit=True, positions_per_launch=k)
 
