@@ -330,6 +330,21 @@ def test_zero_residual_falls_back_to_p(dt, V, B, g):
     assert res["explained"] == 0
 
 
+@pytest.mark.parametrize("dt,V", [("bf16", 128256), ("f32", 3001)])
+def test_draw_with_uniform_just_below_one(dt, V):
+    """The final draw at the top of the uniforms' range: u = 1 - 2^-24, the
+    largest float32 below 1, for every sequence (with and without an earlier
+    rejection).  The threshold u * total then sits just below the total, so
+    the draw lands in the last tokens with mass, or in the fallback to the
+    last positive weight when rounding leaves no crossing; the outputs must
+    match the oracle's under the usual margins."""
+    w = make_workload("b64g7v128k", B=48, V=V, dtype=dt, seed=V + 9)
+    w["uniforms"][:, -1] = np.float32(1.0) - np.float32(2.0 ** -24)
+    w["uniforms"][:24, 0] = np.float32(1.0) - np.float32(2.0 ** -24)    # rejects unless p(x) >= q(x)
+    res = _check_sample(w)
+    assert res["explained"] <= 1, res["details"]
+
+
 @pytest.mark.parametrize("dt,V", [("f32", 50), ("bf16", 9000)])
 def test_invalid_draft_tokens_flag_sequence(dt, V):
     """A drafted token outside [0, V) flags its sequence (accept_len -1, all

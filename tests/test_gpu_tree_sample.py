@@ -295,3 +295,13 @@ def test_without_replacement_committed_tokens_follow_the_target_law():
     acc_i, _, toks_i = _run(dict(w, siblings="iid"))
     counts_i = np.bincount(toks_i[:, 0], minlength=V)
     assert float(np.sum((counts_i - B * p) ** 2 / (B * p))) > 100.0
+
+
+@pytest.mark.parametrize("siblings", ["iid", "without_replacement"])
+def test_final_draw_with_uniform_just_below_one(siblings):
+    # u[0] = 1 - 2^-24 for every sequence: the draw's threshold sits just
+    # below the total of the last residual or of p at a leaf
+    w = make_workload("tree_sample63", B=24, N=15, V=40000, dtype="bf16", tree="wide", draft_noise=1.5,
+                      siblings=siblings, seed=77)
+    w["uniforms"][:, 0] = np.float32(1.0) - np.float32(2.0 ** -24)
+    _check(w)
