@@ -11,8 +11,9 @@ events around every step), the row sweep alone (the roofline line) and a
 plain stream read of the same bytes (the HBM rate reachable on this device),
 the outputs' parity counts against the CPU oracle, the same workload under
 the Zipf recipe (reading B), and the oracle itself on the host's cores as the
-CPU baseline (the sampling workload, and the EAGLE-style LM head plus
-verification with BLAS on every core).
+CPU baseline (the sampling workload; greedy, greedy-tree and stochastic-tree
+verification; the EAGLE-style LM head plus verification with BLAS on every
+core).
 
 Secondary legs (same JSON line, "modes"): greedy verification of the same
 tensors; early-exit sampling; greedy and stochastic tree verification (B=32,
@@ -38,7 +39,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "row_stats_b64g7v128k_counters.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,9 +122,19 @@ def _spans(B, n):
 
 
 def _oracle_slice(span):
+    """The oracle on sequences [b0, b1) of the batch; _BATCH["kind"] names the
+    verification ("sample" when absent)."""
     import oracle
     b0, b1 = span
     f = _BATCH
+    kind = f.get("kind", "sample")
+    if kind == "greedy":
+        return oracle.verify_greedy(f["target"][b0:b1], f["dtype"], f["tokens"][b0:b1])
+    if kind == "tree":
+        return oracle.verify_tree(f["target"][b0:b1], f["dtype"], f["tokens"][b0:b1], f["parent"])
+    if kind == "tree_sample":
+        return oracle.verify_tree_sample(f["target"][b0:b1], f["draft"][b0:b1], f["dtype"], f["tokens"][b0:b1],
+                                         f["parent"], f["uniforms"][b0:b1], f["T"], siblings=f["siblings"])
     return oracle.verify_sample(f["target"][b0:b1], f["draft"][b0:b1], f["dtype"], f["tokens"][b0:b1],
                                 f["uniforms"][b0:b1], f["T"])
 
@@ -633,6 +644,37 @@ def main():
                                             f"processes (float64 NumPy, one thread each), {el:.1f} s",
                                   "gpu_over_cpu": round(value / (passes * B * g / el), 1)}
         if not args.no_modes:
+            # the other verifications, the same way (forked workers over the
+            # sequences, whole passes for about half of args.cpu_seconds)
+            def mode_leg(key, batch, B_, units, unit, what, gpu):
+                _, passes, el = _with_batch(batch, _time_slice, _spans(B_, nw), repeat_until=args.cpu_seconds / 2)
+                cv = passes * units / el
+                result["cpu_baseline"][key] = {
+                    "value": round(cv, 2), "unit": unit, "cores": nw, "kind": "oracle",
+                    "sample": f"{passes} passes over {what}, sequences split over {nw} forked worker processes "
+                              f"(float64 NumPy), {el:.1f} s",
+                    "gpu_over_cpu": round(gpu / cv, 1) if gpu else None}
+
+            md = result.get("modes", {})
+            mode_leg("greedy_b64g7v128k", dict(kind="greedy", target=w["target"], dtype="bf16",
+                                                tokens=w["draft_tokens"]),
+                     B, B * g, "verified positions/s", f"the same {B}-sequence batch (greedy, target rows only)",
+                     md.get("greedy_b64g7v128k", {}).get("positions_per_s"))
+            tw = make_workload("tree63", cache=True)
+            mode_leg("tree_b32n63v128k", dict(kind="tree", target=tw["target"], dtype="bf16",
+                                               tokens=tw["node_tokens"], parent=tw["parent"]),
+                     tw["B"], tw["B"] * (tw["N"] - 1), "verified nodes/s",
+                     f"{tw['B']} greedy trees of {tw['N']} nodes (V={tw['V']} bf16)",
+                     md.get("tree_b32n63v128k", {}).get("nodes_per_s"))
+            sw = make_workload("tree_sample63", cache=True)
+            mode_leg("tree_sample_b32n63v128k", dict(kind="tree_sample", target=sw["target"], draft=sw["draft"],
+                                                      dtype="bf16", tokens=sw["node_tokens"], parent=sw["parent"],
+                                                      uniforms=sw["uniforms"], T=float(sw["temperature"]),
+                                                      siblings="iid"),
+                     sw["B"], sw["B"], "sequences/s",
+                     f"{sw['B']} sampled trees of {sw['N']} nodes (V={sw['V']} bf16, i.i.d. siblings)",
+                     md.get("tree_sample_b32n63v128k", {}).get("sequences_per_s"))
+            del tw, sw
             # the EAGLE-style path: float64 LM head (BLAS on every core) and
             # verification of the resulting logits, 16 sequences per pass
             import oracle
