@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-modes", action="store_true", help="skip the greedy / tree / LM-head legs")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle parity counts")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of each oracle baseline leg")
+    ap.add_argument("--settle", type=float, default=0.2,
+                    help="seconds of each leg's own call before its warm-up steps (GPU clocks leave idle)")
     return ap.parse_args()
 
 
@@ -88,6 +90,25 @@ def time_events(fn, n, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n          # ms per call
+
+
+def settle(fn, seconds):
+    """Run fn(0), fn(1), ... back to back for about `seconds`, then wait for
+    the GPU.  An idle MI355X takes some milliseconds of load to bring its
+    clocks to their working level (about 10 ms here: the first hundred-odd
+    calls of a verification step run 10-15% slower), so every leg first
+    loads the GPU with its own call; the warm-up steps and the timed steps
+    follow.  The queue is drained every 16 calls so that it never runs far
+    ahead of the GPU."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def step_distribution(fn, n, stream):
@@ -227,6 +248,7 @@ def main():
         _, t, dr = reps[i % R]
         L.verify_sample(t, dr, x, u, T, ws=ws, out=out)
 
+    settle(step, args.settle)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -246,6 +268,7 @@ def main():
     def sweep(i):
         L.row_partials(reps[i % R][0], T, 1, out=rs_out)
 
+    settle(sweep, args.settle)
     for i in range(args.warmup):
         sweep(i)
     k1_ms = time_events(sweep, args.steps, stream)
@@ -278,6 +301,7 @@ def main():
                      "avg_launch_us": round(k1_ms * 1e3, 2)},
         "wall_s_timed_region": round(wall, 4),
     }
+    settle(step, args.settle)
     result["step_distribution"] = step_distribution(step, args.steps, stream)
 
     # the HBM read rate reachable here: a plain read of the same 246 MB
@@ -287,6 +311,7 @@ def main():
     def sread(i):
         L.stream_read(reps[i % R][0], sink=sink)
 
+    settle(sread, args.settle)
     for i in range(args.warmup):
         sread(i)
     sr_ms = time_events(sread, args.steps, stream)
@@ -327,6 +352,7 @@ def main():
     def bstep_(i):
         L.verify_sample(reps_b[i % 4][0], reps_b[i % 4][1], xb, ub, T, ws=ws, out=bout)
 
+    settle(bstep_, args.settle)
     for i in range(args.warmup):
         bstep_(i)
     bms = time_events(bstep_, args.steps, stream)
@@ -348,6 +374,7 @@ def main():
         def gstep(i):
             L.verify_greedy(reps[i % R][1], x, ws=gws, out=gout)
 
+        settle(gstep, args.settle)
         for i in range(args.warmup):
             gstep(i)
         gms = time_events(gstep, args.steps, stream)
@@ -383,6 +410,7 @@ def main():
             _, t, dr = reps[i % R]
             L.verify_sample(t, dr, x, u, T, ws=ws, out=eout, early_exit=True, positions_per_launch=K)
 
+        settle(estep, args.settle)
         for i in range(args.warmup):
             estep(i)
             estep(i, 1)
@@ -410,6 +438,7 @@ def main():
             L.verify_sample(lo[i % 4][0], lo[i % 4][1], lx, lu, T, ws=ws, out=eout, early_exit=early,
                             positions_per_launch=K)
 
+        settle(lambda i: lstep(i, False), args.settle)
         for i in range(args.warmup):
             lstep(i, False)
             lstep(i, True)
@@ -440,6 +469,7 @@ def main():
             L.verify_sample(lo4[i % 2][0], lo4[i % 2][1], x4, u4, T, ws=ws4, out=out4, early_exit=early,
                             positions_per_launch=K)
 
+        settle(lambda i: l4(i, False), args.settle)
         for i in range(2):
             l4(i, False)
             l4(i, True)
@@ -466,6 +496,7 @@ def main():
         def tstep(i):
             L.verify_tree(tt if i % 2 == 0 else tt2, tn, tp, ws=tws, out=tout)
 
+        settle(tstep, args.settle)
         for i in range(args.warmup):
             tstep(i)
         tms = time_events(tstep, args.steps, stream)
@@ -491,6 +522,7 @@ def main():
         def sstep(i):
             L.verify_tree_sample(st_, sd_, sn, sp, su, sT, ws=sws, out=sout)
 
+        settle(sstep, args.settle)
         for i in range(args.warmup):
             sstep(i)
         sms = time_events(sstep, args.steps, stream)
@@ -513,6 +545,7 @@ def main():
         def rstep(i):
             L.verify_tree_sample(rt_, rd_, rn, rp, ru, sT, ws=sws, out=sout, siblings="without_replacement")
 
+        settle(rstep, args.settle)
         for i in range(args.warmup):
             rstep(i)
         rms = time_events(rstep, args.steps, stream)
@@ -534,6 +567,7 @@ def main():
         def kstep(i):
             L.kv_compact(kv, kpre, kacc, kpath, new_len=knew)
 
+        settle(kstep, args.settle)
         for i in range(args.warmup):
             kstep(i)
         kms = time_events(kstep, args.steps, stream)
@@ -565,6 +599,7 @@ def main():
         def xstep(i):
             L.tree_expand(xrep[i % 4], xfront, xtable, 1 + xK, 1.0, xk, xK, ws=xws, next_frontier=xnext)
 
+        settle(xstep, args.settle)
         for i in range(args.warmup):
             xstep(i)
         xms = time_events(xstep, args.steps, stream)
@@ -581,6 +616,7 @@ def main():
         def bstep(i):
             L.tree_build(xtable, off, 63, out=bout)
 
+        settle(bstep, args.settle)
         for i in range(args.warmup):
             bstep(i)
         bms = time_events(bstep, args.steps, stream)
@@ -615,9 +651,11 @@ def main():
 
             # the engine clock settles after tens of ms of MFMA work: time the
             # GEMM at its steady state
+            settle(pstep, args.settle)
             for i in range(60):
                 pstep(i)
             pms = time_events(pstep, 20, stream)
+            settle(estep, args.settle)
             for i in range(3):
                 estep(i)
             ems = time_events(estep, 10, stream)

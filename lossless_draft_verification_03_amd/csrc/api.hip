@@ -107,7 +107,9 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
     dt = DT_F32;
   }
   if (mode == SPEC_MODE_TREE_SAMPLE) dt = DT_F32;
-  const RowSweepShape sh = row_sweep_shape((int)V, dt);
+  // greedy and greedy-tree verification sweep with the argmax-only segments
+  const int vpt = (mode == SPEC_MODE_GREEDY || mode == SPEC_MODE_TREE) ? kArgmaxVPT : 0;
+  const RowSweepShape sh = row_sweep_shape((int)V, dt, vpt);
   int seg_elems = 0;
   const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
   size_t o = 0;
@@ -175,10 +177,10 @@ spec_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 // per-row arrays when `merge` is set.
 hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long long rows1, int V,
                      int dt, int want, const TempConst& tc, void* ws, const Layout& L, hipStream_t s,
-                     bool merge = false) {
+                     bool merge = false, int vpt = 0) {
   RowStatsParams p;
   memset(&p, 0, sizeof(p));
-  const RowSweepShape sh = row_sweep_shape(V, dt);
+  const RowSweepShape sh = row_sweep_shape(V, dt, vpt);
   p.src0 = src0;
   p.src1 = src1;
   p.rows0 = rows0;
@@ -187,6 +189,7 @@ hipError_t row_sweep(const void* src0, long long rows0, const void* src1, long l
   p.nseg = sh.nseg;
   p.seg_vecs = sh.seg_vecs;
   p.want = want;
+  p.vpt = vpt;
   p.tc = tc;
   p.part = at<Partial>(ws, L.part);
   p.out_max = at<float>(ws, L.rmax);
@@ -483,11 +486,12 @@ spec_status spec_verify_greedy(const void* target_logits, spec_dtype dt, const i
   if (w != SPEC_OK) return w;
   TempConst tc;
   memset(&tc, 0, sizeof(tc));
-  hipError_t e = row_sweep(target_logits, (long long)B * (gamma + 1), nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
+  hipError_t e = row_sweep(target_logits, (long long)B * (gamma + 1), nullptr, 0, V, (int)dt, 2, tc, ws, L, s,
+                           false, kArgmaxVPT);
   if (e != hipSuccess) return SPEC_EHIP;
   GreedyParams p;
   p.part = at<Partial>(ws, L.part);
-  p.nseg = row_sweep_shape(V, (int)dt).nseg;
+  p.nseg = row_sweep_shape(V, (int)dt, kArgmaxVPT).nseg;
   p.tokens = draft_tokens;
   p.B = B;
   p.g = gamma;
@@ -515,11 +519,12 @@ spec_status spec_verify_tree(const void* target_logits, spec_dtype dt, const int
   if (w != SPEC_OK) return w;
   TempConst tc;
   memset(&tc, 0, sizeof(tc));
-  hipError_t e = row_sweep(target_logits, (long long)B * N, nullptr, 0, V, (int)dt, 2, tc, ws, L, s);
+  hipError_t e = row_sweep(target_logits, (long long)B * N, nullptr, 0, V, (int)dt, 2, tc, ws, L, s, false,
+                           kArgmaxVPT);
   if (e != hipSuccess) return SPEC_EHIP;
   TreeParams p;
   p.part = at<Partial>(ws, L.part);
-  p.nseg = row_sweep_shape(V, (int)dt).nseg;
+  p.nseg = row_sweep_shape(V, (int)dt, kArgmaxVPT).nseg;
   p.node_tokens = node_tokens;
   p.parent = parent;
   p.parent_stride = parent_batch_stride;

@@ -42,7 +42,7 @@ constexpr int kVPT = kSweepVPT;   // 16-byte vectors per lane per segment
 // STEPNP > 0: one early-exit step (see launch_row_step); STEPNP is the lane
 // group the draw kernel merges a row's partials with, so the step's accept
 // test reproduces the draw's decision bit for bit.
-template <int DT, int WANT, int STEPNP = 0>
+template <int DT, int WANT, int STEPNP = 0, int VPT = kVPT>
 __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   __shared__ float sh_m[kBlock / kWave];
   __shared__ double sh_s[kBlock / kWave];
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
       if (x >= 0 && (long long)x < P.V) gx = x;
     }
   }
-  const Partial pp = sweep_segment<DT, WANT>(base, rr, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a, gx,
+  const Partial pp = sweep_segment<DT, WANT, VPT>(base, rr, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a, gx,
                                              P.gather_out != nullptr ? P.gather_out + r : nullptr);
   if (tid == 0) P.part[r * P.nseg + s] = pp;
 }
@@ -157,6 +157,16 @@ hipError_t launch_sweep_t(const RowStatsParams& p, hipStream_t s) {
   const long long grid = (p.rows0 + p.rows1) * (long long)p.nseg;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (p.vpt != 0 && p.vpt != kVPT) {
+    // the argmax-only segments; no other width is built
+    if constexpr (WANT == 2) {
+      if (p.vpt != kArgmaxVPT || p.seg_vecs > kArgmaxVPT * kBlock) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_row_sweep<DT, WANT, 0, kArgmaxVPT>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  if (p.seg_vecs > kVPT * kBlock) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_row_sweep<DT, WANT>), dim3((unsigned)grid), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
@@ -200,10 +210,10 @@ hipError_t launch_merge_t(const RowStatsParams& p, hipStream_t s) {
 
 }  // namespace
 
-RowSweepShape row_sweep_shape(int V, int dt) {
+RowSweepShape row_sweep_shape(int V, int dt, int vpt) {
   const long long epv = dt == DT_BF16 ? 8 : 4;
   const long long whole = (long long)V / epv;           // whole vectors per row, at most
-  const long long cap = (long long)kVPT * kBlock;       // vectors one workgroup reduces
+  const long long cap = (long long)(vpt > 0 ? vpt : kVPT) * kBlock;   // vectors one workgroup reduces
   long long nseg = (whole + cap - 1) / cap;
   if (nseg < 1) nseg = 1;
   long long seg = (whole + nseg - 1) / nseg;

@@ -21,6 +21,7 @@ struct RowStatsParams {
   int nseg;       // workgroup segments per row
   int seg_vecs;   // full 16-byte vectors per segment
   int want;       // bit 0: max/sum, bit 1: argmax
+  int vpt;        // vectors per lane of the segments (0: the default; kArgmaxVPT for want == 2)
   TempConst tc;
   Partial* part;  // [rows][nseg]
   // optional gather: for target row (b, i) with i < gather_g and draft row
@@ -50,7 +51,11 @@ struct RowSweepShape {
   int nseg;
   int seg_vecs;
 };
-RowSweepShape row_sweep_shape(int V, int dt);
+// Segments of vpt * kBlock vectors (vpt = 0: the default of every path that
+// sums; the argmax-only sweeps of greedy verification use kArgmaxVPT: more,
+// smaller segments, which fill the chip better for those shorter passes).
+constexpr int kArgmaxVPT = 6;
+RowSweepShape row_sweep_shape(int V, int dt, int vpt = 0);
 // Sweep then merge (final per-row statistics in out_*).
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);
 // The sweep alone (partials only); its consumers merge partials inline.

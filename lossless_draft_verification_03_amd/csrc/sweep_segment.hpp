@@ -30,18 +30,20 @@ namespace sv {
 #endif
 constexpr int kSweepVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segment
 
+// VPT (vectors per lane) sets the segment's capacity, VPT * kBlock vectors;
+// seg_vecs must not exceed it.
 // tid in [0, kBlock) and wid = tid / kWave index the thread inside its group;
 // sh_m, sh_s, sh_a are the group's LDS slots (kBlock / kWave each).  Every
 // thread of the workgroup must make the call (two workgroup barriers); the
 // returned partial is the same in every lane of the group.  If gdst is not
 // null and 0 <= gx < V, z[rr][gx] is stored to *gdst.
-template <int DT, int WANT>
+template <int DT, int WANT, int VPT = kSweepVPT>
 __device__ __forceinline__ Partial sweep_segment(const char* base, long long rr, long long V, int s, int seg_vecs,
                                                  const TempConst& tc, int tid, int wid, float* sh_m, double* sh_s,
                                                  int* sh_a, long long gx, float* gdst) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
-  constexpr int kVPT = kSweepVPT;
+  constexpr int kVPT = VPT;
   const float NEG_INF = -__builtin_huge_valf();
   const int lane = tid & (kWave - 1);
   (void)ES;
