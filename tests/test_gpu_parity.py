@@ -262,6 +262,50 @@ def test_edge_shapes_sample_greedy(dt, B, g, V):
         assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(out.cpu().numpy(), oout)
 
 
+@pytest.mark.parametrize("dt,V", [("bf16", 128256), ("f32", 50001), ("bf16", 11665)])
+def test_greedy_argmax_ties_across_segments(dt, V):
+    """Greedy and greedy-tree verification keep the lowest index among equal
+    maxima, wherever the copies fall: planted at both sides of multiples of
+    11664 and 16384 logits (segment edges of the argmax-only and the summing
+    sweeps for bf16 rows), at the row's first and last logits, and in rows
+    whose logits are all equal.  A draft token at a higher tied index is
+    rejected and the lowest one emitted."""
+    rng = np.random.default_rng(V)
+    B, g = 6, 5
+    z = rng.normal(0, 1, (B, g + 1, V)).astype(np.float32)
+    edges = [e for k in range(1, 12) for e in (k * 11664 - 1, k * 11664, k * 16384 - 1, k * 16384) if e < V]
+    x = np.zeros((B, g), np.int32)
+    for b in range(B):
+        for i in range(g + 1):
+            kind = (b + i) % 4
+            if kind == 0:
+                idx = rng.choice(edges, size=min(3, len(edges)), replace=False) if edges else np.array([0])
+            elif kind == 1:
+                idx = np.array([0, V - 1])
+            elif kind == 2:
+                z[b, i, :] = 1.5                      # every logit ties
+                idx = np.arange(V)
+            else:
+                idx = np.array([V - 1])
+            z[b, i, idx] = 8.0
+            if i < g:
+                # accept the lowest copy at even b, draft a higher copy at odd b
+                srt = np.sort(idx)
+                x[b, i] = srt[0] if b % 2 == 0 or len(srt) == 1 else srt[-1]
+    arr = f32_to_bf16_bits(z) if dt == "bf16" else z
+    acc, out = L.verify_greedy(to_dev(arr), to_dev(x))
+    oacc, oout = oracle.verify_greedy(arr, dt, x)
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(out.cpu().numpy(), oout)
+    assert oacc[0] == g and oacc[1] == 0              # both outcomes occur
+    # the same rows as chains of a tree (node n + 1 carries draft n)
+    par = np.arange(-1, g, dtype=np.int32)
+    tok = np.concatenate([np.zeros((B, 1), np.int32), x], axis=1)
+    acc, path, toks = L.verify_tree(to_dev(arr), to_dev(tok), to_dev(par))
+    oacc, opath, otoks = oracle.verify_tree(arr, dt, tok, par)
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(path.cpu().numpy(), opath)
+    assert np.array_equal(toks.cpu().numpy(), otoks)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_vocabulary_beyond_64_segments(dt):
     # V = 1100003: more than 64 sweep segments per row (merges loop over
