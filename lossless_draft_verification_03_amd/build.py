@@ -30,9 +30,11 @@ def hipcc():
     return exe
 
 
-def build(verbose=False, jobs=None):
-    """Compile every source to an object in parallel, then link the library."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose=False, jobs=None, lib_path=LIB, objdir=None, extra_flags=(), link_flags=()):
+    """Compile every source to an object in parallel, then link the library
+    (by default the package's own; lib_path, objdir and the extra compile and
+    link flags build a variant elsewhere, e.g. with host-side instrumentation)."""
+    objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     procs = []
@@ -40,7 +42,7 @@ def build(verbose=False, jobs=None):
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -54,13 +56,13 @@ def build(verbose=False, jobs=None):
     if failed:
         msg = "\n".join(f"--- {s}\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib_path + f".tmp{os.getpid()}"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, "-o", tmp, *objs]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
