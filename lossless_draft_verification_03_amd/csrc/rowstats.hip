@@ -13,7 +13,9 @@
 // cache policy.  Elements of a row outside whole aligned vectors (row head /
 // tail when V is not a multiple of the vector width) are loaded one by one
 // by segment 0.  With kVPT = 8 a bf16 row of 128256 logits is eight
-// segments, so consumers merge a row's few partials inline.
+// segments, so consumers merge a row's few partials inline.  Argmax-only
+// sweeps (greedy verification) may ask for kArgmaxVPT = 6 vectors per lane:
+// eleven segments per such row, more and shorter workgroups.
 //
 // Optionally the sweep also picks out z[r][x_r] for a per-row token x_r (the
 // drafted token of that position) while the row is in registers, so the
