@@ -129,8 +129,10 @@ __global__ __launch_bounds__(kBlock) void k_step_alive(RowStatsParams P) {
   if (b >= P.step_B) return;                  // whole waves; no barriers here
   const int i0 = P.step, ip = P.step_prev, g = P.gather_g;
   const long long ab = b * (g + 1);
+  // the previous flag is read beside the positions' inputs, not before
+  // them: the tests run either way and the flag gates only the result
   int al = P.step_alive[ab + ip];
-  if (al) {
+  {
     constexpr int G = kWave / STEPNP;
     const int gq = lane / STEPNP, gl = lane & (STEPNP - 1);
     for (int c0 = ip; c0 < i0; c0 += G) {
@@ -142,8 +144,17 @@ __global__ __launch_bounds__(kBlock) void k_step_alive(RowStatsParams P) {
         float Mt, Md;
         double St, Sd;
         int a;
-        merge_partials<1, STEPNP>(P.part + (ab + ii) * P.nseg, P.nseg, P.tc, gl, &Mt, &St, &a);
-        merge_partials<1, STEPNP>(P.part + (P.rows0 + b * g + ii) * P.nseg, P.nseg, P.tc, gl, &Md, &Sd, &a);
+        const Partial* pt = P.part + (ab + ii) * P.nseg;
+        const Partial* pd = P.part + (P.rows0 + b * g + ii) * P.nseg;
+        if (P.nseg <= STEPNP) {
+          // both rows' partials in flight together
+          const Partial qt = load_partial(pt, P.nseg, gl), qd = load_partial(pd, P.nseg, gl);
+          merge_loaded<1, STEPNP>(qt, gl < P.nseg, P.tc, &Mt, &St, &a);
+          merge_loaded<1, STEPNP>(qd, gl < P.nseg, P.tc, &Md, &Sd, &a);
+        } else {
+          merge_partials<1, STEPNP>(pt, P.nseg, P.tc, gl, &Mt, &St, &a);
+          merge_partials<1, STEPNP>(pd, P.nseg, P.tc, gl, &Md, &Sd, &a);
+        }
         rej = x < 0 || x >= P.V ||
               sample_rejects(P.gather_out[ab + ii], P.gather_out[P.rows0 + b * g + ii], Mt, St, Md, Sd,
                              P.step_unif[ab + ii], P.tc);

@@ -387,9 +387,61 @@ struct Partial {
 // adding their partials in segment order and the group combining them in a
 // fixed order.  Returns M, the sum (WANT & 1) and the lowest index holding
 // M (WANT & 2; 0 for a row of -inf).
+// The same merge when every lane holds at most one partial (nseg <= GROUP):
+// pp is lane gl's partial, loaded by the caller (valid = gl < nseg), so the
+// partials are read once and callers can issue several rows' loads together.
+// Same operations in the same order as merge_partials, so the same bits.
+template <int WANT, int GROUP>
+__device__ __forceinline__ void merge_loaded(const Partial& pp, bool valid, const TempConst& tc, float* M_out,
+                                             double* S_out, int* A_out) {
+  const float NEG_INF = -__builtin_huge_valf();
+  float m = NEG_INF;
+  int a = 0x7fffffff;
+  if (valid) {
+    if (pp.m > m) {
+      m = pp.m;
+      a = pp.arg;
+    } else if (pp.m == m) {
+      a = min(a, pp.arg);
+    }
+  }
+  const float M = group_max<GROUP>(m);
+  double sv = 0.0;
+  if constexpr ((WANT & 1) != 0) {
+    if (M != NEG_INF) {
+      const double Mc = (double)M * tc.c64;
+      if (valid && pp.m != NEG_INF) sv += pp.s * exp2_f64((double)pp.K - Mc);
+    }
+    sv = group_sum<GROUP>(sv);
+  }
+  int aa = (m == M && M != NEG_INF) ? a : 0x7fffffff;
+  if constexpr ((WANT & 2) != 0) aa = group_min<GROUP>(aa);
+  *M_out = M;
+  *S_out = sv;
+  *A_out = aa == 0x7fffffff ? 0 : aa;
+}
+
+__device__ __forceinline__ Partial load_partial(const Partial* part, int nseg, int gl) {
+  Partial pp;
+  if (gl < nseg) {
+    pp = part[gl];
+  } else {
+    pp.m = -__builtin_huge_valf();
+    pp.arg = 0x7fffffff;
+    pp.K = 0.f;
+    pp.pad_ = 0.f;
+    pp.s = 0.0;
+  }
+  return pp;
+}
+
 template <int WANT, int GROUP>
 __device__ __forceinline__ void merge_partials(const Partial* part, int nseg, const TempConst& tc, int gl,
                                                float* M_out, double* S_out, int* A_out) {
+  if (nseg <= GROUP) {                        // uniform: one partial per lane at most, read once
+    merge_loaded<WANT, GROUP>(load_partial(part, nseg, gl), gl < nseg, tc, M_out, S_out, A_out);
+    return;
+  }
   const float NEG_INF = -__builtin_huge_valf();
   float m = NEG_INF;
   int a = 0x7fffffff;
