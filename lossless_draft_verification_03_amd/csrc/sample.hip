@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   // read before j is known; they are ignored when j < 0)
   const DrawInfo di = P.info[b];
   const float u = P.unif[ubase + g];
-  const double m0 = wid == 0 && lane < nsub ? sub[lane] : 0.0;
+  double m0 = wid == 0 && lane < nsub ? sub[lane] : 0.0;
   if (di.j < 0) return;                       // k_draw_mass (b, 0) wrote the -1s
   DrawRow R = draw_row<DT>(P, b, di);
   if (wid == 0) {
@@ -252,8 +252,9 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
     for (int t = 0; t < P.nseg; ++t) segment_masses<DT, ALIGNED>(R, V, t, P.tc, wid, lane, sub);
     __syncthreads();
     if (wid == 0) {
-      double total = 0.0;
-      for (int c0 = 0; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
+      m0 = lane < nsub ? sub[lane] : 0.0;
+      double total = wave_sum(m0);
+      for (int c0 = kWave; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
       if (lane == 0) sh_thr = (double)u * total;
     }
     __syncthreads();
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   if (wid == 0) {
     double base;
     int fb;
-    const int k = locate_segment(sub, nsub, sh_thr, lane, &base, &fb);
+    // the first 64 masses are still in m0
+    const int k = locate_segment(sub, nsub, sh_thr, lane, &base, &fb, m0);
     if (lane == 0) {
       sh_k = k;
       sh_base = base;

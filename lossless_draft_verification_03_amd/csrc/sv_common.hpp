@@ -333,14 +333,16 @@ __device__ __forceinline__ double draw_weight_f64(const DrawRow& R, float zt, fl
 // masses in chunks of 64 (fp64 inclusive scans, fixed order).  Returns the
 // segment index and the mass before it; if rounding leaves no crossing, the
 // last segment with positive mass and fallback = 1.
+// first0 is the caller's copy of the first chunk (lane < nseg ? seg[lane] :
+// 0), already in registers, so that chunk is not read again.
 __device__ __forceinline__ int locate_segment(const double* seg, int nseg, double thr, int lane, double* base,
-                                             int* fallback) {
+                                             int* fallback, double first0) {
   double carry = 0.0;
   int last = 0;
   double lastbase = 0.0;
   for (int c0 = 0; c0 < nseg; c0 += kWave) {
     const int t = c0 + lane;
-    const double m = t < nseg ? seg[t] : 0.0;
+    const double m = c0 == 0 ? first0 : (t < nseg ? seg[t] : 0.0);
     const double incl = carry + wave_incl_scan(m, lane);
     const unsigned long long mc = __ballot(m > 0.0 && incl > thr);
     const unsigned long long mp = __ballot(m > 0.0);
@@ -360,6 +362,11 @@ __device__ __forceinline__ int locate_segment(const double* seg, int nseg, doubl
   *base = lastbase;
   *fallback = 1;
   return last;
+}
+
+__device__ __forceinline__ int locate_segment(const double* seg, int nseg, double thr, int lane, double* base,
+                                             int* fallback) {
+  return locate_segment(seg, nseg, thr, lane, base, fallback, lane < nseg ? seg[lane] : 0.0);
 }
 
 // Sequence-level result of the accept scan, handed to the draw kernels.

@@ -703,14 +703,16 @@ __device__ void draw_final(const TreeSampleParams& P, int b, const TreeWalkState
   double* const sub = P.ws_sub + (long long)b * nsub;
   const float u = P.unif[(long long)b * P.N];
   DrawRow R = node_row<DT>(P, b, st, st.cn);
+  double f0 = 0.0;                            // wave 0: the first 64 masses, kept for the locate step
   for (int attempt = 0;; ++attempt) {
     if (attempt > 0) {
       draw_masses<DT, ALIGNED>(P, b, R, q, TQ, wq, lane);
       __syncthreads();
     }
     if (wid == 0) {
-      double total = 0.0;
-      for (int c0 = 0; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
+      f0 = lane < nsub ? sub[lane] : 0.0;
+      double total = wave_sum(f0);
+      for (int c0 = kWave; c0 < nsub; c0 += kWave) total += wave_sum(c0 + lane < nsub ? sub[c0 + lane] : 0.0);
       if (lane == 0) {
         S.zero = total > 0.0 ? 0 : 1;
         S.thr = (double)u * total;
@@ -724,7 +726,7 @@ __device__ void draw_final(const TreeSampleParams& P, int b, const TreeWalkState
   if (wid == 0) {
     double base;
     int fb;
-    const int k = locate_segment(sub, nsub, S.thr, lane, &base, &fb);
+    const int k = locate_segment(sub, nsub, S.thr, lane, &base, &fb, f0);
     if (lane == 0) {
       S.k = k;
       S.base = base;
