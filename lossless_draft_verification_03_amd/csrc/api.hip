@@ -90,10 +90,11 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
       long long pre = 0;
       for (int t = 0; t < 2; ++t) {
         const long long need =
-            2 * B * tree_presweep_nodes(B, gN, V, t, d) * row_sweep_shape((int)V, t).nseg;
+            2 * B * tree_presweep_nodes(B, gN, V, t, d) * row_sweep_shape((int)V, t, kTreeSampleVPT).nseg;
         if (need > pre) pre = need;
       }
-      rows = 4 * B + (pre + row_sweep_shape((int)V, DT_F32).nseg - 1) / row_sweep_shape((int)V, DT_F32).nseg;
+      rows = 4 * B + (pre + row_sweep_shape((int)V, DT_F32, kTreeSampleVPT).nseg - 1) /
+                         row_sweep_shape((int)V, DT_F32, kTreeSampleVPT).nseg;
       break;
     }
     case SPEC_MODE_ROWSTATS:
@@ -107,8 +108,11 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
     dt = DT_F32;
   }
   if (mode == SPEC_MODE_TREE_SAMPLE) dt = DT_F32;
-  // greedy and greedy-tree verification sweep with the argmax-only segments
-  const int vpt = (mode == SPEC_MODE_GREEDY || mode == SPEC_MODE_TREE) ? kArgmaxVPT : 0;
+  // greedy and greedy-tree verification sweep with the argmax-only segments,
+  // the tree sampler with its own
+  const int vpt = (mode == SPEC_MODE_GREEDY || mode == SPEC_MODE_TREE) ? kArgmaxVPT
+                  : mode == SPEC_MODE_TREE_SAMPLE                        ? kTreeSampleVPT
+                                                                         : 0;
   const RowSweepShape sh = row_sweep_shape((int)V, dt, vpt);
   int seg_elems = 0;
   const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
@@ -563,7 +567,7 @@ spec_status spec_verify_tree_sample(const void* target_logits, const void* draft
   if (!make_layout(SPEC_MODE_TREE_SAMPLE, B, N, V, n_sweep, DT_F32, &L)) return SPEC_EINVAL;
   const spec_status w = check_ws(ws, ws_bytes, L);
   if (w != SPEC_OK) return w;
-  const RowSweepShape sh = row_sweep_shape(V, (int)dt);
+  const RowSweepShape sh = row_sweep_shape(V, (int)dt, kTreeSampleVPT);
   TreeSampleParams p;
   p.tgt = target_logits;
   p.drf = draft_logits;

@@ -12,7 +12,7 @@
 // into the segment, the excess masked afterwards), with the non-temporal
 // cache policy.  Elements of a row outside whole aligned vectors (row head /
 // tail when V is not a multiple of the vector width) are loaded one by one
-// by segment 0.  With kVPT = 8 a bf16 row of 128256 logits is eight
+// by segment 0.  With kVPT = 7 a bf16 row of 128256 logits is nine
 // segments, so consumers merge a row's few partials inline.  Argmax-only
 // sweeps (greedy verification) may ask for kArgmaxVPT = 6 vectors per lane:
 // eleven segments per such row, more and shorter workgroups.

@@ -55,6 +55,11 @@ struct RowSweepShape {
 // sums; the argmax-only sweeps of greedy verification use kArgmaxVPT: more,
 // smaller segments, which fill the chip better for those shorter passes).
 constexpr int kArgmaxVPT = 6;
+// The tree sampler's row statistics (presweep and the walk's entry passes)
+// keep 8-vector segments: then a node's two rows take at most as many
+// workgroups (2 nseg) as a W pass (V / 8192), so the rounds' grids stay at
+// one W pass's width.
+constexpr int kTreeSampleVPT = 8;
 RowSweepShape row_sweep_shape(int V, int dt, int vpt = 0);
 // Sweep then merge (final per-row statistics in out_*).
 hipError_t launch_row_stats(const RowStatsParams& p, int dt, hipStream_t s);

@@ -26,7 +26,7 @@
 namespace sv {
 
 #ifndef SV_SWEEP_VPT
-#define SV_SWEEP_VPT 8
+#define SV_SWEEP_VPT 7
 #endif
 constexpr int kSweepVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segment
 

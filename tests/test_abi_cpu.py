@@ -119,8 +119,8 @@ def test_other_entry_points_reject_invalid_arguments():
     # probe: q requested without draft logits
     assert lib.spec_probe_probs(FAKE, None, 1, 2, 10, 1.0, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     # row partials: want range, buffer size, alignment
-    nseg = lib.spec_row_segments(128256, 1)
-    assert nseg == 8 and lib.spec_row_segments(0, 1) == 0 and lib.spec_row_segments(10, 7) == 0
+    nseg = lib.spec_row_segments(128256, 1)        # 16032 vectors in segments of at most 7 x 256
+    assert nseg == 9 and lib.spec_row_segments(0, 1) == 0 and lib.spec_row_segments(10, 7) == 0
     assert lib.spec_row_partials(FAKE, 1, 4, 128256, 1.0, 1, FAKE, 4 * nseg * 24 - 1, None) == 1
     assert lib.spec_row_partials(FAKE, 1, 4, 128256, 1.0, 0, FAKE, 1 << 30, None) == 1
     assert lib.spec_row_partials(FAKE, 1, 4, 128256, 0.0, 1, FAKE, 1 << 30, None) == 1

@@ -3,8 +3,9 @@
 [R] "The Complete EAGLE-3 Inference Process", 4. Strict Acceptance (min(1,
 p/q) acceptance with residual correction, on a tree).  Outputs must equal the
 oracle's except where the first differing decision sits at an oracle margin
-(parity.classify_tree_sample); a chain tree must reproduce the chain sampler,
-and the committed tokens must follow the target law (chi-square, no oracle).
+(parity.classify_tree_sample); a chain tree must reproduce the chain sampler
+(up to the same margins), and the committed tokens must follow the target law
+(chi-square, no oracle).
 """
 import numpy as np
 import pytest
@@ -123,16 +124,19 @@ def test_chain_tree_equals_chain_sampler():
         a2, o2 = L.verify_sample(to_dev(wl["target"]), to_dev(wl["draft"]), to_dev(wl["draft_tokens"]),
                                  to_dev(wl["uniforms"]), T)
         a2, o2 = a2.cpu().numpy(), o2.cpu().numpy()
-        # the accept tests are the same fp64 computation on the same statistics
-        assert np.array_equal(acc, a2)
         for b in range(B):
             assert list(path[b, :acc[b]]) == list(range(1, acc[b] + 1))
-        # final tokens: equal, except at a draw margin of the oracle
+        # both equal the oracle's outputs, except at an oracle margin below
+        # 1e-6; the two samplers sum their row statistics over different
+        # segments, so they may differ from each other only there
         oacc, oout, infos = oracle.verify_sample(wl["target"], wl["draft"], dt, wl["draft_tokens"],
                                                  wl["uniforms"], T)
         res = classify_sample(acc, toks[:, :g + 1], oacc, oout, infos)
         assert not res["unexplained"] and res["explained"] <= 1, res
-        assert np.sum(toks != o2) <= 1
+        res2 = classify_sample(a2, o2, oacc, oout, infos)
+        assert not res2["unexplained"] and res2["explained"] <= 1, res2
+        assert np.sum(acc != a2) <= res["explained"] + res2["explained"]
+        assert np.sum(toks != o2) <= 2
 
 
 def test_draft_equal_to_target_takes_first_children():
