@@ -41,8 +41,10 @@
  *  - Workspace: `ws` is caller-owned device memory of at least
  *    spec_workspace_bytes(...) bytes, 256-byte aligned, holding per-row
  *    partial statistics between the kernels of one call.  It needs no
- *    initialisation: a call writes every byte it reads.  Calls that overlap
- *    in time must use distinct workspaces.
+ *    initialisation: no output depends on a byte the call did not write
+ *    (the early-exit call may read, and then discard, a skipped sequence's
+ *    stale partials).  Calls that overlap in time must use distinct
+ *    workspaces.
  *  - Errors: argument errors are reported synchronously, before anything is
  *    launched, as a non-zero spec_status.  A failed launch reports
  *    SPEC_EHIP.  Data-dependent conditions that can only be seen on the
@@ -217,7 +219,7 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
  * Sizes whose workspace (spec_workspace_bytes(SPEC_MODE_SAMPLE, B, gamma, V,
  * 0)) exceeds SPEC_NOALLOC_SCRATCH_BYTES are rejected with SPEC_EWORKSPACE
  * before anything is launched (B = 64, gamma = 7, V = 128256 needs about
- * 0.42 MB; the limit holds about 2500 such sequences).  Every call on one GPU
+ * 0.47 MB; the limit holds about 2300 such sequences).  Every call on one GPU
  * shares that GPU's array and leaves its contents behind; the array needs no
  * clearing (each call writes every byte it reads), but calls that overlap in
  * time on the same GPU (several streams, several host threads) race on it
