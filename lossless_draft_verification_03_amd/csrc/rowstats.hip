@@ -83,17 +83,15 @@ __global__ __launch_bounds__(kBlock) void k_row_sweep(RowStatsParams P) {
   const bool second = r >= P.rows0;
   const char* base = static_cast<const char*>(second ? P.src1 : P.src0);
   const long long rr = second ? r - P.rows0 : r;
-  // the drafted token of this row, if the caller asked for the gather
-  long long gx = -1;
+  // where the drafted token of this row is, if the caller asked for the
+  // gather (read by sweep_segment once its loads are in flight)
+  const int* xtok = nullptr;
   if (P.gather_tokens != nullptr) {
     const long long g1 = second ? P.gather_g : P.gather_g + 1;
     const long long b = rr / g1, i = rr - b * g1;
-    if (i < P.gather_g) {
-      const int x = P.gather_tokens[b * P.gather_g + i];
-      if (x >= 0 && (long long)x < P.V) gx = x;
-    }
+    if (i < P.gather_g) xtok = P.gather_tokens + b * P.gather_g + i;
   }
-  const Partial pp = sweep_segment<DT, WANT, VPT>(base, rr, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a, gx,
+  const Partial pp = sweep_segment<DT, WANT, VPT>(base, rr, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a, xtok,
                                              P.gather_out != nullptr ? P.gather_out + r : nullptr);
   if (tid == 0) P.part[r * P.nseg + s] = pp;
 }

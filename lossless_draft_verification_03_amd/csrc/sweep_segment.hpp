@@ -35,12 +35,13 @@ constexpr int kSweepVPT = SV_SWEEP_VPT;   // 16-byte vectors per lane per segmen
 // tid in [0, kBlock) and wid = tid / kWave index the thread inside its group;
 // sh_m, sh_s, sh_a are the group's LDS slots (kBlock / kWave each).  Every
 // thread of the workgroup must make the call (two workgroup barriers); the
-// returned partial is the same in every lane of the group.  If gdst is not
-// null and 0 <= gx < V, z[rr][gx] is stored to *gdst.
+// returned partial is the same in every lane of the group.  If xtok is not
+// null and x = *xtok lies in [0, V), z[rr][x] is stored to *gdst; *xtok is
+// read only after the segment's loads are issued, so they do not wait for it.
 template <int DT, int WANT, int VPT = kSweepVPT>
 __device__ __forceinline__ Partial sweep_segment(const char* base, long long rr, long long V, int s, int seg_vecs,
                                                  const TempConst& tc, int tid, int wid, float* sh_m, double* sh_s,
-                                                 int* sh_a, long long gx, float* gdst) {
+                                                 int* sh_a, const int* xtok, float* gdst) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int kVPT = VPT;
@@ -62,6 +63,11 @@ __device__ __forceinline__ Partial sweep_segment(const char* base, long long rr,
       const int q = min(k * kBlock + tid, nv - 1);
       raw[k] = load16(rsrc, (uint32_t)q * 16u);
     }
+  }
+  long long gx = -1;
+  if (xtok != nullptr) {
+    const int x = *xtok;
+    if (x >= 0 && (long long)x < V) gx = x;
   }
   const int neg_pat = DT == DT_BF16 ? (int)0xff80ff80u : (int)0xff800000u;
 #pragma unroll

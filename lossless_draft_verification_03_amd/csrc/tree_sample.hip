@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_presweep(TreeSampleParams P) {
   const long long b = rl / P.n_pre, n = rl - b * P.n_pre;
   const char* base = static_cast<const char*>(drow ? P.drf : P.tgt);
   const Partial pp = sweep_segment<DT, 1, kTreeSampleVPT>(base, b * P.N + n, P.V, s, P.seg_vecs, P.tc, tid, wid, sh_m, sh_s, sh_a,
-                                          -1, nullptr);
+                                          nullptr, nullptr);
   if (tid == 0) P.pre_part[row * P.nseg + s] = pp;
 }
 
@@ -529,7 +529,7 @@ __device__ void walk(const TreeSampleParams& P, int b, TreeWalkState& st, bool f
             const bool drow = u >= P.nseg && u < units;
             const int s = u < units ? (drow ? u - P.nseg : u) : P.nseg;
             const Partial pp = sweep_segment<DT, 1, kTreeSampleVPT>(drow ? drf : tgt, row0 + st.n, V, s, P.seg_vecs, P.tc, tq, wq,
-                                                    L.qm[q], L.qs[q], L.qa[q], -1, nullptr);
+                                                    L.qm[q], L.qs[q], L.qa[q], nullptr, nullptr);
             if (tq == 0 && u < units) part_in[u] = pp;
           }
           __syncthreads();
@@ -896,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void k_ts_round(TreeSampleParams P, int r) 
       const bool drow = u >= P.nseg;
       const Partial pp = sweep_segment<DT, 1, kTreeSampleVPT>(static_cast<const char*>(drow ? P.drf : P.tgt),
                                               (long long)b * P.N + st.n, P.V, (int)(drow ? u - P.nseg : u),
-                                              P.seg_vecs, P.tc, tid, wid, qm[0], qs[0], qa[0], -1, nullptr);
+                                              P.seg_vecs, P.tc, tid, wid, qm[0], qs[0], qa[0], nullptr, nullptr);
       if (tid == 0) part_out[u] = pp;
     }
   } else if (st.phase == kNeedW) {
