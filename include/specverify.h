@@ -114,7 +114,7 @@ typedef enum {
  * (0 when an argument is out of range).  d is the feature width for
  * SPEC_MODE_LMHEAD and the call's n_sweep for SPEC_MODE_TREE_SAMPLE; other
  * modes ignore it.  The LMHEAD workspace holds the float32 logits of all
- * B(2*gamma+1) rows. */
+ * B(2*gamma+1) rows and 16 bytes of row statistics per 128 logits. */
 size_t spec_workspace_bytes(int mode, int B, int gamma_or_N, int V, int d);
 
 /* Zero-fill a workspace (a device fill kernel; graph-capture safe).  Not
@@ -427,7 +427,11 @@ size_t lmhead_project_workspace_bytes(int M, int d);
  * The feature rows (target rows, then draft rows) are first staged in the
  * workspace in the blocked layout of lmhead_project_staged, so one GEMM
  * streams W once for both; the logits stay in the workspace (float32, no
- * host round trip) for the verification kernels.
+ * host round trip) for the verification kernels.  The GEMM's epilogue also
+ * leaves each row's softmax statistics (max and sum of exp((z - max)/T)) as
+ * one partial per 128 columns, computed from the accumulators before they are
+ * stored; a merge of those gives the accept test its p and q normalisers, so
+ * the logits are read back only for the rows the final draw needs.
  * Workspace: spec_workspace_bytes(SPEC_MODE_LMHEAD, B, gamma, V, d).  After
  * the call the logits are left in the last ceil256(B(2 gamma+1) V 4) bytes
  * of the workspace: B(gamma+1) target rows, then B gamma draft rows.

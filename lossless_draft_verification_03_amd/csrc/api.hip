@@ -29,7 +29,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // is fully written before it is read within one call, so a workspace needs
 // no initialisation and can be shared by calls of any layout (one at a time).
 struct Layout {
-  size_t info, part, rmax, rsum, rarg, gath, segsum, hcat, logits, total;
+  size_t info, part, rmax, rsum, rarg, gath, segsum, gpart, hcat, logits, total;
   size_t tstate, tglog, twpart;        // tree sampler: walk states, token logits, W sums
   long long rows;
   int nseg, nseg2;
@@ -132,6 +132,9 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
     L->tglog = o;  o = up(o + (size_t)B * gN * 2 * 4);
     L->twpart = o; o = up(o + (size_t)2 * B * tree_segments(V) * 3 * 8);
   }
+  // the LM head's per-row partials (its GEMM epilogue's row statistics)
+  L->gpart = o;
+  if (mode == SPEC_MODE_LMHEAD) o = up(o + (size_t)rows * lmhead_stat_parts(V) * sizeof(LmPartial));
   L->hcat = o;
   if (mode == SPEC_MODE_LMHEAD) o = up(o + lmhead_staged_bytes(rows, d));
   L->logits = o;
@@ -226,9 +229,10 @@ RowStatsParams sample_sweep_params(const void* tgt, const void* drf, const int32
 }
 
 // Accept scan and final draw on the partials the sweep left in the workspace.
+// nseg_rows: partials per row (-1: the row sweep's segments).
 spec_status draw_on(const void* tgt, const void* drf, int dt, const int32_t* tokens, const float* unif, int B,
                     int g, int V, const TempConst& tc, int32_t* accept_len, int32_t* out_tokens, void* ws,
-                    const Layout& L, hipStream_t s) {
+                    const Layout& L, hipStream_t s, int nseg_rows = -1) {
   SampleParams p;
   memset(&p, 0, sizeof(p));
   p.tgt = tgt;
@@ -236,7 +240,7 @@ spec_status draw_on(const void* tgt, const void* drf, int dt, const int32_t* tok
   p.tokens = tokens;
   p.unif = unif;
   p.part = at<Partial>(ws, L.part);
-  p.nseg_rows = row_sweep_shape(V, dt).nseg;
+  p.nseg_rows = nseg_rows > 0 ? nseg_rows : row_sweep_shape(V, dt).nseg;
   p.gathered = at<float>(ws, L.gath);
   p.B = B;
   p.g = g;
@@ -611,6 +615,9 @@ spec_status lmhead_project(const uint16_t* feat, int M, int d, const uint16_t* W
   p.N = V;
   p.C = out_logits;
   p.a_staged = 0;
+  p.part = nullptr;
+  p.pstride = 0;
+  memset(&p.tc, 0, sizeof(p.tc));
   return hip_status(launch_lmhead(p, s));
 }
 
@@ -643,6 +650,9 @@ spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint
   p.N = V;
   p.C = out_logits;
   p.a_staged = 1;
+  p.part = nullptr;
+  p.pstride = 0;
+  memset(&p.tc, 0, sizeof(p.tc));
   return hip_status(launch_lmhead(p, s));
 }
 
@@ -651,7 +661,10 @@ spec_status lmhead_project_staged(const uint16_t* feat, int M, int d, const uint
 namespace {
 
 // lmhead_verify for either weight layout: stage the feature rows, one GEMM
-// into the workspace's float32 logits, then the sampling path on them.
+// into the workspace's float32 logits whose epilogue also leaves per-row
+// partials of the row statistics, a merge of those partials (with the gather
+// of the drafted tokens' logits), then the accept scan and the draw on them:
+// the logits are read again only for the rows the draw needs.
 spec_status lmhead_verify_layout(const uint16_t* target_feat, const uint16_t* draft_feat, const uint16_t* W,
                                  int w_vd, const int32_t* draft_tokens, const float* uniforms, int B, int gamma,
                                  int d, int V, float temperature, int32_t* accept_len, int32_t* out_tokens,
@@ -692,10 +705,26 @@ spec_status lmhead_verify_layout(const uint16_t* target_feat, const uint16_t* dr
   p.K = d;
   p.N = V;
   p.C = Z;
+  p.part = at<LmPartial>(ws, L.gpart);
+  p.pstride = lmhead_stat_parts(V);
+  p.tc = tc;
   if (launch_lmhead(p, s) != hipSuccess) return SPEC_EHIP;
+  LmHeadMergeParams mp;
+  mp.part = p.part;
+  mp.nparts = p.pstride;
+  mp.C = Z;
+  mp.M = p.M;
+  mp.N = V;
+  mp.tokens = draft_tokens;
+  mp.B = B;
+  mp.g = gamma;
+  mp.tc = tc;
+  mp.out = at<Partial>(ws, L.part);
+  mp.gathered = at<float>(ws, L.gath);
+  if (launch_lmhead_merge(mp, s) != hipSuccess) return SPEC_EHIP;
   const float* Zd = Z + (size_t)B * (gamma + 1) * (size_t)V;
-  return sample_on(Z, Zd, DT_F32, draft_tokens, uniforms, B, gamma, V, tc, accept_len, out_tokens, ws,
-                   L, s);
+  return draw_on(Z, Zd, DT_F32, draft_tokens, uniforms, B, gamma, V, tc, accept_len, out_tokens, ws, L, s,
+                 1);
 }
 
 }  // namespace

@@ -52,6 +52,8 @@
 // W tile through that XCD's L2.
 #include "sv_kernels.hpp"
 
+#include <limits.h>
+
 namespace sv {
 
 namespace {
@@ -120,11 +122,59 @@ constexpr int kWDvElem = 0;  // W[K][N], N % 8 != 0: element loads through regis
 constexpr int kWDvDma = 1;   // W[K][N]: LDS-DMA, transposing LDS reads
 constexpr int kWVd = 2;      // W[N][K]: LDS-DMA, plain LDS reads (like A)
 
+// Row statistics of one wave tile's 128 columns, in the row sweep's partial
+// form: m = the max, K = fl(m c_hi), s = sum 2^(fl(z c_lo + fl(z c_hi - K)))
+// with four fp32 accumulators per lane (sixteen terms each) and fp64 from the
+// lane up.  A row's 128 columns sit in lanes l and l + 32 (the output layout
+// below).  FULL: all 128 columns lie inside V; else the first nv do.
+template <int MI, bool FULL>
+__device__ __forceinline__ void lmhead_row_stats(const LmHeadParams& P, const f32x16 (&acc)[MI][4], int m0,
+                                                 long long n0, long long c0, int wm, int wn, int lane, int nv) {
+  const float NEG_INF = -__builtin_huge_valf();
+  const float c_hi = P.tc.c_hi, c_lo = P.tc.c_lo;
+  const int h = 4 * (lane >> 5);
+  const int pidx = (int)(n0 / BN) * 2 + wn;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    float m = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (FULL || 32 * j + 8 * (r >> 2) + (r & 3) + h < nv) m = fmaxf(m, acc[i][j][r]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float K = 0.f;
+    double S = 0.0;
+    if (m != NEG_INF) {   // the same in both lanes of a row
+      K = m * c_hi;
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (FULL || 32 * j + 8 * (r >> 2) + (r & 3) + h < nv) {
+            const float z = acc[i][j][r];
+            a[r & 3] += __builtin_amdgcn_exp2f(fmaf(z, c_lo, fmaf(z, c_hi, -K)));
+          }
+      const double sl = ((double)a[0] + (double)a[1]) + ((double)a[2] + (double)a[3]);
+      S = sl + __shfl_xor(sl, 32);   // the same sum in both lanes of the row
+    }
+    const int row = m0 + wm * 32 * MI + i * 32 + (lane & 31);
+    if (lane < 32 && row < P.M) {
+      LmPartial pp;
+      pp.m = m;
+      pp.K = K;
+      pp.s = S;
+      P.part[(long long)row * P.pstride + pidx] = pp;
+    }
+  }
+}
+
 // One workgroup tile: rows m0 .. m0 + 64 MI - 1 of C (MI = 4: 256 rows; MI =
 // 3: 192 rows, the last M tile when at most 192 rows remain, so that M = 704
 // issues the MFMAs of 704 rows rather than 768), columns n0 .. n0 + 255.
 // The four waves form a 2 x 2 grid of (32 MI) x 128 wave tiles.
-template <int WL, int MI>
+template <int WL, int MI, bool STATS>
 __device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long long n0, uint16_t* const* SA,
                                             uint16_t* const* SB, int lane, int wid) {
   constexpr int TM = 64 * MI;                  // rows of the tile
@@ -384,9 +434,22 @@ __device__ __forceinline__ void lmhead_tile(const LmHeadParams& P, int m0, long 
         }
     }
   }
+
+  // Row statistics of the wave's 128 columns, in the row sweep's partial
+  // form: m = the max, K = fl(m c_hi), s = sum 2^(fl(z c_lo + fl(z c_hi - K)))
+  // with four fp32 accumulators per lane (sixteen terms each) and fp64 from
+  // the lane up.  A row's 128 columns sit in lanes l and l + 32.
+  if constexpr (STATS) {
+    // lane l's column offsets inside the wave tile are 32 j + 8 q + t + h,
+    // h = 4 (l / 32); nv of the 128 columns lie inside V (wave-uniform)
+    const long long rem = N - c0;
+    const int nv = rem >= 128 ? 128 : (rem > 0 ? (int)rem : 0);
+    if (nv == 128) lmhead_row_stats<MI, true>(P, acc, m0, n0, c0, wm, wn, lane, nv);
+    else lmhead_row_stats<MI, false>(P, acc, m0, n0, c0, wm, wn, lane, nv);
+  }
 }
 
-template <int WL>
+template <int WL, bool STATS>
 __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int ntiles) {
   // one LDS object per ring slot: the A stage, then the W stage
   __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * BM * BK], s1[2 * BM * BK], s2[2 * BM * BK],
@@ -404,8 +467,90 @@ __global__ __launch_bounds__(256) void k_lmhead(LmHeadParams P, int mtiles, int 
   if (nt >= ntiles) return;
   const int m0 = mt * BM;
   const long long n0 = (long long)nt * BN;
-  if (P.M - m0 <= 192) lmhead_tile<WL, 3>(P, m0, n0, SA, SB, lane, wid);   // uniform
-  else lmhead_tile<WL, 4>(P, m0, n0, SA, SB, lane, wid);
+  if (P.M - m0 <= 192) lmhead_tile<WL, 3, STATS>(P, m0, n0, SA, SB, lane, wid);   // uniform
+  else lmhead_tile<WL, 4, STATS>(P, m0, n0, SA, SB, lane, wid);
+}
+
+// One workgroup per row: the row's GEMM partials merged in fp64, as the
+// sampling kernels merge row-sweep partials (M = the max of the partial
+// maxima, S = sum s 2^(K - M c)), stored as one partial with K = fl(M c_hi)
+// and s = S 2^(M c - K).  Each thread holds up to kMergeRun partials per
+// pass, all loaded before use; a second pass reads them again (cache-hot) for
+// the sum.  Thread 0 first gathers the drafted token's logit of the row.
+constexpr int kMergeRun = 4;
+
+__global__ __launch_bounds__(256) void k_lmhead_merge(LmHeadMergeParams P) {
+  __shared__ float sh_m[4];
+  __shared__ double sh_s[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const long long r = blockIdx.x;
+  const float NEG_INF = -__builtin_huge_valf();
+  if (tid == 0 && P.tokens != nullptr) {
+    const long long rows_t = (long long)P.B * (P.g + 1);
+    int x = -1;
+    if (r < rows_t) {
+      const int b = (int)(r / (P.g + 1)), i = (int)(r % (P.g + 1));
+      if (i < P.g) x = P.tokens[(long long)b * P.g + i];
+    } else {
+      x = P.tokens[r - rows_t];               // draft rows follow the tokens' [B, g] order
+    }
+    if (x >= 0 && (long long)x < P.N) P.gathered[r] = P.C[r * P.N + x];
+  }
+  const LmPartial* pr = P.part + r * P.nparts;
+  const int n = P.nparts;
+  float m = NEG_INF;
+  for (int base = 0; base < n; base += kMergeRun * 256) {
+    float pm[kMergeRun];
+#pragma unroll
+    for (int k = 0; k < kMergeRun; ++k) {
+      const int t = base + k * 256 + tid;
+      pm[k] = t < n ? pr[t].m : NEG_INF;
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeRun; ++k) m = fmaxf(m, pm[k]);
+  }
+  m = wave_max(m);
+  if (lane == 0) sh_m[wid] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
+  double sv = 0.0;
+  if (M != NEG_INF) {
+    const double Mc = (double)M * P.tc.c64;
+    for (int base = 0; base < n; base += kMergeRun * 256) {
+      LmPartial pp[kMergeRun];
+#pragma unroll
+      for (int k = 0; k < kMergeRun; ++k) {
+        const int t = base + k * 256 + tid;
+        if (t < n) {
+          pp[k] = pr[t];
+        } else {
+          pp[k].m = NEG_INF;
+          pp[k].K = 0.f;
+          pp[k].s = 0.0;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeRun; ++k)
+        if (pp[k].m != NEG_INF) sv += pp[k].s * exp2_f64((double)pp[k].K - Mc);
+    }
+  }
+  sv = wave_sum(sv);
+  if (lane == 0) sh_s[wid] = sv;
+  __syncthreads();
+  if (tid == 0) {
+    const double S = (sh_s[0] + sh_s[1]) + (sh_s[2] + sh_s[3]);
+    Partial o;
+    o.m = M;
+    o.arg = INT_MAX;
+    o.pad_ = 0.f;
+    o.K = 0.f;
+    o.s = 0.0;
+    if (M != NEG_INF) {
+      o.K = M * P.tc.c_hi;
+      o.s = S * exp2_f64((double)M * P.tc.c64 - (double)o.K);
+    }
+    P.out[r] = o;
+  }
 }
 
 // One 16-byte chunk per thread: chunk q of the staged buffer is chunk q % 4
@@ -452,13 +597,29 @@ hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s) {
   // 32-bit buffer offsets: one A tile, one W tile, one K step of W[K][N]
   if (grid > 0x7fffffffLL || (long long)BM * p.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
   if (!p.w_vd && (long long)BK * p.N * 2 >= (1LL << 32)) return hipErrorInvalidValue;
+  if (p.part != nullptr && p.pstride < lmhead_stat_parts(p.N)) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), b(256);
-  if (p.w_vd)
-    hipLaunchKernelGGL(k_lmhead<kWVd>, g, b, 0, s, p, (int)mt, (int)nt);
-  else if (p.N % 8 == 0)  // rows of W[K][N] start 16-byte aligned
-    hipLaunchKernelGGL(k_lmhead<kWDvDma>, g, b, 0, s, p, (int)mt, (int)nt);
-  else
-    hipLaunchKernelGGL(k_lmhead<kWDvElem>, g, b, 0, s, p, (int)mt, (int)nt);
+  if (p.part != nullptr) {
+    if (p.w_vd)
+      hipLaunchKernelGGL((k_lmhead<kWVd, true>), g, b, 0, s, p, (int)mt, (int)nt);
+    else if (p.N % 8 == 0)
+      hipLaunchKernelGGL((k_lmhead<kWDvDma, true>), g, b, 0, s, p, (int)mt, (int)nt);
+    else
+      hipLaunchKernelGGL((k_lmhead<kWDvElem, true>), g, b, 0, s, p, (int)mt, (int)nt);
+  } else if (p.w_vd) {
+    hipLaunchKernelGGL((k_lmhead<kWVd, false>), g, b, 0, s, p, (int)mt, (int)nt);
+  } else if (p.N % 8 == 0) {  // rows of W[K][N] start 16-byte aligned
+    hipLaunchKernelGGL((k_lmhead<kWDvDma, false>), g, b, 0, s, p, (int)mt, (int)nt);
+  } else {
+    hipLaunchKernelGGL((k_lmhead<kWDvElem, false>), g, b, 0, s, p, (int)mt, (int)nt);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_merge(const LmHeadMergeParams& p, hipStream_t s) {
+  if (p.M < 1 || p.nparts < 1 || p.part == nullptr || p.out == nullptr) return hipErrorInvalidValue;
+  if (p.tokens != nullptr && (p.C == nullptr || p.gathered == nullptr || p.g < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)p.M), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -141,6 +141,14 @@ long long stream_read_workgroups(long long bytes);
 hipError_t launch_stream_read(const void* src, long long bytes, uint32_t* sink, hipStream_t s);
 
 // ---------------------------------------------------------- LM head
+// A row partial of the LM head's epilogue: m the max of its columns, K =
+// fl(m c_hi), s the sum of 2^(z c - K) over them (m = -inf: no columns).
+struct LmPartial {
+  float m;
+  float K;
+  double s;
+};
+
 struct LmHeadParams {
   const uint16_t* A;      // [M, K] bf16 rows, 16-byte aligned (a_staged = 0), or the staged layout
   int M;
@@ -149,8 +157,36 @@ struct LmHeadParams {
   int K, N;
   float* C;               // [M, N] fp32
   int a_staged;
+  // optional row statistics of the logits as they leave the accumulators:
+  // part[row][c] is the partial (max, K offset, sum of 2^(z c - K)) of
+  // columns 128 c .. 128 c + 127 of the row, the row sweep's segment
+  // statistics without the argmax; null: logits only
+  LmPartial* part;
+  int pstride;            // partials per row, lmhead_stat_parts(N)
+  TempConst tc;
 };
 hipError_t launch_lmhead(const LmHeadParams& p, hipStream_t s);
+// Partials per row of the GEMM's row statistics (one per 128 columns).
+inline int lmhead_stat_parts(long long N) { return (int)(2 * ((N + 255) / 256)); }
+
+// Merge of the GEMM's per-row partials into one partial per row (the form
+// the sampling kernels merge, with nseg_rows = 1), plus the gather of the
+// drafted token's logit for the accept test: row r < B(g+1) is target row
+// (b, i) = (r / (g+1), r % (g+1)) (token tokens[b][i] when i < g), the rows
+// after it draft rows (b, i) in order (token tokens[b][i]).
+struct LmHeadMergeParams {
+  const LmPartial* part;  // [M][nparts]
+  int nparts;
+  const float* C;         // [M, N] logits
+  int M;
+  long long N;
+  const int* tokens;      // [B, g]
+  int B, g;
+  TempConst tc;
+  Partial* out;           // [M]
+  float* gathered;        // [M]
+};
+hipError_t launch_lmhead_merge(const LmHeadMergeParams& p, hipStream_t s);
 
 // Staged feature rows: for every 256-row M tile mt and K step ks (32
 // features) one contiguous 16 KB block, 256 rows x 64 bytes, at element

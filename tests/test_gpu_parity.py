@@ -557,6 +557,51 @@ def test_lmhead_project_small_shapes_exact_on_integers(layout):
         assert np.array_equal(Zs, Z), (M, d, V)
 
 
+@pytest.mark.parametrize("layout", ["dv", "vd"])
+def test_lmhead_verify_ragged_shapes_vs_oracle(layout):
+    """lmhead_verify takes its row statistics from the GEMM's epilogue (one
+    partial per 128 columns, merged per row) instead of a sweep over the
+    logits.  Shapes whose last column tile is partly or wholly past V (V =
+    1000, 1100, 997, the last with V % 8 != 0 for the [d, V] element path),
+    ragged M tiles, and logits made large in the ragged last tile so a lost
+    or double-counted partial would move many accept ratios and residuals:
+    the oracle run on the GPU's own float32 logits must reproduce the outputs
+    under the standard rules.  One sequence has an out-of-range drafted
+    token and must come back flagged (accept_len -1), like the oracle's."""
+    rng = np.random.default_rng(11)
+    tally = dict(explained=0, positions=0)
+    lay = L.W_DV if layout == "dv" else L.W_VD
+    for (B, g, d, V, T) in ((64, 3, 128, 1100, 1.0), (37, 3, 192, 1000, 0.8), (20, 4, 64, 997, 1.3)):
+        rows_t = B * (g + 1)
+        Ht = rng.normal(0.0, 1.0, (rows_t, d)).astype(np.float32)
+        Hd = (Ht.reshape(B, g + 1, d)[:, :g].reshape(B * g, d)
+              + rng.normal(0.0, 0.4, (B * g, d))).astype(np.float32)
+        Wf = rng.normal(0.0, 0.08, (d, V)).astype(np.float32)
+        Wf[:, 1024 if V > 1024 else 896:] *= 3.0
+        ht, hd, Wb = f32_to_bf16_bits(Ht), f32_to_bf16_bits(Hd), f32_to_bf16_bits(Wf)
+        # draft tokens drawn from q of the float64 draft logits
+        zd64 = oracle.lmhead_logits(hd, Wb).reshape(B, g, V) / T
+        q = np.exp(zd64 - zd64.max(-1, keepdims=True))
+        q /= q.sum(-1, keepdims=True)
+        x = np.array([[rng.choice(V, p=q[b, i]) for i in range(g)] for b in range(B)], np.int32)
+        x[1, 0] = V                                      # invalid: the sequence is flagged
+        u = rng.random((B, g + 1), dtype=np.float32)
+        Wl = Wb if layout == "dv" else np.ascontiguousarray(Wb.T)
+        ws = L.new_workspace(L.MODE_LMHEAD, B, g, V, d)
+        ws.fill_(0xA5)
+        acc, out = L.lmhead_verify(to_dev(ht), to_dev(hd), to_dev(Wl), to_dev(x), to_dev(u), T, ws=ws,
+                                   layout=lay)
+        zt_gpu, zd_gpu = L.lmhead_logits_view(ws, B, g, V, d)
+        acc, out = acc.cpu().numpy(), out.cpu().numpy()
+        assert acc[1] == -1 and np.all(out[1] == -1), (B, g, V)
+        oacc, oout, infos = oracle.verify_sample(zt_gpu.cpu().numpy(), zd_gpu.cpu().numpy(), "f32", x, u, T)
+        res = classify_sample(acc, out, oacc, oout, infos)
+        assert not res["unexplained"], ((B, g, d, V), res["unexplained"][:5])
+        tally["explained"] += res["explained"]
+        tally["positions"] += B * g
+    assert tally["explained"] <= MAX_RATE * tally["positions"] + 1e-9, tally
+
+
 @pytest.fixture(scope="module")
 def c5():
     return make_workload("eagle_lmhead", cache=True)
