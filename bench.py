@@ -367,6 +367,34 @@ def main():
     # ------------------------------------------------------- other modes
     if not args.no_modes:
         modes = {}
+        # the small stochastic case: B = 8, gamma = 5, V = 32000, fp32 Zipf
+        # logits (11.3 MB a call, latency-bound); 24 replicas (270 MB) rotate
+        # so the Infinity Cache cannot serve them
+        wz = make_workload("zipf32k", cache=True)
+        zB, zg, zV, zT = wz["B"], wz["gamma"], wz["V"], float(wz["temperature"])
+        zbase = torch.cat([d(wz["target"]).reshape(-1), d(wz["draft"]).reshape(-1)])
+        zn_t = zB * (zg + 1) * zV
+        zreps = []
+        for _ in range(24):
+            zbuf = zbase.clone()
+            zreps.append((zbuf[:zn_t].view(zB, zg + 1, zV), zbuf[zn_t:].view(zB, zg, zV)))
+        del zbase
+        zx, zu = d(wz["draft_tokens"]), d(wz["uniforms"])
+        zws = L.new_workspace(L.MODE_SAMPLE, zB, zg, zV, device=dev)
+        zout = (torch.empty(zB, dtype=torch.int32, device=dev), torch.empty((zB, zg + 1), dtype=torch.int32, device=dev))
+
+        def zstep(i):
+            L.verify_sample(zreps[i % 24][0], zreps[i % 24][1], zx, zu, zT, ws=zws, out=zout)
+
+        settle(zstep, args.settle)
+        for i in range(args.warmup):
+            zstep(i)
+        zms = time_events(zstep, args.steps, stream)
+        zbytes = zB * (2 * zg + 1) * zV * 4
+        modes["sample_b8g5v32k_f32_zipf"] = {
+            "ms": round(zms, 5), "positions_per_s": round(zB * zg / (zms * 1e-3), 1), "bytes": zbytes,
+            "GBs": round(zbytes / (zms * 1e-3) / 1e9, 1), "mean_accept_len": round(zout[0].float().mean().item(), 3)}
+        del zreps
         # greedy on the same replicas (target rows only)
         gws = L.new_workspace(L.MODE_GREEDY, B, g, V, device=dev)
         gout = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, g + 1), dtype=torch.int32, device=dev))
