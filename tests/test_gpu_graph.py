@@ -1,4 +1,5 @@
-"""The verification calls under HIP graph capture and on concurrent streams.
+"""The verification calls (linear, early exit, greedy, trees and the
+EAGLE-style LM head) under HIP graph capture and on concurrent streams.
 
 The library allocates nothing, keeps no state between calls and enqueues
 only kernels (and device-to-device copies) on the caller's stream, so a
@@ -32,18 +33,31 @@ class _Calls:
         self.tree = {k: to_dev(np.ascontiguousarray(t[k])) for k in ("target", "draft", "node_tokens", "parent",
                                                                        "uniforms")}
         self.Tt = float(t["temperature"])
+        # EAGLE-style: feature rows through an LM head, then verification
+        rng = np.random.default_rng(100 + seed)
+        from gen.synth import f32_to_bf16_bits
+        eB, eg, ed, eV = 4, 3, 128, 3000
+        self.eag = {
+            "ft": to_dev(f32_to_bf16_bits(rng.normal(0.0, 1.0, (eB * (eg + 1), ed)).astype(np.float32))),
+            "fd": to_dev(f32_to_bf16_bits(rng.normal(0.0, 1.0, (eB * eg, ed)).astype(np.float32))),
+            "W": to_dev(f32_to_bf16_bits(rng.normal(0.0, 0.1, (ed, eV)).astype(np.float32))),
+            "x": to_dev(rng.integers(0, eV, (eB, eg)).astype(np.int32)),
+            "u": to_dev(rng.random((eB, eg + 1), dtype=np.float32)),
+        }
         dev = self.lin["target"].device
         i32 = dict(dtype=torch.int32, device=dev)
         self.ws = {m: L.new_workspace(m, *shape, device=dev) for m, shape in (
             (L.MODE_SAMPLE, (B, g, V)), (L.MODE_GREEDY, (B, g, V)), (L.MODE_TREE, (4, 15, 9000)),
             (L.MODE_TREE_SAMPLE, (4, 15, 9000)))}
         self.ws_ee = L.new_workspace(L.MODE_SAMPLE, B, g, V, device=dev)
+        self.ws_lm = L.new_workspace(L.MODE_LMHEAD, eB, eg, eV, ed, device=dev)
         self.out = {
             "sample": (torch.empty(B, **i32), torch.empty((B, g + 1), **i32)),
             "early": (torch.empty(B, **i32), torch.empty((B, g + 1), **i32)),
             "greedy": (torch.empty(B, **i32), torch.empty((B, g + 1), **i32)),
             "tree": (torch.empty(4, **i32), torch.empty((4, 15), **i32), torch.empty((4, 15), **i32)),
             "tsample": (torch.empty(4, **i32), torch.empty((4, 15), **i32), torch.empty((4, 15), **i32)),
+            "lmhead": (torch.empty(eB, **i32), torch.empty((eB, eg + 1), **i32)),
         }
         self.clear()                             # no output starts from recycled memory
 
@@ -57,6 +71,8 @@ class _Calls:
         L.verify_tree(t["target"], t["node_tokens"], t["parent"], ws=self.ws[L.MODE_TREE], out=self.out["tree"])
         L.verify_tree_sample(t["target"], t["draft"], t["node_tokens"], t["parent"], t["uniforms"], self.Tt,
                              ws=self.ws[L.MODE_TREE_SAMPLE], out=self.out["tsample"])
+        e = self.eag
+        L.lmhead_verify(e["ft"], e["fd"], e["W"], e["x"], e["u"], 1.0, ws=self.ws_lm, out=self.out["lmhead"])
 
     def snapshot(self):
         return {k: [x.cpu().numpy().copy() for x in v] for k, v in self.out.items()}
@@ -68,7 +84,7 @@ class _Calls:
 
     def load(self, other):
         """Copy another instance's inputs into this one's buffers."""
-        for d, s in ((self.lin, other.lin), (self.tree, other.tree)):
+        for d, s in ((self.lin, other.lin), (self.tree, other.tree), (self.eag, other.eag)):
             for k in d:
                 d[k].copy_(s[k])
 
