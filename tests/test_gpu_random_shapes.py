@@ -6,6 +6,9 @@ vector or not), element type, temperature and draft noise.  Sampling must
 match the oracle under the margin rules (parity.classify_sample,
 classify_tree_sample); greedy and greedy-tree verification on the same target
 rows must match exactly; early exit must equal the full sweep bit for bit.
+EAGLE-style verification (lmhead_verify, both weight layouts) draws feature
+width, vocabulary, batch and positions, and must match the oracle run on the
+float32 logits it leaves in its workspace under the same margin rules.
 """
 import numpy as np
 import pytest
@@ -14,6 +17,7 @@ import torch
 import lossless_draft_verification_03_amd as _binding
 import oracle
 from gen import make_workload
+from gen.synth import f32_to_bf16_bits
 from parity import classify_sample, classify_tree_sample, to_dev
 import sentinel
 
@@ -85,3 +89,36 @@ def test_tree_random_shapes(case):
     oacc, opath, otoks = oracle.verify_tree(w["target"], w["dtype"], w["node_tokens"], w["parent"])
     assert np.array_equal(tacc.cpu().numpy(), oacc)
     assert np.array_equal(tpath.cpu().numpy(), opath) and np.array_equal(ttoks.cpu().numpy(), otoks)
+
+
+def _lmhead_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(B=int(rng.integers(1, 40)), gamma=int(rng.integers(1, 9)), d=int(rng.choice([64, 128, 192, 320])),
+                 V=int(rng.choice([rng.integers(1, 300), rng.integers(300, 3000), rng.integers(3000, 20000)])),
+                 layout=str(rng.choice(["dv", "vd"])), temperature=round(float(rng.uniform(0.5, 1.5)), 3),
+                 wstd=float(rng.choice([0.05, 0.2])), seed=int(rng.integers(0, 1 << 30)))
+            for _ in range(n)]
+
+
+def _lm_id(c):
+    return f"B{c['B']}g{c['gamma']}d{c['d']}V{c['V']}{c['layout']}"
+
+
+@pytest.mark.parametrize("case", _lmhead_cases(12, 13), ids=_lm_id)
+def test_lmhead_verify_random_shapes(case):
+    rng = np.random.default_rng(case["seed"])
+    B, g, dd, V, T = case["B"], case["gamma"], case["d"], case["V"], case["temperature"]
+    ht = f32_to_bf16_bits(rng.normal(0.0, 1.0, (B * (g + 1), dd)).astype(np.float32))
+    hd = f32_to_bf16_bits(rng.normal(0.0, 1.0, (B * g, dd)).astype(np.float32))
+    Wb = f32_to_bf16_bits(rng.normal(0.0, case["wstd"], (dd, V)).astype(np.float32))
+    x = rng.integers(0, V, (B, g)).astype(np.int32)
+    u = rng.random((B, g + 1), dtype=np.float32)
+    lay = L.W_DV if case["layout"] == "dv" else L.W_VD
+    Wl = Wb if case["layout"] == "dv" else np.ascontiguousarray(Wb.T)
+    ws = _binding.new_workspace(_binding.MODE_LMHEAD, B, g, V, dd)
+    ws.fill_(0x5A)
+    acc, out = L.lmhead_verify(to_dev(ht), to_dev(hd), to_dev(Wl), to_dev(x), to_dev(u), T, ws=ws, layout=lay)
+    zt, zd = _binding.lmhead_logits_view(ws, B, g, V, dd)
+    oacc, oout, infos = oracle.verify_sample(zt.cpu().numpy(), zd.cpu().numpy(), "f32", x, u, T)
+    res = classify_sample(acc.cpu().numpy(), out.cpu().numpy(), oacc, oout, infos)
+    assert not res["unexplained"], res["unexplained"][:5]
