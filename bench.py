@@ -9,11 +9,12 @@ cannot serve them.  Prints ONE JSON line.
 Besides the headline: the per-step time distribution (median, p10, p90 from
 events around every step), the row sweep alone (the roofline line) and a
 plain stream read of the same bytes (the HBM rate reachable on this device),
-the outputs' parity counts against the CPU oracle, the same workload under
-the Zipf recipe (reading B), and the oracle itself on the host's cores as the
-CPU baseline (the sampling workload; greedy, greedy-tree and stochastic-tree
-verification; the EAGLE-style LM head plus verification with BLAS on every
-core).
+the same workload under the Zipf recipe (reading B), and the oracle itself on
+the host's cores as the CPU baseline (the sampling workload; greedy,
+greedy-tree and stochastic-tree verification; the EAGLE-style LM head plus
+verification with BLAS on every core).  The CPU-baseline leg, the only one
+that runs the oracle, also reports the parity counts of this run's GPU
+outputs (headline and Zipf batches) against it.
 
 Secondary legs (same JSON line, "modes"): greedy verification of the same
 tensors; early-exit sampling; greedy and stochastic tree verification (B=32,
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip the greedy / tree / LM-head legs")
-    ap.add_argument("--no-parity", action="store_true", help="skip the oracle parity counts")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle parity counts (they also need the CPU-baseline leg)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work of each oracle baseline leg")
     ap.add_argument("--settle", type=float, default=0.2,
                     help="seconds of each leg's own call before its warm-up steps (GPU clocks leave idle)")
@@ -321,20 +323,19 @@ def main():
                              "sweep_frac_of_stream_read": round(k1_gbs / sr_gbs, 4),
                              "step_frac_of_stream_read": round(step_gbs / sr_gbs, 4)}
 
-    # parity of this run's outputs with the oracle (one fresh call, outputs
-    # filled with -7 first so nothing stale can pass), and of greedy mode
+    # this run's outputs for the parity counts (one fresh call, outputs
+    # filled with -7 first so nothing stale can pass), and greedy mode's; the
+    # oracle compares them in the CPU-baseline leg below
+    parity_outs = {}
     if not args.no_parity:
         pout = (torch.full((B,), -7, dtype=torch.int32, device=dev),
                 torch.full((B, g + 1), -7, dtype=torch.int32, device=dev))
         L.verify_sample(reps[0][1], reps[0][2], x, u, T, ws=ws, out=pout)
-        result["parity"] = parity_counts(w, pout[0].cpu().numpy(), pout[1].cpu().numpy())
-        import oracle
         gout_ = (torch.full((B,), -7, dtype=torch.int32, device=dev),
                  torch.full((B, g + 1), -7, dtype=torch.int32, device=dev))
         L.verify_greedy(reps[0][1], x, out=gout_)
-        oacc, oout = oracle.verify_greedy(w["target"], "bf16", w["draft_tokens"])
-        result["parity"]["greedy_bit_exact_sequences"] = int(np.sum(
-            (gout_[0].cpu().numpy() == oacc) & np.all(gout_[1].cpu().numpy() == oout, axis=1)))
+        parity_outs["sample"] = (pout[0].cpu().numpy(), pout[1].cpu().numpy())
+        parity_outs["greedy"] = (gout_[0].cpu().numpy(), gout_[1].cpu().numpy())
 
     # the same shapes under the Zipf recipe (target N(0, 3) - 1.1 ln pi(v)
     # over one seeded permutation, draft noise N(0, 0.8))
@@ -360,7 +361,7 @@ def main():
                                 "hbm_frac_step": round(k1_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                 "mean_accept_len": round(bout[0].float().mean().item(), 3)}
     if not args.no_parity:
-        result["reading_b_zipf"]["parity"] = parity_counts(wb, bout[0].cpu().numpy(), bout[1].cpu().numpy())
+        parity_outs["zipf"] = (bout[0].cpu().numpy(), bout[1].cpu().numpy())
     del reps_b
     torch.cuda.empty_cache()
 
@@ -695,6 +696,16 @@ def main():
         result["modes"] = modes
 
     # --------------------------------------------------------- CPU baseline
+    # (the only leg that runs the oracle: the baseline timings, and the parity
+    # counts of the GPU outputs captured above)
+    if not args.no_cpu_baseline and parity_outs:
+        result["parity"] = parity_counts(w, *parity_outs["sample"])
+        import oracle
+        oacc, oout = oracle.verify_greedy(w["target"], "bf16", w["draft_tokens"])
+        gacc_, gout_np = parity_outs["greedy"]
+        result["parity"]["greedy_bit_exact_sequences"] = int(np.sum(
+            (gacc_ == oacc) & np.all(gout_np == oout, axis=1)))
+        result["reading_b_zipf"]["parity"] = parity_counts(wb, *parity_outs["zipf"])
     if not args.no_cpu_baseline:
         # the oracle as it stands, float64 NumPy, on the headline batch: the
         # 64 sequences split over one forked worker process per core, whole
