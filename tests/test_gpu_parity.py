@@ -571,13 +571,16 @@ def test_lmhead_verify_ragged_shapes_vs_oracle(layout):
     rng = np.random.default_rng(11)
     tally = dict(explained=0, positions=0)
     lay = L.W_DV if layout == "dv" else L.W_VD
-    for (B, g, d, V, T) in ((64, 3, 128, 1100, 1.0), (37, 3, 192, 1000, 0.8), (20, 4, 64, 997, 1.3)):
+    # the last shape has 2344 partials per row, so the merge takes them in
+    # three passes of 1024
+    for (B, g, d, V, T) in ((64, 3, 128, 1100, 1.0), (37, 3, 192, 1000, 0.8), (20, 4, 64, 997, 1.3),
+                            (3, 2, 64, 300001, 1.0)):
         rows_t = B * (g + 1)
         Ht = rng.normal(0.0, 1.0, (rows_t, d)).astype(np.float32)
         Hd = (Ht.reshape(B, g + 1, d)[:, :g].reshape(B * g, d)
               + rng.normal(0.0, 0.4, (B * g, d))).astype(np.float32)
         Wf = rng.normal(0.0, 0.08, (d, V)).astype(np.float32)
-        Wf[:, 1024 if V > 1024 else 896:] *= 3.0
+        Wf[:, (V // 256) * 256 - 128 if V > 1100 else (1024 if V > 1024 else 896):] *= 3.0
         ht, hd, Wb = f32_to_bf16_bits(Ht), f32_to_bf16_bits(Hd), f32_to_bf16_bits(Wf)
         # draft tokens drawn from q of the float64 draft logits
         zd64 = oracle.lmhead_logits(hd, Wb).reshape(B, g, V) / T
