@@ -219,7 +219,7 @@ spec_status spec_verify_sample(const void* target_logits, const void* draft_logi
  * Sizes whose workspace (spec_workspace_bytes(SPEC_MODE_SAMPLE, B, gamma, V,
  * 0)) exceeds SPEC_NOALLOC_SCRATCH_BYTES are rejected with SPEC_EWORKSPACE
  * before anything is launched (B = 64, gamma = 7, V = 128256 needs about
- * 0.47 MB; the limit holds about 2300 such sequences).  Every call on one GPU
+ * 0.50 MB; the limit holds about 2100 such sequences).  Every call on one GPU
  * shares that GPU's array and leaves its contents behind; the array needs no
  * clearing (each call writes every byte it reads), but calls that overlap in
  * time on the same GPU (several streams, several host threads) race on it

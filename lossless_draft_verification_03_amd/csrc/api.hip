@@ -115,7 +115,8 @@ bool make_layout(int mode, long long B, long long gN, long long V, long long d, 
                                                                          : 0;
   const RowSweepShape sh = row_sweep_shape((int)V, dt, vpt);
   int seg_elems = 0;
-  const int nseg2 = seqs ? sample_draw_segments((int)V, &seg_elems) : 0;
+  // fp32 rows take the most draw segments
+  const int nseg2 = seqs ? sample_draw_segments((int)V, DT_F32, &seg_elems) : 0;
   size_t o = 0;
   L->info = o;   o = up(o + (size_t)seqs * sizeof(DrawInfo));
   L->part = o;   o = up(o + (size_t)rows * sh.nseg * sizeof(Partial));
@@ -245,7 +246,7 @@ spec_status draw_on(const void* tgt, const void* drf, int dt, const int32_t* tok
   p.B = B;
   p.g = g;
   p.V = V;
-  p.nseg = sample_draw_segments(V, &p.seg_elems);
+  p.nseg = sample_draw_segments(V, dt, &p.seg_elems);
   p.tc = tc;
   p.info = at<DrawInfo>(ws, L.info);
   p.segsum = at<double>(ws, L.segsum);

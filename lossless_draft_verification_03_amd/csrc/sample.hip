@@ -27,9 +27,9 @@
 //               both rows' normalisers and offsets.
 //  k_draw_pick  one workgroup per sequence: wave 0 locates the sub-segment
 //               holding u[b][gamma] * total among the B x 4 nseg masses, the
-//               block rescans those 2048 elements with one contiguous run per
-//               lane (weights kept in registers), block-scans the lane sums
-//               in fp64 and the crossing lane walks its run.
+//               block rescans those 2048 bf16 (1024 fp32) elements with one
+//               16-byte run per lane (weights kept in registers), block-scans
+//               the lane sums in fp64 and the crossing lane walks its run.
 // A residual weight costs two exp2 and about seven other VALU instructions
 // per element pair; the pick's rescan is VALU-bound on its one CU, and the
 // sub-segments cut it to a quarter of a segment.
@@ -41,9 +41,16 @@ namespace sv {
 
 namespace {
 
-constexpr int kRun = 8;                             // elements per lane in the pick's rescan
-constexpr int kSubElems = kBlock * kRun;            // 2048: one wave's share of a segment
-constexpr int kSegElems = kDrawSub * kSubElems;     // 8192: one mass workgroup
+// Draw segments by element type: the pick's rescan gives each lane one
+// 16-byte vector (8 bf16 or 4 fp32 logits), so a sub-segment (one wave's
+// share of a mass workgroup) is 2048 bf16 or 1024 fp32 logits, and a segment
+// 8192 or 4096: the same 16 KB of each row per mass workgroup either way.
+template <int DT>
+constexpr int run_elems() { return DT == DT_BF16 ? 8 : 4; }
+template <int DT>
+constexpr int sub_elems() { return kBlock * run_elems<DT>(); }
+template <int DT>
+constexpr int seg_elems() { return kDrawSub * sub_elems<DT>(); }
 static_assert(kDrawSub * kWave == kBlock, "one sub-segment per wave");
 
 
@@ -67,7 +74,7 @@ __device__ DrawRow draw_row(const SampleParams& P, int b, const DrawInfo& di) {
 }
 
 // Sum of the draw weights over elements [s0, s1) of the draw row (at most
-// kSubElems), lane-interleaved over one wave, fp64 accumulation; returns the
+// sub_elems<DT>()), lane-interleaved over one wave, fp64 accumulation; returns the
 // wave's total in every lane (fixed combination order).
 template <int DT, bool ALIGNED, bool RESID>
 __device__ double sub_partial(const DrawRow& R, long long s0, long long s1, const TempConst& tc, int lane) {
@@ -77,7 +84,7 @@ __device__ double sub_partial(const DrawRow& R, long long s0, long long s1, cons
   if constexpr (ALIGNED) {
     // every lane issues its KV loads (offsets clamped into the range) before
     // computing
-    constexpr int KV = kSubElems / EPV / kWave;
+    constexpr int KV = sub_elems<DT>() / EPV / kWave;
     const int nvec = (int)((s1 - s0) / EPV);
     if (nvec > 0) {
       const __amdgpu_buffer_rsrc_t rt = make_rsrc(R.t + s0 * ES, (uint32_t)nvec * 16u);
@@ -114,8 +121,8 @@ __device__ double sub_partial(const DrawRow& R, long long s0, long long s1, cons
 template <int DT, bool ALIGNED>
 __device__ void segment_masses(const DrawRow& R, long long V, int s, const TempConst& tc, int wid, int lane,
                                double* sub) {
-  const long long s0 = min((long long)s * kSegElems + (long long)wid * kSubElems, V);
-  const long long s1 = min(s0 + kSubElems, V);
+  const long long s0 = min((long long)s * seg_elems<DT>() + (long long)wid * sub_elems<DT>(), V);
+  const long long s1 = min(s0 + sub_elems<DT>(), V);
   const double m = R.resid ? sub_partial<DT, ALIGNED, true>(R, s0, s1, tc, lane)
                            : sub_partial<DT, ALIGNED, false>(R, s0, s1, tc, lane);
   if (lane == 0) sub[s * kDrawSub + wid] = m;
@@ -208,6 +215,8 @@ template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void k_draw_pick(SampleParams P) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
+  constexpr int kRun = run_elems<DT>();
+  constexpr int kSubElems = sub_elems<DT>();
   __shared__ double sh_wtot[4];
   __shared__ int sh_first[4];
   __shared__ long long sh_y;
@@ -384,10 +393,11 @@ hipError_t launch_sample_t(const SampleParams& p, hipStream_t s) {
 
 }  // namespace
 
-int sample_draw_segments(int V, int* seg_elems) {
-  long long n = ((long long)V + kSegElems - 1) / kSegElems;
+int sample_draw_segments(int V, int dt, int* seg_elems_out) {
+  const int se = dt == DT_BF16 ? seg_elems<DT_BF16>() : seg_elems<DT_F32>();
+  long long n = ((long long)V + se - 1) / se;
   if (n < 1) n = 1;
-  *seg_elems = kSegElems;
+  *seg_elems_out = se;
   return (int)n;
 }
 

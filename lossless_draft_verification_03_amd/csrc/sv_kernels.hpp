@@ -92,7 +92,9 @@ struct SampleParams {
 // Each draw segment is summed as kDrawSub contiguous sub-segments, one per
 // wave; the pick rescans one sub-segment.
 constexpr int kDrawSub = 4;
-int sample_draw_segments(int V, int* seg_elems);
+// Draw segments per row for element type dt (DT_BF16 / DT_F32): 8192 bf16 or
+// 4096 fp32 logits each.
+int sample_draw_segments(int V, int dt, int* seg_elems);
 hipError_t launch_sample(const SampleParams& p, int dt, hipStream_t s);
 
 // ---------------------------------------------------------- greedy / tree
