@@ -248,6 +248,25 @@ def test_probe_probs_within_tolerance():
             assert np.all(np.abs(r[i] - ro) <= bound)
 
 
+# ------------------------------------------------------ extreme temperatures
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [0.02, 0.1, 25.0])
+def test_extreme_temperatures(dt, T):
+    """Very peaked (T = 0.02: exponents of a few hundred, most of the
+    vocabulary underflows in float32) and nearly flat (T = 25) distributions:
+    sampling under the margin rules and greedy bit-exact against the oracle,
+    over several batches."""
+    tally = dict(explained=0, positions=0)
+    for seed in range(4):
+        w = make_workload("tiny", B=16, gamma=5, V=5000, dtype=dt, temperature=T, draft_noise=0.8, seed=100 + seed)
+        _check_sample(w, tally)
+        t, x = to_dev(w["target"]), to_dev(w["draft_tokens"])
+        gacc, gout = L.verify_greedy(t, x)
+        oacc, oout = oracle.verify_greedy(w["target"], w["dtype"], w["draft_tokens"])
+        assert np.array_equal(gacc.cpu().numpy(), oacc) and np.array_equal(gout.cpu().numpy(), oout)
+    assert tally["explained"] <= MAX_RATE * tally["positions"] + 1e-9, tally
+
+
 # ---------------------------------------------------------------- edges
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,g,V", [(1, 1, 1), (2, 1, 2), (3, 2, 3), (2, 3, 5), (4, 2, 8), (3, 4, 9),
