@@ -61,6 +61,8 @@ def _check(w, T=None, max_explained=1, n_sweep=-1):
     ("bf16", 70001, 7, "star", 2.5, 1.0),              # several draw segments, unaligned
     ("bf16", 131080, 5, "wide", 2.0, 0.9),             # several draw segments, aligned
     ("f32", 65540, 6, "random", 1.5, 1.0),
+    ("bf16", 5000, 15, "binary", 0.8, 0.03),           # very peaked: most of each row underflows
+    ("f32", 3000, 15, "star", 1.0, 20.0),              # nearly flat
 ])
 def test_matches_oracle(dtype, V, N, tree, noise, T):
     w = make_workload("tree_sample63", B=6, N=N, V=V, dtype=dtype, tree=tree, draft_noise=noise,
