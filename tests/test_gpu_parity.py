@@ -267,6 +267,25 @@ def test_extreme_temperatures(dt, T):
     assert tally["explained"] <= MAX_RATE * tally["positions"] + 1e-9, tally
 
 
+def test_large_logit_offsets():
+    """Softmax is shift-invariant: float32 logits moved by large offsets
+    (target + 3000, draft - 2000, and one batch scaled by 40) keep p and q,
+    so the drafted tokens stay valid draws.  The row maxima absorb the
+    offsets; the outputs must match the oracle on the moved logits under the
+    margin rules."""
+    tally = dict(explained=0, positions=0)
+    for seed, (shift_t, shift_d, scale) in enumerate(((3000.0, -2000.0, 1.0), (-5000.0, 4000.0, 1.0),
+                                                       (0.0, 0.0, 40.0))):
+        w = make_workload("tiny", B=16, gamma=6, V=7000, dtype="f32", temperature=1.0, draft_noise=0.8,
+                          seed=200 + seed)
+        w = dict(w)
+        w["target"] = (w["target"] * scale + shift_t).astype(np.float32)
+        w["draft"] = (w["draft"] * scale + shift_d).astype(np.float32)
+        w["temperature"] = float(scale)
+        _check_sample(w, tally)
+    assert tally["explained"] <= MAX_RATE * tally["positions"] + 1e-9, tally
+
+
 # ---------------------------------------------------------------- edges
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,g,V", [(1, 1, 1), (2, 1, 2), (3, 2, 3), (2, 3, 5), (4, 2, 8), (3, 4, 9),
