@@ -687,7 +687,7 @@ def main():
             settle(estep, args.settle)
             for i in range(3):
                 estep(i)
-            ems = time_events(estep, 10, stream)
+            ems = time_events(estep, 20, stream)
             modes[f"eagle_lmhead_b64g5d4096_{name}"] = {
                 "ms": round(ems, 4), "positions_per_s": round(eB * eg / (ems * 1e-3), 1),
                 "gemm_ms": round(pms, 4), "gemm_tflops": round(flops / (pms * 1e-3) / 1e12, 1),
